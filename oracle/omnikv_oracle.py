@@ -1,0 +1,404 @@
+"""Plain CPU oracle for the OmniKVQuant hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the entry
+module and the benchmark's CPU-baseline leg may import, call or execute this
+module.  The library (HIP kernels + C ABI + Python binding) never does, and
+this module shares no code, table or constant with it.
+
+What it computes, and from which passage
+----------------------------------------
+Source pages (cited by title and section):
+  [paper]  "OmniKVQuant: KV Cache Quantization for Omni-LLMs" (paper text)
+  [digest] "OmniKVQuant：面向 Omni-LLM 的 KV 缓存量化" (Chinese digest of the paper)
+
+* Keys: a randomized Hadamard rotation shared by every modality, inherited
+  from TurboQuant ([paper] §1 Introduction; [digest] "这篇论文解决什么问题",
+  "关联工作"), then a min-max range per 32-token window of the stream mapped
+  onto a fixed codebook ([paper] §1 and §3.1 Implementation details, g = 32;
+  [digest] "方法概览"), with a minimum m_gc and a scale s_gc per group g and
+  channel c stored in FP16 ([paper] §3.3 Error comparison).
+* Values: a separate basis U_m per modality m in {V, A, L} ([paper] §2.3),
+  then a fixed codebook.  The per-token scale and the codebook's values are
+  not printed; the reading used here is TurboQuant's fixed Lloyd-Max codebook
+  for N(0,1), applied to v'/sigma with sigma the token's RMS.
+* Decode: attention over the dequantized cache.  The pages' fused kernel
+  reorders this computation ([paper] §1, Fig. 1(d)); the oracle computes the
+  plain definition, softmax(scale * q . k_hat) . v_hat, in float64.
+
+Fixed arithmetic of the codec (fp32, in this exact order, so that the GPU
+codes and metadata can be compared bit for bit):
+  rotation   y = c_d * FWHT(D x): z = D x; butterfly stages h = 1, 2, ..., d/2,
+             each mapping (z_i, z_{i+h}) -> (z_i + z_{i+h}, z_i - z_{i+h})
+             for i with bit h clear; then one multiply by c_d = fp32(1/sqrt(d)).
+  key range  mn, mx over the 32 tokens of a window; m = fp16(mn);
+             s = fp16((mx - mn) / L) with L = 2^bits - 1 (IEEE fp32 division,
+             fp16 round-to-nearest-even).
+  key code   theta_j = m + s * (j + 1/2) (product and sum each rounded to fp32),
+             code = #{ j < L : y >= theta_j }.
+  value scale  S = sum of v_i^2 by the stride-halving tree (pairs (i, i + d/2),
+             then (i, i + d/4), ..., each square and sum rounded to fp32);
+             sigma = sqrt(S / d) (correctly rounded); stored fp16.
+  value rot  v'_i = sum_k U[k][i] v_k accumulated for k = 0, 1, ..., d-1 with
+             every product and every partial sum rounded to fp32 (no fma).
+  value code theta_j = fp32(sigma_fp16) * beta_j with beta_j the fp32 midpoint of
+             adjacent fp16 codebook levels; code = #{ j : v' >= theta_j }.
+
+Parity pins for every function live in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+F32 = np.float32
+WINDOW = 32
+
+
+# ----------------------------------------------------------------------------- fp16 helpers
+def f16_bits(x) -> np.ndarray:
+    """fp32 -> IEEE binary16 bit patterns, round to nearest even (numpy's cast)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_to_f32(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- key rotation
+def rotation_constant(d: int) -> np.float32:
+    """c_d: the fp32 number nearest to 1/sqrt(d)."""
+    return F32(1.0 / math.sqrt(d))
+
+
+def rotate_keys_f32(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """y = c_d * H_d (D x) in fp32, butterfly stages h = 1, 2, ..., d/2 in order.
+
+    Randomized Hadamard rotation of TurboQuant ([paper] §1 Introduction;
+    [digest] "关联工作").  x: fp32 [..., d]; signs: +-1 [d] (the diagonal D).
+    """
+    x = np.asarray(x, dtype=F32)
+    d = x.shape[-1]
+    lead = x.shape[:-1]
+    z = (x * np.asarray(signs, dtype=F32)).reshape(-1, d)
+    h = 1
+    while h < d:
+        z = z.reshape(-1, d // (2 * h), 2, h)
+        a = z[:, :, 0, :]
+        b = z[:, :, 1, :]
+        z = np.stack([a + b, a - b], axis=2).reshape(-1, d)
+        h *= 2
+    return (z * rotation_constant(d)).reshape(*lead, d)
+
+
+def sylvester(d: int) -> np.ndarray:
+    """H_d with H_ij = (-1)^popcount(i & j), float64."""
+    i = np.arange(d)
+    bits = np.bitwise_and(i[:, None], i[None, :])
+    pc = np.zeros_like(bits)
+    while bits.any():
+        pc += bits & 1
+        bits >>= 1
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def inverse_key_rotation_f64(y: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """x = R^{-1} y for R = c_d H D, in float64: x = D H y / (c_d d)."""
+    d = y.shape[-1]
+    H = sylvester(d)
+    c = float(rotation_constant(d))
+    return (np.asarray(y, dtype=np.float64) @ H) * (np.asarray(signs, np.float64) / (c * d))
+
+
+# ----------------------------------------------------------------------------- packed layouts
+def key_code_position(d: int, bits: int, t: int, c: int):
+    """(word, bit) of key code (window token t, rotated channel c) in a window block.
+
+    A window block holds the 32 x d codes of one (sequence, KV head, window) in
+    d * bits uint32 words.  Lane l = 16 g + rho owns d*bits/64 consecutive words
+    and holds tokens {rho, rho + 16} (tau = 0, 1) of channels g*d/4 + 8 s + j
+    (s < d/32, j < 8).  In each word, j even sits in bits 0..15 and j odd in
+    bits 16..31, at a slot (bits-wide field) chosen per case below.
+    """
+    tau, rho = divmod(t, 16)
+    g, r = divmod(c, d // 4)
+    s, j = divmod(r, 8)
+    i, e = divmod(j, 2)
+    per_lane = d * bits // 64
+    if (d, bits) == (128, 2):
+        lw, slot = i, 4 * tau + s
+    elif (d, bits) == (128, 4):
+        lw, slot = 4 * tau + i, s
+    elif (d, bits) == (64, 2):
+        lw, slot = i & 1, 4 * (i >> 1) + 2 * tau + s
+    elif (d, bits) == (64, 4):
+        lw, slot = i, 2 * tau + s
+    else:
+        raise ValueError((d, bits))
+    return (16 * g + rho) * per_lane + lw, 16 * e + bits * slot
+
+
+def value_code_position(d: int, bits: int, t: int, c: int):
+    """(word, bit) of value code (window token t, channel c) in a window block.
+
+    Lane l = 16 g + rho holds channels 16 u + rho (u < d/16) of the eight
+    tokens {4g .. 4g+3, 16+4g .. 16+4g+3} (index j = 0..7 in that order).
+    Word/slot per case below; j even in bits 0..15, j odd in bits 16..31.
+    """
+    u, rho = divmod(c, 16)
+    if t < 16:
+        g, j = divmod(t, 4)
+    else:
+        g, j = divmod(t - 16, 4)
+        j += 4
+    i, e = divmod(j, 2)
+    per_lane = d * bits // 64
+    if (d, bits) == (128, 2):
+        lw, slot = i, u
+    elif (d, bits) == (64, 2):
+        lw, slot = i & 1, 4 * (i >> 1) + u
+    elif (d, bits) == (128, 4):
+        lw, slot = 4 * (u >> 2) + i, u & 3
+    elif (d, bits) == (64, 4):
+        lw, slot = i, u
+    else:
+        raise ValueError((d, bits))
+    return (16 * g + rho) * per_lane + lw, 16 * e + bits * slot
+
+
+def _position_table(fn, d: int, bits: int):
+    word = np.empty((WINDOW, d), dtype=np.int64)
+    bit = np.empty((WINDOW, d), dtype=np.int64)
+    for t in range(WINDOW):
+        for c in range(d):
+            word[t, c], bit[t, c] = fn(d, bits, t, c)
+    return word, bit
+
+
+_TABLES = {}
+
+
+def position_table(kind: str, d: int, bits: int):
+    key = (kind, d, bits)
+    if key not in _TABLES:
+        fn = key_code_position if kind == "key" else value_code_position
+        _TABLES[key] = _position_table(fn, d, bits)
+    return _TABLES[key]
+
+
+def pack_windows(codes: np.ndarray, kind: str, bits: int) -> np.ndarray:
+    """codes [..., 32, d] (ints < 2^bits) -> uint32 words [..., d*bits]."""
+    d = codes.shape[-1]
+    word, bit = position_table(kind, d, bits)
+    lead = codes.shape[:-2]
+    c = codes.reshape(-1, WINDOW * d).astype(np.uint64)
+    out = np.zeros((c.shape[0], d * bits), dtype=np.uint64)
+    shifted = c << bit.reshape(-1).astype(np.uint64)
+    for k in range(WINDOW * d):          # positions are disjoint: OR == add
+        out[:, word.flat[k]] |= shifted[:, k]
+    return out.astype(np.uint32).reshape(*lead, d * bits)
+
+
+def unpack_windows(words: np.ndarray, kind: str, d: int, bits: int) -> np.ndarray:
+    """uint32 words [..., d*bits] -> codes uint8 [..., 32, d]."""
+    word, bit = position_table(kind, d, bits)
+    lead = words.shape[:-1]
+    w = words.reshape(-1, d * bits).astype(np.uint64)
+    vals = (w[:, word.reshape(-1)] >> bit.reshape(-1).astype(np.uint64)) & np.uint64(2**bits - 1)
+    return vals.astype(np.uint8).reshape(*lead, WINDOW, d)
+
+
+# ----------------------------------------------------------------------------- key codec
+def key_window_quantize(y: np.ndarray, bits: int):
+    """One window's range metadata and codes from rotated keys y: fp32 [..., 32, d].
+
+    Returns (codes uint8 [..., 32, d], m fp16 bits [..., d], s fp16 bits [..., d]).
+    """
+    L = 2**bits - 1
+    y = np.asarray(y, dtype=F32)
+    mn = y.min(axis=-2)
+    mx = y.max(axis=-2)
+    step = (mx - mn) / F32(L)
+    m16, s16 = f16_bits(mn), f16_bits(step)
+    m, s = f16_to_f32(m16), f16_to_f32(s16)
+    codes = np.zeros(y.shape, dtype=np.uint8)
+    for j in range(L):
+        theta = m + s * F32(j + 0.5)
+        codes += (y >= theta[..., None, :]).astype(np.uint8)
+    return codes, m16, s16
+
+
+def quantize_keys(k: np.ndarray, signs: np.ndarray, bits: int):
+    """Quantize a chunk of keys.  k: fp32 [B][n][Hkv][d], n a multiple of 32.
+
+    Returns (k_codes uint32 [B][Hkv][n/32][d*bits], k_min, k_scale fp16 bits
+    [B][Hkv][n/32][d]); window w of the result is window t0/32 + w of the cache.
+    """
+    B, n, H, d = k.shape
+    assert n % WINDOW == 0
+    y = rotate_keys_f32(k, signs)                                # [B][n][H][d]
+    y = y.transpose(0, 2, 1, 3).reshape(B, H, n // WINDOW, WINDOW, d)
+    codes, m16, s16 = key_window_quantize(y, bits)
+    return pack_windows(codes, "key", bits), m16, s16
+
+
+# ----------------------------------------------------------------------------- value codec
+def lloyd_max_gaussian(n_levels: int, iters: int = 4000) -> np.ndarray:
+    """Lloyd-Max levels for N(0,1) (float64, ascending).
+
+    Alternates the two optimality conditions: every threshold is the midpoint
+    of its neighbouring levels, every level is the conditional mean of N(0,1)
+    between its thresholds, E[X | a < X < b] = (phi(a) - phi(b)) / (Phi(b) - Phi(a)).
+    """
+    phi = lambda x: math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi) if math.isfinite(x) else 0.0
+    Phi = lambda x: 0.5 * (1.0 + math.erf(x / math.sqrt(2.0))) if math.isfinite(x) else (1.0 if x > 0 else 0.0)
+    lv = np.linspace(-2.0, 2.0, n_levels)
+    for _ in range(iters):
+        th = [-math.inf] + [0.5 * (lv[i] + lv[i + 1]) for i in range(n_levels - 1)] + [math.inf]
+        lv = np.array([(phi(th[i]) - phi(th[i + 1])) / (Phi(th[i + 1]) - Phi(th[i]))
+                       for i in range(n_levels)])
+    return lv
+
+
+def value_codebook_f16(bits: int) -> np.ndarray:
+    """Fixed value codebook: Lloyd-Max levels for N(0,1) rounded to fp16 (bit patterns)."""
+    return f16_bits(lloyd_max_gaussian(2**bits).astype(np.float32))
+
+
+def value_boundaries_f32(levels16: np.ndarray) -> np.ndarray:
+    """beta_j = (l_j + l_{j+1}) / 2 in fp32 from fp16 levels."""
+    lv = f16_to_f32(levels16)
+    return ((lv[:-1] + lv[1:]) / F32(2)).astype(F32)
+
+
+def value_scale_f32(v: np.ndarray) -> np.ndarray:
+    """sigma = sqrt(S/d), S = stride-halving tree sum of v_i^2, all fp32.  v: [..., d]."""
+    v = np.asarray(v, dtype=F32)
+    d = v.shape[-1]
+    S = v * v
+    w = d // 2
+    while w >= 1:
+        S = S[..., :w] + S[..., w:2 * w]
+        w //= 2
+    return np.sqrt(S[..., 0] / F32(d))
+
+
+def rotate_values_f32(v: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """v'_i = sum_k U[k][i] v_k, k ascending, each product and sum rounded to fp32."""
+    v = np.asarray(v, dtype=F32)
+    U = np.asarray(U, dtype=F32)
+    acc = np.zeros(v.shape, dtype=F32)
+    for kk in range(v.shape[-1]):
+        acc = acc + U[kk][None, :] * v[..., kk:kk + 1]
+    return acc
+
+
+def quantize_values(v: np.ndarray, tags: np.ndarray, U: np.ndarray, levels16: np.ndarray, bits: int):
+    """Quantize a chunk of values.
+
+    v: fp32 [B][n][Hkv][d]; tags: uint8 [B][n] modality of each token (rotation
+    index); U: fp32 [M][d][d]; levels16: fp16 codebook bits [2^bits].
+    Returns (v_codes uint32 [B][Hkv][n/32][d*bits], v_scale fp16 bits [B][Hkv][n]).
+    """
+    B, n, H, d = v.shape
+    assert n % WINDOW == 0
+    sigma16 = f16_bits(value_scale_f32(v))                      # [B][n][H]
+    sig = f16_to_f32(sigma16)
+    vr = np.empty_like(v, dtype=F32)
+    for m in range(U.shape[0]):
+        sel = tags == m
+        if sel.any():
+            vr[sel] = rotate_values_f32(v[sel], U[m])
+    beta = value_boundaries_f32(levels16)
+    codes = np.zeros(v.shape, dtype=np.uint8)
+    for j in range(beta.shape[0]):
+        theta = sig * beta[j]
+        codes += (vr >= theta[..., None]).astype(np.uint8)
+    codes = codes.transpose(0, 2, 1, 3).reshape(B, H, n // WINDOW, WINDOW, d)
+    return pack_windows(codes, "value", bits), sigma16.transpose(0, 2, 1).copy()
+
+
+def rotated_values_f64(v: np.ndarray, tags: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """v' = U_m^T v in float64 (for distance-to-boundary diagnostics)."""
+    out = np.empty(v.shape, dtype=np.float64)
+    for m in range(U.shape[0]):
+        sel = tags == m
+        if sel.any():
+            out[sel] = np.asarray(v[sel], np.float64) @ np.asarray(U[m], np.float64)
+    return out
+
+
+# ----------------------------------------------------------------------------- dequantization
+def dequantize_keys(k_codes, k_min, k_scale, signs, bits: int, length: Optional[int] = None):
+    """Original-space keys x_hat = R^{-1}(m + s * code), float64 [B][Hkv][T][d]."""
+    B, H, nw, _ = k_codes.shape
+    d = k_min.shape[-1]
+    codes = unpack_windows(k_codes, "key", d, bits).astype(np.float64)   # [B][H][nw][32][d]
+    yhat = f16_to_f64(k_min)[:, :, :, None, :] + f16_to_f64(k_scale)[:, :, :, None, :] * codes
+    yhat = yhat.reshape(B, H, nw * WINDOW, d)
+    if length is not None:
+        yhat = yhat[:, :, :length]
+    return inverse_key_rotation_f64(yhat, signs)
+
+
+def dequantize_values(v_codes, v_scale, tags, U, levels16, bits: int, length: Optional[int] = None):
+    """Original-space values v_hat = U_m (sigma * l[code]), float64 [B][Hkv][T][d]."""
+    B, H, nw, _ = v_codes.shape
+    d = U.shape[-1]
+    T = nw * WINDOW if length is None else length
+    codes = unpack_windows(v_codes, "value", d, bits).reshape(B, H, nw * WINDOW, d)[:, :, :T]
+    lv = f16_to_f64(levels16)
+    vprime = f16_to_f64(v_scale)[:, :, :T, None] * lv[codes]
+    out = np.empty_like(vprime)
+    for m in range(U.shape[0]):
+        for b in range(B):
+            sel = tags[b, :T] == m
+            if sel.any():
+                out[b][:, sel] = vprime[b][:, sel] @ np.asarray(U[m], np.float64).T
+    return out
+
+
+# ----------------------------------------------------------------------------- attention
+def attention_f64(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * q . k_t) . v_t for one query head; zeros when there is no token."""
+    if keys.shape[0] == 0:
+        return np.zeros(values.shape[-1])
+    s = scale * (keys @ np.asarray(q, np.float64))
+    p = np.exp(s - s.max())
+    return (p @ values) / p.sum()
+
+
+def decode_attention(q, seq_lens, cache: dict, signs, U, levels16, scale: Optional[float] = None,
+                     rows: Optional[Sequence] = None):
+    """Decode attention over the dequantized packed cache, float64.
+
+    q: fp32 [B][Hq][d]; seq_lens: [B]; cache: dict with k_codes, k_min, k_scale,
+    v_codes, v_scale, modality, key_bits, value_bits.  Query head h reads KV
+    head h // (Hq/Hkv).  rows: optional list of (b, h) to compute (others 0).
+    """
+    B, Hq, d = q.shape
+    Hkv = cache["k_min"].shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if not scale else float(scale)
+    out = np.zeros((B, Hq, d))
+    want = [(b, h) for b in range(B) for h in range(Hq)] if rows is None else list(rows)
+    by_kv = {}
+    for b, h in want:
+        by_kv.setdefault((b, h // G), []).append(h)
+    for (b, kv), heads in sorted(by_kv.items()):
+        n = int(seq_lens[b])
+        nw = (n + WINDOW - 1) // WINDOW
+        sl = lambda a: a[b:b + 1, kv:kv + 1, :nw]
+        keys = dequantize_keys(sl(cache["k_codes"]), sl(cache["k_min"]), sl(cache["k_scale"]),
+                               signs, cache["key_bits"], length=n)[0, 0]
+        vals = dequantize_values(sl(cache["v_codes"]), cache["v_scale"][b:b + 1, kv:kv + 1, :nw * WINDOW],
+                                 cache["modality"][b:b + 1], U, levels16, cache["value_bits"],
+                                 length=n)[0, 0]
+        for h in heads:
+            out[b, h] = attention_f64(q[b, h], keys, vals, scale)
+    return out

@@ -1,0 +1,379 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test ties one oracle function to something other than itself: a closed
+form, a textbook table, an invariant, a worked example or brute force.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import omnikv_oracle as O
+from decode_attention_fwht_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- fp16
+def test_fp16_rounding_matches_binary16_definition():
+    for line in open(os.path.join(GOLDEN, "fp16_rne.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        v, bits = line.split()
+        with np.errstate(over="ignore"):
+            got = int(O.f16_bits(np.float32(float(v))))
+        assert got == int(bits, 16), (v, hex(got), bits)
+
+
+# ----------------------------------------------------------------------------- rotation (T1)
+@pytest.mark.parametrize("d", [64, 128])
+def test_rotation_equals_sylvester_closed_form(d):
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((5, d)).astype(np.float32)
+    signs = synth.rademacher_signs(d, 3)
+    y = O.rotate_keys_f32(x, signs).astype(np.float64)
+    # closed form: H_ij = (-1)^popcount(i&j), written out element by element here
+    H = np.array([[(-1) ** bin(i & j).count("1") for j in range(d)] for i in range(d)], dtype=np.float64)
+    ref = (x.astype(np.float64) * signs) @ H.T / math.sqrt(d)
+    assert np.max(np.abs(y - ref)) < 1e-5 * np.max(np.abs(ref))
+
+
+def test_rotation_is_an_involution_on_small_integers_d64():
+    # d = 64: c_d = 1/8 exactly, H H = 64 I, so (c H)(c H) x = x with no rounding at all
+    rng = np.random.default_rng(1)
+    x = rng.integers(-7, 8, (9, 64)).astype(np.float32)
+    ones = np.ones(64, np.int8)
+    y = O.rotate_keys_f32(O.rotate_keys_f32(x, ones), ones)
+    assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rotation_is_orthogonal_and_inverse_recovers_input(d):
+    signs = synth.rademacher_signs(d, 5)
+    eye = np.eye(d, dtype=np.float32)
+    R = O.rotate_keys_f32(eye, signs).astype(np.float64).T        # columns = R e_i
+    assert np.max(np.abs(R @ R.T - np.eye(d))) < 1e-6
+    x = np.random.default_rng(2).standard_normal((4, d)).astype(np.float32)
+    back = O.inverse_key_rotation_f64(O.rotate_keys_f32(x, signs), signs)
+    assert np.max(np.abs(back - x)) < 1e-5
+
+
+def test_rotation_stage_order_scalar_reference():
+    # A scalar loop that follows the documented stage order one butterfly at a
+    # time (h = 1, 2, ..., d/2; (a, b) -> (a + b, a - b)), in fp32, must match
+    # the vectorised oracle bit for bit.
+    d = 16
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(d).astype(np.float32)
+    signs = synth.rademacher_signs(d, 1)
+    z = [np.float32(x[i]) * np.float32(signs[i]) for i in range(d)]
+    h = 1
+    while h < d:
+        for i in range(d):
+            if i & h == 0:
+                a, b = z[i], z[i + h]
+                z[i], z[i + h] = np.float32(a + b), np.float32(a - b)
+        h *= 2
+    c = np.float32(1.0 / math.sqrt(d))
+    ref = np.array([np.float32(v * c) for v in z], np.float32)
+    assert np.array_equal(O.rotate_keys_f32(x, signs), ref)
+
+
+# ----------------------------------------------------------------------------- layouts (T3)
+@pytest.mark.parametrize("kind", ["key", "value"])
+@pytest.mark.parametrize("d,bits", [(64, 2), (64, 4), (128, 2), (128, 4)])
+def test_layout_is_a_bijection(kind, d, bits):
+    word, bit = O.position_table(kind, d, bits)
+    flat = word * 32 + bit
+    assert flat.min() >= 0 and flat.max() < d * bits * 32
+    assert len(np.unique(flat)) == 32 * d
+    assert np.all(bit % bits == 0)
+    # every code stays inside one 16-bit half
+    assert np.all((bit % 16) + bits <= 16)
+
+
+@pytest.mark.parametrize("kind", ["key", "value"])
+@pytest.mark.parametrize("d,bits", [(64, 2), (64, 4), (128, 2), (128, 4)])
+def test_pack_unpack_round_trip(kind, d, bits):
+    rng = np.random.default_rng(d * bits)
+    codes = rng.integers(0, 2**bits, (3, 32, d)).astype(np.uint8)
+    words = O.pack_windows(codes, kind, bits)
+    assert words.shape == (3, d * bits) and words.dtype == np.uint32
+    assert np.array_equal(O.unpack_windows(words, kind, d, bits), codes)
+
+
+def test_layout_worked_examples_keys_d128_2bit():
+    # Hand-derived from the documented key layout (d = 128, 2 bits, 4 words per lane):
+    # lane = 16*(c // 32) + t % 16; word = 4*lane + (c % 8) // 2;
+    # bit = 16*(c % 2) + 2*(4*(t // 16) + (c % 32) // 8).
+    P = lambda t, c: O.key_code_position(128, 2, t, c)
+    assert P(0, 0) == (0, 0)
+    assert P(0, 1) == (0, 16)
+    assert P(0, 2) == (1, 0)
+    assert P(0, 8) == (0, 2)
+    assert P(16, 0) == (0, 8)
+    assert P(1, 0) == (4, 0)
+    assert P(0, 32) == (64, 0)
+    assert P(31, 127) == (4 * (16 * 3 + 15) + 3, 16 + 2 * (4 + 3))
+    codes = np.zeros((32, 128), np.uint8)
+    codes[0, 0], codes[16, 0], codes[0, 1], codes[0, 8] = 1, 2, 3, 1
+    w = O.pack_windows(codes[None], "key", 2)[0]
+    assert w[0] == 0x1 | (2 << 8) | (3 << 16) | (1 << 2)
+    assert np.count_nonzero(w) == 1
+
+
+def test_layout_worked_examples_values_d128_2bit():
+    # value layout (d = 128, 2 bits): lane = 16*g + c % 16 with token t -> (g, j):
+    # t < 16: g = t // 4, j = t % 4; else g = (t - 16) // 4, j = 4 + t % 4;
+    # word = 4*lane + j // 2; bit = 16*(j % 2) + 2*(c // 16).
+    P = lambda t, c: O.value_code_position(128, 2, t, c)
+    assert P(0, 0) == (0, 0)
+    assert P(1, 0) == (0, 16)
+    assert P(2, 0) == (1, 0)
+    assert P(16, 0) == (2, 0)
+    assert P(4, 0) == (16 * 4, 0)
+    assert P(0, 16) == (0, 2)
+    assert P(0, 5) == (4 * 5, 0)
+    assert P(31, 127) == (4 * (16 * 3 + 15) + 3, 16 + 2 * 7)
+
+
+# ----------------------------------------------------------------------------- key codec (T4)
+def test_key_window_worked_example():
+    # one channel whose 32 rotated values are 0, 1, ..., 31 (2 bits, L = 3):
+    # mn = 0, mx = 31, s = fp16(31/3) = 10.3359375, m = 0;
+    # thresholds 5.16796875, 15.50390625, 25.83984375 -> codes by hand.
+    y = np.zeros((32, 1), np.float32)
+    y[:, 0] = np.arange(32)
+    codes, m16, s16 = O.key_window_quantize(y, 2)
+    assert O.f16_to_f32(m16)[0] == 0.0
+    assert O.f16_to_f32(s16)[0] == np.float32(np.float16(31.0 / 3.0))
+    expect = np.array([0] * 6 + [1] * 10 + [2] * 10 + [3] * 6)
+    assert np.array_equal(codes[:, 0], expect)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_key_window_bounds(bits):
+    L = 2**bits - 1
+    rng = np.random.default_rng(bits)
+    y = (rng.standard_normal((50, 32, 16)) * rng.uniform(0.1, 3, (50, 1, 16))
+         + rng.uniform(-2, 2, (50, 1, 16))).astype(np.float32)
+    codes, m16, s16 = O.key_window_quantize(y, bits)
+    m, s = O.f16_to_f64(m16), O.f16_to_f64(s16)
+    yhat = m[:, None, :] + s[:, None, :] * codes
+    # min token -> 0, max token -> L
+    amin, amax = y.argmin(1), y.argmax(1)
+    assert np.all(np.take_along_axis(codes, amin[:, None, :], 1) == 0)
+    assert np.all(np.take_along_axis(codes, amax[:, None, :], 1) == L)
+    # reconstruction bound: half a step plus the fp16 rounding of m and s
+    mn, mx = y.min(1).astype(np.float64), y.max(1).astype(np.float64)
+    slack = np.abs(m - mn) + L * np.abs(s - (mx - mn) / L) + 1e-6
+    err = np.abs(yhat - y)
+    assert np.all(err <= (s / 2 + slack)[:, None, :])
+    assert np.all(yhat >= m[:, None, :]) and np.all(yhat <= (m + L * s)[:, None, :] + 1e-9)
+
+
+# ----------------------------------------------------------------------------- value codec
+def test_lloyd_max_matches_textbook_table():
+    for line in open(os.path.join(GOLDEN, "lloyd_max_gaussian.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        left, mse = line.split("|")
+        parts = left.split()
+        n = int(parts[0])
+        pos = np.array([float(v) for v in parts[1:]])
+        lv = O.lloyd_max_gaussian(n)
+        assert np.allclose(lv[n // 2:], pos, atol=6e-4), (n, lv)
+        assert np.allclose(lv[: n // 2], -pos[::-1], atol=6e-4)
+        # MSE by numeric integration over the Gaussian density
+        x = np.linspace(-12, 12, 400001)
+        p = np.exp(-x * x / 2) / math.sqrt(2 * math.pi)
+        th = (lv[:-1] + lv[1:]) / 2
+        got = ((x - lv[np.searchsorted(th, x)]) ** 2 * p).sum() * (x[1] - x[0])
+        assert abs(got - float(mse)) < 2e-4 * max(1.0, float(mse) * 100)
+
+
+def test_value_scale_closed_forms():
+    d = 128
+    v = np.full((1, d), -3.0, np.float32)
+    assert O.value_scale_f32(v)[0] == np.float32(3.0)
+    e = np.zeros((1, d), np.float32)
+    e[0, 77] = 8.0
+    assert O.value_scale_f32(e)[0] == np.float32(8.0 / math.sqrt(d))
+    x = np.random.default_rng(0).standard_normal((100, d)).astype(np.float32)
+    ref = np.sqrt((x.astype(np.float64) ** 2).mean(1))
+    assert np.max(np.abs(O.value_scale_f32(x) - ref) / ref) < 1e-6
+
+
+def test_value_scale_tree_order():
+    # the stride-halving tree: pairs (i, i+d/2) first.  With d = 4 and values
+    # whose squares are 2^24, 1, -.. the tree ((a+c)+(b+d)) differs from a
+    # left-to-right sum; check the oracle follows the tree.
+    v = np.array([[4096.0, 1.0, 1.0, 1.0]], np.float32)   # squares 2^24, 1, 1, 1
+    S_tree = np.float32(np.float32(2**24 + 1.0) + np.float32(2.0))  # (a^2+c^2) + (b^2+d^2)
+    assert O.value_scale_f32(v)[0] == np.sqrt(S_tree / np.float32(4))
+
+
+def test_value_rotation_is_U_transpose_v():
+    d = 32
+    rng = np.random.default_rng(9)
+    U = rng.standard_normal((d, d)).astype(np.float32)   # deliberately not symmetric
+    v = rng.standard_normal((6, d)).astype(np.float32)
+    got = O.rotate_values_f32(v, U).astype(np.float64)
+    ref = v.astype(np.float64) @ U.astype(np.float64)     # (U^T v)_i = sum_k U[k][i] v_k
+    assert np.max(np.abs(got - ref)) < 1e-4
+    assert np.max(np.abs(got - v.astype(np.float64) @ U.T.astype(np.float64))) > 1e-2
+
+
+def test_value_worked_example_identity_rotation():
+    # U = I, one token with v = sigma * (0.1, -0.1, 1.2, -1.2, 0, ...) scaled so
+    # that sigma is exactly representable; 2-bit levels +-0.45288, +-1.5107,
+    # boundaries -0.98181, 0, 0.98181 -> codes 2, 1, 3, 0, 2 (0 >= 0 counts).
+    d = 64
+    v = np.zeros((1, 1, 1, d), np.float32)
+    v[..., :4] = [0.1, -0.1, 1.2, -1.2]
+    U = np.eye(d, dtype=np.float32)[None]
+    lv = O.value_codebook_f16(2)
+    words, sig16 = O.quantize_values(np.repeat(np.repeat(v, 32, 1), 1, 2), np.zeros((1, 32), np.uint8), U, lv, 2)
+    codes = O.unpack_windows(words, "value", d, 2)[0, 0, 0]
+    sig = O.f16_to_f32(sig16)[0, 0, 0]
+    assert sig == np.float32(np.float16(math.sqrt((0.01 + 0.01 + 1.44 + 1.44) / d)))
+    beta = O.value_boundaries_f32(lv)
+    assert np.array_equal(codes[0, :5], np.array(
+        [sum(x >= sig * b for b in beta) for x in [0.1, -0.1, 1.2, -1.2, 0.0]]))
+    # sigma * beta = (-0.2090, 0, 0.2090): 0.1 -> 2, -0.1 -> 1, 1.2 -> 3, -1.2 -> 0, 0 -> 2
+    assert list(codes[0, :5]) == [2, 1, 3, 0, 2]
+
+
+# ----------------------------------------------------------------------------- codec error (T5)
+def _codec_mse(cfg_id, kbits, vbits, seed=0):
+    cfg = synth.CONFIGS[cfg_id]
+    T = 256
+    tags = synth.modality_layout(cfg, seed, T)
+    k = synth.drifting_tensor(cfg, tags, seed, 0, 0, T)
+    v = synth.drifting_tensor(cfg, tags, seed, 1, 0, T)
+    d = cfg.head_dim
+    signs = synth.rademacher_signs(d, seed)
+    U = synth.value_rotations(d, seed)
+    kc, km, ks = O.quantize_keys(k, signs, kbits)
+    lv = O.value_codebook_f16(vbits)
+    vc, vs = O.quantize_values(v, tags, U, lv, vbits)
+    khat = O.dequantize_keys(kc, km, ks, signs, kbits)                   # [B][H][T][d]
+    vhat = O.dequantize_values(vc, vs, tags, U, lv, vbits)
+    kref = k.transpose(0, 2, 1, 3).astype(np.float64)
+    vref = v.transpose(0, 2, 1, 3).astype(np.float64)
+    rel = lambda a, b: np.mean((a - b) ** 2) / np.mean(b ** 2)
+    return rel(khat, kref), rel(vhat, vref)
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2])
+def test_four_bits_beat_two_bits(cfg_id):
+    k2, v2 = _codec_mse(cfg_id, 2, 2)
+    k4, v4 = _codec_mse(cfg_id, 4, 4)
+    assert k4 < 0.25 * k2 and v4 < 0.25 * v2
+    # values: per-token RMS scale + Lloyd-Max -> distortion near the textbook MSE
+    assert 0.08 < v2 < 0.16 and 0.005 < v4 < 0.02
+    # keys: window min-max at 2 bits keeps the error well below a global range
+    assert k2 < 0.2
+
+
+def test_value_codec_reaches_lloyd_max_distortion_on_gaussian():
+    d = 128
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal((1, 4096, 1, d)).astype(np.float32)
+    tags = np.zeros((1, 4096), np.uint8)
+    U = np.eye(d, dtype=np.float32)[None]
+    for bits, target in [(2, 0.1175), (4, 0.009497)]:
+        lv = O.value_codebook_f16(bits)
+        vc, vs = O.quantize_values(v, tags, U, lv, bits)
+        vhat = O.dequantize_values(vc, vs, tags, U, lv, bits)[0, 0]
+        mse = np.mean((vhat - v[0, :, 0].astype(np.float64)) ** 2)
+        assert abs(mse - target) < 0.06 * target, (bits, mse)
+
+
+# ----------------------------------------------------------------------------- attention (T7, T8)
+def _tiny_cache(seed=0, T=256, d=64, G=2):
+    cfg = synth.CONFIGS[1]
+    tags = synth.modality_layout(cfg, seed, T)
+    k = synth.drifting_tensor(cfg, tags, seed, 0, 0, T)
+    v = synth.drifting_tensor(cfg, tags, seed, 1, 0, T)
+    signs = synth.rademacher_signs(d, seed)
+    U = synth.value_rotations(d, seed)
+    lv = O.value_codebook_f16(2)
+    kc, km, ks = O.quantize_keys(k, signs, 2)
+    vc, vs = O.quantize_values(v, tags, U, lv, 2)
+    cache = dict(k_codes=kc, k_min=km, k_scale=ks, v_codes=vc, v_scale=vs, modality=tags,
+                 key_bits=2, value_bits=2)
+    return cache, signs, U, lv
+
+
+def test_attention_brute_force_equals_rotated_domain_formula():
+    # The fused kernel's restructuring: q . R^{-1} y_hat = (R^{-T} q) . y_hat and
+    # sum_t p_t U_m(t) v'_t = sum_m U_m (sum_{t in m} p_t v'_t).  Both sides in fp64.
+    cache, signs, U, lv = _tiny_cache()
+    q = synth.queries(synth.CONFIGS[1], 0)
+    out = O.decode_attention(q, [256], cache, signs, U, lv)
+    d, T = 64, 256
+    codes_k = O.unpack_windows(cache["k_codes"], "key", d, 2).reshape(1, 1, T, d)[0, 0]
+    yhat = (O.f16_to_f64(cache["k_min"])[0, 0].repeat(32, 0)
+            + O.f16_to_f64(cache["k_scale"])[0, 0].repeat(32, 0) * codes_k)
+    codes_v = O.unpack_windows(cache["v_codes"], "value", d, 2).reshape(T, d)
+    vprime = O.f16_to_f64(cache["v_scale"])[0, 0][:, None] * O.f16_to_f64(lv)[codes_v]
+    c = float(O.rotation_constant(d))
+    H = O.sylvester(d)
+    for h in range(2):
+        qr = (H @ (signs * q[0, h].astype(np.float64))) / (c * d)          # R^{-T} q
+        s = (yhat @ qr) / math.sqrt(d)
+        p = np.exp(s - s.max())
+        acc = np.zeros((3, d))
+        for m in range(3):
+            sel = cache["modality"][0] == m
+            acc[m] = p[sel] @ vprime[sel]
+        fused = sum(U[m].astype(np.float64) @ acc[m] for m in range(3)) / p.sum()
+        assert np.max(np.abs(fused - out[0, h])) < 1e-12 * max(1.0, np.max(np.abs(out[0, h])))
+
+
+def test_attention_special_cases():
+    cache, signs, U, lv = _tiny_cache()
+    d = 64
+    vals = O.dequantize_values(cache["v_codes"], cache["v_scale"], cache["modality"], U, lv, 2)[0, 0]
+    q = synth.queries(synth.CONFIGS[1], 1)
+    # one token: the output is that token's value
+    out1 = O.decode_attention(q, [1], cache, signs, U, lv)
+    assert np.allclose(out1[0, 0], vals[0], atol=1e-12)
+    # zero query: uniform attention -> mean of the values over the prefix
+    out0 = O.decode_attention(np.zeros_like(q), [100], cache, signs, U, lv)
+    assert np.allclose(out0[0, 1], vals[:100].mean(0), atol=1e-12)
+    # empty prefix -> zeros
+    oute = O.decode_attention(q, [0], cache, signs, U, lv)
+    assert np.all(oute == 0)
+
+
+def test_attention_identity_rotation_single_modality_is_plain_attention():
+    cache, signs, U, lv = _tiny_cache()
+    d, T = 64, 256
+    I3 = np.stack([np.eye(d, dtype=np.float32)] * 3)
+    q = synth.queries(synth.CONFIGS[1], 2)
+    out = O.decode_attention(q, [T], cache, signs, I3, lv)
+    keys = O.dequantize_keys(cache["k_codes"], cache["k_min"], cache["k_scale"], signs, 2)[0, 0]
+    codes_v = O.unpack_windows(cache["v_codes"], "value", d, 2).reshape(T, d)
+    vals = O.f16_to_f64(cache["v_scale"])[0, 0][:, None] * O.f16_to_f64(lv)[codes_v]
+    for h in range(2):
+        s = keys @ q[0, h].astype(np.float64) / 8.0
+        p = np.exp(s - s.max())
+        assert np.allclose(out[0, h], p @ vals / p.sum(), atol=1e-12)
+
+
+def test_gqa_head_mapping():
+    cfg = synth.CONFIGS[2]
+    cache = synth.random_packed_cache(cfg, 0, length=64)
+    d = cfg.head_dim
+    signs = synth.rademacher_signs(d, 0)
+    U = synth.value_rotations(d, 0)
+    lv = O.value_codebook_f16(2)
+    q = np.zeros((1, 16, d), np.float32)
+    out = O.decode_attention(q, [64], cache, signs, U, lv)
+    vals = O.dequantize_values(cache["v_codes"], cache["v_scale"], cache["modality"], U, lv, 2)
+    for h in range(16):
+        assert np.allclose(out[0, h], vals[0, h // 8].mean(0), atol=1e-12)
+    assert not np.allclose(out[0, 0], out[0, 8])
