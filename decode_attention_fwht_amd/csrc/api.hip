@@ -1,0 +1,264 @@
+// C ABI of libomnikv: contexts, argument validation, built-in codebook, launches.
+// The public contract (shapes, layouts, arithmetic, errors) is in include/omnikv.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "omnikv_internal.h"
+
+struct omnikv_ctx {
+  omnikv::Shape sh{};
+  omnikv::DeviceTables tb{};
+  std::vector<uint16_t> levels;  // fp16 value codebook
+  int device = 0;
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+omnikv_status fail(omnikv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+omnikv_status hip_fail(hipError_t e, const char* what) {
+  return fail(OMNIKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Lloyd-Max quantizer of a unit Gaussian with n levels: alternate the midpoint
+// condition for the thresholds and the centroid condition for the levels, the
+// centroid of N(0,1) on (a, b) being (phi(a) - phi(b)) / (Phi(b) - Phi(a)).
+std::vector<double> gaussian_lloyd_max(int n) {
+  auto pdf = [](double x) { return std::isinf(x) ? 0.0 : exp(-0.5 * x * x) * 0.3989422804014327; };
+  auto cdf = [](double x) { return std::isinf(x) ? (x > 0 ? 1.0 : 0.0) : 0.5 * erfc(-x * 0.7071067811865476); };
+  std::vector<double> lv(n), th(n + 1);
+  for (int i = 0; i < n; ++i) lv[i] = -2.0 + 4.0 * i / (n - 1);
+  for (int it = 0; it < 20000; ++it) {
+    th[0] = -INFINITY;
+    th[n] = INFINITY;
+    for (int i = 1; i < n; ++i) th[i] = 0.5 * (lv[i - 1] + lv[i]);
+    double change = 0.0;
+    for (int i = 0; i < n; ++i) {
+      const double c = (pdf(th[i]) - pdf(th[i + 1])) / (cdf(th[i + 1]) - cdf(th[i]));
+      change = std::max(change, fabs(c - lv[i]));
+      lv[i] = c;
+    }
+    if (change < 1e-15) break;
+  }
+  return lv;
+}
+
+uint16_t host_f16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
+float host_f16_value(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
+
+template <typename T>
+omnikv_status upload(T** dst, const T* src, size_t count) {
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), count * sizeof(T));
+  if (e != hipSuccess) return fail(OMNIKV_ENOMEM, "hipMalloc(%zu bytes): %s", count * sizeof(T), hipGetErrorString(e));
+  e = hipMemcpy(*dst, src, count * sizeof(T), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  return OMNIKV_OK;
+}
+
+void free_tables(omnikv::DeviceTables& tb) {
+  if (tb.signs) (void)hipFree(tb.signs);
+  if (tb.rotations) (void)hipFree(tb.rotations);
+  if (tb.boundaries) (void)hipFree(tb.boundaries);
+  if (tb.pair_table) (void)hipFree(tb.pair_table);
+  tb = omnikv::DeviceTables{};
+}
+
+omnikv_status check_ctx(const omnikv_ctx* ctx) {
+  if (!ctx) return fail(OMNIKV_EINVAL, "context is NULL");
+  return OMNIKV_OK;
+}
+
+omnikv_status check_chunk(int32_t batch, int64_t t0, int64_t n, int64_t t_cap) {
+  if (batch <= 0) return fail(OMNIKV_EINVAL, "batch must be positive (got %d)", batch);
+  if (t_cap <= 0 || t_cap % omnikv::kWindow) return fail(OMNIKV_EINVAL, "t_cap must be a positive multiple of 32 (got %lld)", (long long)t_cap);
+  if (t0 < 0 || t0 % omnikv::kWindow) return fail(OMNIKV_EINVAL, "t0 must be a non-negative multiple of 32 (got %lld)", (long long)t0);
+  if (n <= 0 || n % omnikv::kWindow) return fail(OMNIKV_EINVAL, "n must be a positive multiple of 32 (got %lld)", (long long)n);
+  if (t0 + n > t_cap) return fail(OMNIKV_EINVAL, "t0 + n = %lld exceeds t_cap = %lld", (long long)(t0 + n), (long long)t_cap);
+  return OMNIKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, const float* value_rotations,
+                            const uint16_t* value_codebook, omnikv_ctx** out) {
+  if (!out) return fail(OMNIKV_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!cfg || !key_signs || !value_rotations) return fail(OMNIKV_EINVAL, "cfg, key_signs and value_rotations are required");
+  const int d = cfg->head_dim;
+  if (cfg->window != omnikv::kWindow) return fail(OMNIKV_EUNSUPPORTED, "window must be 32 (got %d)", cfg->window);
+  if (d != 64 && d != 128) return fail(OMNIKV_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d);
+  if ((cfg->key_bits != 2 && cfg->key_bits != 4) || (cfg->value_bits != 2 && cfg->value_bits != 4))
+    return fail(OMNIKV_EUNSUPPORTED, "key_bits and value_bits must be 2 or 4 (got %d, %d)", cfg->key_bits, cfg->value_bits);
+  if (cfg->num_kv_heads <= 0 || cfg->num_q_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads)
+    return fail(OMNIKV_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", cfg->num_q_heads, cfg->num_kv_heads);
+  const int group = cfg->num_q_heads / cfg->num_kv_heads;
+  if (group > omnikv::kMaxGroup) return fail(OMNIKV_EUNSUPPORTED, "at most 8 query heads per KV head (got %d)", group);
+  const int M = cfg->num_modalities;
+  if (M < 1 || M > omnikv::kMaxModalities) return fail(OMNIKV_EINVAL, "num_modalities must be 1..3 (got %d)", M);
+  for (int i = 0; i < d; ++i)
+    if (key_signs[i] != 1 && key_signs[i] != -1) return fail(OMNIKV_EINVAL, "key_signs[%d] = %d is not +-1", i, key_signs[i]);
+  for (int m = 0; m < M; ++m) {
+    const float* U = value_rotations + static_cast<size_t>(m) * d * d;
+    double worst = 0.0;
+    for (int a = 0; a < d; ++a)
+      for (int b = a; b < d; ++b) {
+        double s = 0.0;
+        for (int k = 0; k < d; ++k) s += static_cast<double>(U[k * d + a]) * U[k * d + b];
+        worst = std::max(worst, fabs(s - (a == b ? 1.0 : 0.0)));
+      }
+    if (!(worst <= 1e-3)) return fail(OMNIKV_EINVAL, "value_rotations[%d] is not orthogonal (max |U^T U - I| = %g)", m, worst);
+  }
+  const int nl = 1 << cfg->value_bits;
+  std::vector<uint16_t> levels(nl);
+  if (value_codebook) {
+    for (int i = 0; i < nl; ++i) levels[i] = value_codebook[i];
+    for (int i = 0; i < nl; ++i)
+      if (!std::isfinite(host_f16_value(levels[i]))) return fail(OMNIKV_EINVAL, "value_codebook[%d] is not finite", i);
+    for (int i = 1; i < nl; ++i)
+      if (!(host_f16_value(levels[i]) > host_f16_value(levels[i - 1])))
+        return fail(OMNIKV_EINVAL, "value_codebook must be strictly ascending (entry %d)", i);
+  } else {
+    const std::vector<double> lv = gaussian_lloyd_max(nl);
+    for (int i = 0; i < nl; ++i) levels[i] = host_f16_bits(static_cast<float>(lv[i]));
+  }
+
+  auto* ctx = new (std::nothrow) omnikv_ctx();
+  if (!ctx) return fail(OMNIKV_ENOMEM, "out of host memory");
+  ctx->sh = omnikv::Shape{d, cfg->num_q_heads, cfg->num_kv_heads, group, cfg->key_bits, cfg->value_bits, M};
+  ctx->levels = levels;
+  (void)hipGetDevice(&ctx->device);
+
+  std::vector<float> sg(d);
+  for (int i = 0; i < d; ++i) sg[i] = static_cast<float>(key_signs[i]);
+  // all three rotation slots exist on the device; unused ones repeat U_0
+  std::vector<float> rot(static_cast<size_t>(omnikv::kMaxModalities) * d * d);
+  for (int m = 0; m < omnikv::kMaxModalities; ++m)
+    std::copy(value_rotations + static_cast<size_t>(m < M ? m : 0) * d * d,
+              value_rotations + static_cast<size_t>((m < M ? m : 0) + 1) * d * d, rot.begin() + static_cast<size_t>(m) * d * d);
+  std::vector<float> bnd(nl - 1);
+  for (int j = 0; j + 1 < nl; ++j) bnd[j] = (host_f16_value(levels[j]) + host_f16_value(levels[j + 1])) / 2.0f;
+  const int np = 1 << (2 * cfg->value_bits);
+  std::vector<uint32_t> pairs(np);
+  for (int idx = 0; idx < np; ++idx)
+    pairs[idx] = static_cast<uint32_t>(levels[idx & (nl - 1)]) | (static_cast<uint32_t>(levels[idx >> cfg->value_bits]) << 16);
+
+  omnikv_status st;
+  if ((st = upload(&ctx->tb.signs, sg.data(), sg.size())) != OMNIKV_OK ||
+      (st = upload(&ctx->tb.rotations, rot.data(), rot.size())) != OMNIKV_OK ||
+      (st = upload(&ctx->tb.boundaries, bnd.data(), bnd.size())) != OMNIKV_OK ||
+      (st = upload(&ctx->tb.pair_table, pairs.data(), pairs.size())) != OMNIKV_OK) {
+    free_tables(ctx->tb);
+    delete ctx;
+    return st;
+  }
+  *out = ctx;
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_destroy(omnikv_ctx* ctx) {
+  if (!ctx) return OMNIKV_OK;
+  free_tables(ctx->tb);
+  delete ctx;
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_value_codebook(const omnikv_ctx* ctx, uint16_t* levels) {
+  if (check_ctx(ctx) != OMNIKV_OK) return OMNIKV_EINVAL;
+  if (!levels) return fail(OMNIKV_EINVAL, "levels is NULL");
+  std::copy(ctx->levels.begin(), ctx->levels.end(), levels);
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_quantize_keys(const omnikv_ctx* ctx, const void* k, omnikv_dtype dt, int32_t batch,
+                                   int64_t t0, int64_t n, int64_t t_cap, uint32_t* k_codes, uint16_t* k_min,
+                                   uint16_t* k_scale, hipStream_t stream) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!k || !k_codes || !k_min || !k_scale) return fail(OMNIKV_EINVAL, "quantize_keys: NULL device pointer");
+  if (!aligned16(k) || !aligned16(k_codes) || !aligned16(k_min) || !aligned16(k_scale))
+    return fail(OMNIKV_EINVAL, "quantize_keys: device pointers must be 16-byte aligned");
+  if (dt != OMNIKV_F32 && dt != OMNIKV_BF16) return fail(OMNIKV_EINVAL, "quantize_keys: dtype must be F32 or BF16");
+  if ((st = check_chunk(batch, t0, n, t_cap)) != OMNIKV_OK) return st;
+  const hipError_t e = omnikv::launch_quantize_keys(ctx->sh, ctx->tb, k, dt == OMNIKV_BF16, batch, t0, n, t_cap,
+                                                    k_codes, k_min, k_scale, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize_keys launch");
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_quantize_values(const omnikv_ctx* ctx, const void* v, omnikv_dtype dt, const uint8_t* modality,
+                                     int32_t batch, int64_t t0, int64_t n, int64_t t_cap, uint32_t* v_codes,
+                                     uint16_t* v_scale, hipStream_t stream) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!v || !modality || !v_codes || !v_scale) return fail(OMNIKV_EINVAL, "quantize_values: NULL device pointer");
+  if (!aligned16(v) || !aligned16(modality) || !aligned16(v_codes) || !aligned16(v_scale))
+    return fail(OMNIKV_EINVAL, "quantize_values: device pointers must be 16-byte aligned");
+  if (dt != OMNIKV_F32 && dt != OMNIKV_BF16) return fail(OMNIKV_EINVAL, "quantize_values: dtype must be F32 or BF16");
+  if ((st = check_chunk(batch, t0, n, t_cap)) != OMNIKV_OK) return st;
+  const hipError_t e = omnikv::launch_quantize_values(ctx->sh, ctx->tb, v, dt == OMNIKV_BF16, modality, batch, t0, n,
+                                                      t_cap, v_codes, v_scale, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize_values launch");
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_decode_workspace_size(const omnikv_ctx* ctx, int32_t batch, int64_t max_len, int32_t num_splits,
+                                           size_t* bytes) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!bytes) return fail(OMNIKV_EINVAL, "bytes is NULL");
+  if (batch <= 0) return fail(OMNIKV_EINVAL, "batch must be positive (got %d)", batch);
+  if (max_len < 0) return fail(OMNIKV_EINVAL, "max_len must be >= 0");
+  if (num_splits < 0) return fail(OMNIKV_EINVAL, "num_splits must be >= 0");
+  *bytes = omnikv::plan_decode(ctx->sh, batch, max_len, num_splits).workspace_bytes;
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_decode_attention(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens, int32_t batch,
+                                      int64_t max_len, const uint32_t* k_codes, const uint16_t* k_min,
+                                      const uint16_t* k_scale, const uint32_t* v_codes, const uint16_t* v_scale,
+                                      const uint8_t* modality, int64_t t_cap, float softmax_scale, int32_t num_splits,
+                                      void* workspace, size_t workspace_bytes, float* out, hipStream_t stream) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!q || !seq_lens || !k_codes || !k_min || !k_scale || !v_codes || !v_scale || !modality || !out || !workspace)
+    return fail(OMNIKV_EINVAL, "decode_attention: NULL device pointer");
+  const void* ptrs[] = {q, seq_lens, k_codes, k_min, k_scale, v_codes, v_scale, modality, workspace, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(OMNIKV_EINVAL, "decode_attention: device pointers must be 16-byte aligned");
+  if (batch <= 0) return fail(OMNIKV_EINVAL, "batch must be positive (got %d)", batch);
+  if (t_cap <= 0 || t_cap % omnikv::kWindow) return fail(OMNIKV_EINVAL, "t_cap must be a positive multiple of 32");
+  if (max_len < 0 || max_len > t_cap) return fail(OMNIKV_EINVAL, "max_len must be in [0, t_cap] (got %lld)", (long long)max_len);
+  if (num_splits < 0) return fail(OMNIKV_EINVAL, "num_splits must be >= 0");
+  if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale)) return fail(OMNIKV_EINVAL, "softmax_scale must be finite and >= 0");
+  const omnikv::DecodePlan plan = omnikv::plan_decode(ctx->sh, batch, max_len, num_splits);
+  if (workspace_bytes < plan.workspace_bytes)
+    return fail(OMNIKV_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, plan.workspace_bytes);
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(ctx->sh.d));
+  const hipError_t e = omnikv::launch_decode(ctx->sh, ctx->tb, plan, q, seq_lens, batch, max_len, k_codes, k_min,
+                                             k_scale, v_codes, v_scale, modality, t_cap, scale, workspace, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_attention launch");
+  return OMNIKV_OK;
+}
+
+const char* omnikv_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

@@ -30,7 +30,8 @@ codes and metadata can be compared bit for bit):
   rotation   y = c_d * FWHT(D x): z = D x; butterfly stages h = 1, 2, ..., d/2,
              each mapping (z_i, z_{i+h}) -> (z_i + z_{i+h}, z_i - z_{i+h})
              for i with bit h clear; then one multiply by c_d = fp32(1/sqrt(d)).
-  key range  mn, mx over the 32 tokens of a window; m = fp16(mn);
+  key range  mn, mx over the 32 tokens of a window, each + 0 (so that a zero
+             extreme is +0); m = fp16(mn);
              s = fp16((mx - mn) / L) with L = 2^bits - 1 (IEEE fp32 division,
              fp16 round-to-nearest-even).
   key code   theta_j = m + s * (j + 1/2) (product and sum each rounded to fp32),
@@ -147,8 +148,11 @@ def value_code_position(d: int, bits: int, t: int, c: int):
     """(word, bit) of value code (window token t, channel c) in a window block.
 
     Lane l = 16 g + rho holds channels 16 u + rho (u < d/16) of the eight
-    tokens {4g .. 4g+3, 16+4g .. 16+4g+3} (index j = 0..7 in that order).
-    Word/slot per case below; j even in bits 0..15, j odd in bits 16..31.
+    tokens {4g .. 4g+3, 16+4g .. 16+4g+3} (index j = 0..7 in that order).  The
+    codes of tokens j = 2i and 2i + 1 of one channel form a pair p = 4 u + i of
+    2*bits bits (the even token in the low half of the pair); the lane's words
+    hold 16/bits pairs each, pair p in word p // (16/bits) at bit
+    2*bits*(p % (16/bits)).
     """
     u, rho = divmod(c, 16)
     if t < 16:
@@ -156,19 +160,12 @@ def value_code_position(d: int, bits: int, t: int, c: int):
     else:
         g, j = divmod(t - 16, 4)
         j += 4
-    i, e = divmod(j, 2)
-    per_lane = d * bits // 64
-    if (d, bits) == (128, 2):
-        lw, slot = i, u
-    elif (d, bits) == (64, 2):
-        lw, slot = i & 1, 4 * (i >> 1) + u
-    elif (d, bits) == (128, 4):
-        lw, slot = 4 * (u >> 2) + i, u & 3
-    elif (d, bits) == (64, 4):
-        lw, slot = i, u
-    else:
+    if (d, bits) not in ((64, 2), (64, 4), (128, 2), (128, 4)):
         raise ValueError((d, bits))
-    return (16 * g + rho) * per_lane + lw, 16 * e + bits * slot
+    p = 4 * u + j // 2
+    ppw = 16 // bits
+    per_lane = d * bits // 64
+    return (16 * g + rho) * per_lane + p // ppw, 2 * bits * (p % ppw) + bits * (j % 2)
 
 
 def _position_table(fn, d: int, bits: int):
@@ -221,8 +218,8 @@ def key_window_quantize(y: np.ndarray, bits: int):
     """
     L = 2**bits - 1
     y = np.asarray(y, dtype=F32)
-    mn = y.min(axis=-2)
-    mx = y.max(axis=-2)
+    mn = y.min(axis=-2) + F32(0)     # "+ 0": a zero extreme is +0
+    mx = y.max(axis=-2) + F32(0)
     step = (mx - mn) / F32(L)
     m16, s16 = f16_bits(mn), f16_bits(step)
     m, s = f16_to_f32(m16), f16_to_f32(s16)

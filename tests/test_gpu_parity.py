@@ -1,0 +1,227 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Bars (fixed by the target of the build):
+  * packed codes, k_min, k_scale, v_scale: bit-exact (the codec's fp32 order is
+    part of its definition and both sides follow it);
+  * decode outputs: per (sequence, query head) row, max |gpu - oracle| over the
+    channels divided by max |oracle| <= 1e-3 (fp32 accumulation on the GPU,
+    float64 brute force in the oracle over the same packed cache).
+Small sizes are compared in full; the configurations' full sizes are compared
+on sampled windows (codec) or sampled rows (decode).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import omnikv_oracle as O
+from decode_attention_fwht_amd import synth
+from tests.gpu_helpers import (bf16_tensor, cache_to_device, from_dev, make_context, row_errors, say,
+                               to_dev)
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+def _inputs(cfg, n, seed=0, t0=0):
+    tags = synth.modality_layout(cfg, seed, max(cfg.context, t0 + n))
+    k = synth.drifting_tensor(cfg, tags, seed, 0, t0, n)
+    v = synth.drifting_tensor(cfg, tags, seed, 1, t0, n)
+    return tags, k, v
+
+
+def _dev_kv(cfg, x):
+    import torch
+    return torch.from_numpy(x).cuda() if cfg.fp32_inputs else bf16_tensor(x)
+
+
+# ----------------------------------------------------------------------------- codec, full compare
+@pytest.mark.parametrize("cid,kbits,vbits,n", [
+    (1, 2, 2, 256), (1, 4, 4, 256), (2, 2, 2, 10240), (2, 4, 4, 2048), (3, 2, 2, 4096), (3, 4, 2, 4096),
+])
+def test_quantize_parity_full(cid, kbits, vbits, n):
+    import torch
+    cfg = synth.CONFIGS[cid]
+    say(f"[codec] cfg{cid} K{kbits}V{vbits} n={n}")
+    ctx, signs, U, lv = make_context(cfg, kbits, vbits)
+    tags, k, v = _inputs(cfg, n)
+    t_cap = n
+    cache = ctx.alloc_cache(cfg.batch, t_cap)
+    cache["modality"].copy_(to_dev(tags[:, :t_cap]))
+    ctx.quantize_keys(_dev_kv(cfg, k), 0, cache)
+    ctx.quantize_values(_dev_kv(cfg, v), 0, cache)
+    torch.cuda.synchronize()
+    kc, km, ks = O.quantize_keys(k, signs, kbits)
+    vc, vs = O.quantize_values(v, tags[:, :n], U, lv, vbits)
+    assert np.array_equal(from_dev(cache["k_min"], np.uint16), km)
+    assert np.array_equal(from_dev(cache["k_scale"], np.uint16), ks)
+    gk = from_dev(cache["k_codes"], np.uint32)
+    assert np.array_equal(gk, kc), f"{np.count_nonzero(gk != kc)} key words differ"
+    assert np.array_equal(from_dev(cache["v_scale"], np.uint16), vs)
+    gv = from_dev(cache["v_codes"], np.uint32)
+    if not np.array_equal(gv, vc):
+        gcodes = O.unpack_windows(gv, "value", cfg.head_dim, vbits)
+        ocodes = O.unpack_windows(vc, "value", cfg.head_dim, vbits)
+        raise AssertionError(f"{np.count_nonzero(gcodes != ocodes)} of {gcodes.size} value codes differ")
+    ctx.close()
+
+
+def test_quantize_offset_chunk_writes_only_its_windows():
+    import torch
+    cfg = synth.CONFIGS[2]
+    ctx, signs, U, lv = make_context(cfg)
+    t0, n, t_cap = 96, 160, 512
+    tags, k, v = _inputs(cfg, n, t0=t0)
+    cache = ctx.alloc_cache(cfg.batch, t_cap)
+    for key in ("k_codes", "v_codes"):
+        cache[key].fill_(0x5A5A5A5A)
+    for key in ("k_min", "k_scale", "v_scale"):
+        cache[key].fill_(0x5A5A)
+    cache["modality"].copy_(to_dev(tags[:, :t_cap]))
+    ctx.quantize_keys(_dev_kv(cfg, k), t0, cache)
+    ctx.quantize_values(_dev_kv(cfg, v), t0, cache)
+    torch.cuda.synchronize()
+    kc, km, ks = O.quantize_keys(k, signs, 2)
+    vc, vs = O.quantize_values(v, tags[:, t0:t0 + n], U, lv, 2)
+    w0, w1 = t0 // 32, (t0 + n) // 32
+    gkc = from_dev(cache["k_codes"], np.uint32)
+    assert np.array_equal(gkc[:, :, w0:w1], kc)
+    assert np.all(gkc[:, :, :w0] == 0x5A5A5A5A) and np.all(gkc[:, :, w1:] == 0x5A5A5A5A)
+    assert np.array_equal(from_dev(cache["k_min"], np.uint16)[:, :, w0:w1], km)
+    assert np.array_equal(from_dev(cache["v_codes"], np.uint32)[:, :, w0:w1], vc)
+    gvs = from_dev(cache["v_scale"], np.uint16)
+    assert np.array_equal(gvs[:, :, t0:t0 + n], vs)
+    assert np.all(gvs[:, :, :t0] == 0x5A5A) and np.all(gvs[:, :, t0 + n:] == 0x5A5A)
+    ctx.close()
+
+
+# ----------------------------------------------------------------------------- codec at full size, sampled
+@pytest.mark.parametrize("cid", [3, 5])
+def test_quantize_parity_prefill_sampled(cid):
+    import torch
+    cfg = synth.CONFIGS[cid]
+    n = cfg.prefill
+    say(f"[codec-sampled] cfg{cid} prefill {n} tokens x batch {cfg.batch}")
+    ctx, signs, U, lv = make_context(cfg)
+    tags, k, v = _inputs(cfg, n)
+    cache = ctx.alloc_cache(cfg.batch, n)
+    cache["modality"].copy_(to_dev(tags[:, :n]))
+    ctx.quantize_keys(_dev_kv(cfg, k), 0, cache)
+    ctx.quantize_values(_dev_kv(cfg, v), 0, cache)
+    torch.cuda.synchronize()
+    gk = from_dev(cache["k_codes"], np.uint32)
+    gkm = from_dev(cache["k_min"], np.uint16)
+    gks = from_dev(cache["k_scale"], np.uint16)
+    gv = from_dev(cache["v_codes"], np.uint32)
+    gvs = from_dev(cache["v_scale"], np.uint16)
+    rng = np.random.default_rng(cid)
+    picks = [(int(rng.integers(cfg.batch)), int(rng.integers(cfg.kv_heads)), int(rng.integers(n // 32)))
+             for _ in range(48)]
+    picks += [(cfg.batch - 1, cfg.kv_heads - 1, n // 32 - 1), (0, 0, 0)]
+    for b, h, w in picks:
+        ks_ = slice(32 * w, 32 * w + 32)
+        kc, km, ksc = O.quantize_keys(k[b:b + 1, ks_, h:h + 1], signs, cfg.key_bits)
+        assert np.array_equal(gk[b, h, w], kc[0, 0, 0]), (b, h, w)
+        assert np.array_equal(gkm[b, h, w], km[0, 0, 0]) and np.array_equal(gks[b, h, w], ksc[0, 0, 0])
+        vc, vs = O.quantize_values(v[b:b + 1, ks_, h:h + 1], tags[b:b + 1, ks_], U, lv, cfg.value_bits)
+        assert np.array_equal(gv[b, h, w], vc[0, 0, 0]), (b, h, w)
+        assert np.array_equal(gvs[b, h, ks_], vs[0, 0])
+    ctx.close()
+
+
+# ----------------------------------------------------------------------------- decode, full compare
+def _oracle_cache(cfg, ctx, signs, U, lv, T, kbits, vbits, seed=0):
+    tags, k, v = _inputs(cfg, T, seed)
+    kc, km, ks = O.quantize_keys(k, signs, kbits)
+    vc, vs = O.quantize_values(v, tags[:, :T], U, lv, vbits)
+    return dict(k_codes=kc, k_min=km, k_scale=ks, v_codes=vc, v_scale=vs, modality=tags[:, :T].copy(),
+                key_bits=kbits, value_bits=vbits, t_cap=T)
+
+
+@pytest.mark.parametrize("cid,kbits,vbits,T,ragged", [
+    (1, 2, 2, 256, False), (1, 2, 2, 256, True), (1, 4, 4, 256, False),
+    (2, 2, 2, 10240, False), (2, 2, 2, 10240, True), (2, 4, 4, 4096, True), (2, 2, 4, 2048, False),
+])
+def test_decode_parity_oracle_cache(cid, kbits, vbits, T, ragged):
+    import torch
+    cfg = synth.CONFIGS[cid]
+    say(f"[decode] cfg{cid} K{kbits}V{vbits} T={T} ragged={ragged}")
+    ctx, signs, U, lv = make_context(cfg, kbits, vbits)
+    cache = _oracle_cache(cfg, ctx, signs, U, lv, T, kbits, vbits)
+    B = cfg.batch
+    q = synth.queries(cfg, 3)
+    lens = np.full(B, T, np.int32)
+    if ragged:
+        lens[:] = [T - 17 - 5 * b for b in range(B)]
+    dcache = cache_to_device(cache)
+    out = ctx.decode(to_dev(q), to_dev(lens), T, dcache)
+    torch.cuda.synchronize()
+    got = from_dev(out)
+    ref = O.decode_attention(q, lens, cache, signs, U, lv)
+    err = row_errors(got, ref)
+    say(f"    max row error {err.max():.3e}")
+    assert err.max() <= TOL
+    ctx.close()
+
+
+def test_decode_edge_lengths():
+    import torch
+    cfg = synth.CONFIGS[2]
+    T = 256
+    ctx, signs, U, lv = make_context(cfg)
+    cache = _oracle_cache(cfg, ctx, signs, U, lv, T, 2, 2)
+    # batch of four sequences sharing the same cache rows: lengths 0, 1, 33, 256
+    B = 4
+    big = {k: (np.repeat(v, B, axis=0) if isinstance(v, np.ndarray) else v) for k, v in cache.items()}
+    q = np.random.default_rng(5).standard_normal((B, cfg.q_heads, cfg.head_dim)).astype(np.float32)
+    lens = np.array([0, 1, 33, 256], np.int32)
+    out = from_dev(ctx.decode(to_dev(q), to_dev(lens), T, cache_to_device(big)))
+    torch.cuda.synchronize()
+    ref = O.decode_attention(q, lens, big, signs, U, lv)
+    assert np.all(out[0] == 0.0)
+    err = row_errors(out[1:], ref[1:])
+    say(f"    max row error {err.max():.3e}")
+    assert err.max() <= TOL
+    ctx.close()
+
+
+def test_decode_split_invariance():
+    import torch
+    cfg = synth.CONFIGS[2]
+    T = 10240
+    ctx, signs, U, lv = make_context(cfg)
+    cache = cache_to_device(synth.random_packed_cache(cfg, 1, length=T))
+    q = to_dev(synth.queries(cfg, 7))
+    lens = to_dev(np.array([T - 3], np.int32))
+    outs = [from_dev(ctx.decode(q, lens, T, cache, num_splits=s)) for s in (1, 3, 0, 64, 320)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert row_errors(o, outs[0]).max() < 2e-6
+    ctx.close()
+
+
+# ----------------------------------------------------------------------------- decode at full size, sampled rows
+@pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (4, 2, 2), (5, 2, 2), (4, 4, 4)])
+def test_decode_parity_full_size_sampled(cid, kbits, vbits):
+    import torch
+    cfg = synth.CONFIGS[cid]
+    T = cfg.context
+    say(f"[decode-sampled] cfg{cid} K{kbits}V{vbits} B={cfg.batch} T={T}")
+    ctx, signs, U, lv = make_context(cfg, kbits, vbits)
+    cache = synth.random_packed_cache(cfg, 2, key_bits=kbits, value_bits=vbits)
+    lens = synth.seq_lens(cfg, ragged=True, seed=cid)
+    lens[0] = T
+    q = synth.queries(cfg, 4)
+    out = from_dev(ctx.decode(to_dev(q), to_dev(lens), T, cache_to_device(cache)))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cid)
+    rows = sorted({(int(rng.integers(cfg.batch)), int(rng.integers(cfg.q_heads))) for _ in range(5)}
+                  | {(0, 0), (cfg.batch - 1, cfg.q_heads - 1)})
+    ref = O.decode_attention(q, lens, cache, signs, U, lv, rows=rows)
+    bi = [r[0] for r in rows]
+    hi = [r[1] for r in rows]
+    err = row_errors(out[bi, hi], ref[bi, hi])
+    say(f"    rows {rows} max row error {err.max():.3e}")
+    assert err.max() <= TOL
+    assert np.all(np.isfinite(out))
+    ctx.close()

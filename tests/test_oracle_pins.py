@@ -126,16 +126,31 @@ def test_layout_worked_examples_keys_d128_2bit():
 def test_layout_worked_examples_values_d128_2bit():
     # value layout (d = 128, 2 bits): lane = 16*g + c % 16 with token t -> (g, j):
     # t < 16: g = t // 4, j = t % 4; else g = (t - 16) // 4, j = 4 + t % 4;
-    # word = 4*lane + j // 2; bit = 16*(j % 2) + 2*(c // 16).
+    # pair p = 4*(c // 16) + j // 2; word = 4*lane + p // 8; bit = 4*(p % 8) + 2*(j % 2).
     P = lambda t, c: O.value_code_position(128, 2, t, c)
     assert P(0, 0) == (0, 0)
-    assert P(1, 0) == (0, 16)
-    assert P(2, 0) == (1, 0)
-    assert P(16, 0) == (2, 0)
+    assert P(1, 0) == (0, 2)
+    assert P(2, 0) == (0, 4)
+    assert P(16, 0) == (0, 8)
     assert P(4, 0) == (16 * 4, 0)
-    assert P(0, 16) == (0, 2)
+    assert P(0, 16) == (0, 16)
     assert P(0, 5) == (4 * 5, 0)
-    assert P(31, 127) == (4 * (16 * 3 + 15) + 3, 16 + 2 * 7)
+    assert P(0, 32) == (1, 0)
+    assert P(31, 127) == (4 * 63 + 3, 30)
+    codes = np.zeros((32, 128), np.uint8)
+    codes[0, 0], codes[1, 0], codes[16, 0], codes[0, 16] = 3, 1, 2, 1
+    w = O.pack_windows(codes[None], "value", 2)[0]
+    assert w[0] == 3 | (1 << 2) | (2 << 8) | (1 << 16) and np.count_nonzero(w) == 1
+
+
+def test_layout_worked_examples_values_d128_4bit():
+    # 4 bits: a pair is one byte, four pairs per word: word = 8*lane + p // 4, bit = 8*(p % 4) + 4*(j % 2)
+    P = lambda t, c: O.value_code_position(128, 4, t, c)
+    assert P(0, 0) == (0, 0)
+    assert P(1, 0) == (0, 4)
+    assert P(16, 0) == (0, 16)
+    assert P(0, 16) == (1, 0)
+    assert P(31, 127) == (8 * 63 + 7, 28)
 
 
 # ----------------------------------------------------------------------------- key codec (T4)
