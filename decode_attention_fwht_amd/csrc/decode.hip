@@ -56,22 +56,40 @@ __device__ __forceinline__ float row_ror8(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
 }
 
-// reduce over the four 16-lane groups holding the same column: xor 32 then xor 16
+// Cross-half lane swaps.  Written in asm: the compiler's combine of the
+// permlane{16,32}_swap builtins can replace the second result by the first
+// (as if the operand were the same in every lane), which drops the lanes the
+// swap brings in.  Each asm swaps two registers in place and touches no memory.
+// The s_nop pairs give the wait states a VALU write needs before a permlane
+// reads the register, and a permlane result before the next VALU reads it
+// (the hazard recognizer does not look inside asm).
+//   swap32(a, b): lanes 32..63 of a <-> lanes 0..31 of b
+//   swap16(a, b): odd 16-lane rows of a <-> even rows of b
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// reduce over the four 16-lane groups holding the same column (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float group_max(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const uint32_t v = __builtin_bit_cast(uint32_t, x);
-  auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap32(a, b);  // a = lower half in both halves, b = upper half in both halves
+  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = __builtin_bit_cast(uint32_t, x);
+  b = a;
+  swap16(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float group_sum(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = __builtin_bit_cast(float, a[0]) + __builtin_bit_cast(float, a[1]);
-  const uint32_t v = __builtin_bit_cast(uint32_t, x);
-  auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return __builtin_bit_cast(float, b[0]) + __builtin_bit_cast(float, b[1]);
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap32(a, b);
+  x = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  a = __builtin_bit_cast(uint32_t, x);
+  b = a;
+  swap16(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
 template <int D>
