@@ -1,0 +1,241 @@
+"""Benchmark: K2V2 decode attention over the packed OmniKVQuant cache on one MI355X.
+
+One step = one decode step of the whole batch: the split-KV partial pass and the
+merge + batched inverse value rotation (omnikv_decode_partial then
+omnikv_decode_combine) over every cached token of every sequence.  The packed
+caches are built before timing by the library's own write path (keys and values
+of synthetic drifting K/V, quantized in prefill-sized chunks), and several
+independent caches are cycled so that a step never finds its cache in the 256 MB
+Infinity Cache: the timed bytes come from HBM.  The write path itself is timed
+separately on one prefill chunk per sequence and reported under "write_path".
+
+Prints one JSON line: the headline (effective KV GB/s of the decode step), the
+roofline of the partial kernel, the write-path timings and a CPU-oracle
+baseline on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from decode_attention_fwht_amd import binding, synth  # noqa: E402
+
+METRIC = "K2V2 decode-attention µs/step + effective KV HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def algorithmic_bytes(cfg, kbits, vbits, lens):
+    """Bytes one decode step must read: packed codes, window metadata, value
+    scales and modality tags of every cached token (queries/outputs excluded)."""
+    d, H = cfg.head_dim, cfg.kv_heads
+    per_token_head = d * kbits / 8 + d * vbits / 8 + 2 * 2 * d / 32 + 2
+    total = 0.0
+    for L in lens:
+        nwin = math.ceil(L / 32)
+        total += nwin * 32 * (H * per_token_head + 1)
+    return total
+
+
+def build_caches(ctx, cfg, nbuf, kbits, vbits, chunk=4096, seed=0):
+    import torch
+    T = cfg.context
+    caches = []
+    tags_np = synth.modality_layout(cfg, seed, T)
+    for k in range(nbuf):
+        c = ctx.alloc_cache(cfg.batch, T)
+        c["modality"].copy_(torch.from_numpy(tags_np))
+        for t0 in range(0, T, chunk):
+            n = min(chunk, T - t0)
+            kk = synth.drifting_tensor_device(cfg, tags_np, seed + 17 * k, 0, t0, n)
+            vv = synth.drifting_tensor_device(cfg, tags_np, seed + 17 * k, 1, t0, n)
+            ctx.quantize_keys(kk, t0, c)
+            ctx.quantize_values(vv, t0, c)
+            del kk, vv
+        caches.append(c)
+    torch.cuda.synchronize()
+    return caches, tags_np
+
+
+def time_write_path(ctx, cfg, tags_np, reps=20, seed=3):
+    """Time omnikv_quantize_keys / _values on one prefill chunk per sequence."""
+    import torch
+    n = cfg.prefill if cfg.prefill else 4096
+    c = ctx.alloc_cache(cfg.batch, n)
+    c["modality"].copy_(torch.from_numpy(tags_np[:, :n]))
+    kk = synth.drifting_tensor_device(cfg, tags_np, seed, 0, 0, n)
+    vv = synth.drifting_tensor_device(cfg, tags_np, seed, 1, 0, n)
+    for _ in range(3):
+        ctx.quantize_keys(kk, 0, c)
+        ctx.quantize_values(vv, 0, c)
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn, x in (("keys", ctx.quantize_keys, kk), ("values", ctx.quantize_values, vv)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn(x, 0, c)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        in_bytes = x.numel() * x.element_size()
+        res[name] = {"us_per_call": round(us, 2), "input_GBps": round(in_bytes / us / 1e3, 1)}
+    res["chunk"] = {"tokens_per_sequence": n, "batch": cfg.batch, "dtype": "fp32" if cfg.fp32_inputs else "bf16"}
+    return res
+
+
+def cpu_baseline(cfg, kbits, vbits, budget_s=15.0, seed=11):
+    """The CPU oracle (float64 brute force over the dequantized cache) on a bounded
+    sample of the same workload: whole (sequence, KV head) units of a synthetic
+    packed cache of this configuration's shape, until the time budget is spent."""
+    from oracle import omnikv_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    d = cfg.head_dim
+    signs = synth.rademacher_signs(d, seed)
+    U = synth.value_rotations(d, seed)
+    lv = O.value_codebook_f16(vbits)
+    one = synth.Config(**{**cfg.__dict__, "batch": 1})
+    q = synth.queries(cfg, seed)
+    done_units, done_bytes, t_used = 0, 0.0, 0.0
+    k = 0
+    while t_used < budget_s and done_units < cfg.batch * cfg.kv_heads:
+        cache = synth.random_packed_cache(one, seed + k, key_bits=kbits, value_bits=vbits)
+        b = k % cfg.batch
+        lens = np.array([cfg.context], np.int32)
+        for kv in range(cfg.kv_heads):
+            rows = [(0, kv * cfg.group + h) for h in range(cfg.group)]
+            t0 = time.perf_counter()
+            O.decode_attention(q[b:b + 1], lens, cache, signs, U, lv, rows=rows)
+            t_used += time.perf_counter() - t0
+            done_units += 1
+            done_bytes += algorithmic_bytes(synth.Config(**{**cfg.__dict__, "batch": 1, "kv_heads": 1}),
+                                            kbits, vbits, lens)
+            if t_used >= budget_s:
+                break
+        k += 1
+    gbs = done_bytes / t_used / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done_units} of {cfg.batch * cfg.kv_heads} (sequence, KV head) units at "
+                      f"{cfg.context} tokens, {cfg.group} query heads each, float64 brute force "
+                      f"({t_used:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload id (default 3: 16 x 32k, 16Q/2KV/d128)")
+    ap.add_argument("--kbits", type=int, default=2)
+    ap.add_argument("--vbits", type=int, default=2)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--buffers", type=int, default=0, help="independent caches cycled (0: enough to exceed the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(one GPU holds one shard of the KV heads; no collective is implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.config]
+    d = cfg.head_dim
+    signs = synth.rademacher_signs(d, 0)
+    U = synth.value_rotations(d, 0)
+    ctx = binding.Context(d, cfg.q_heads, cfg.kv_heads, args.kbits, args.vbits, signs, U)
+
+    lens_np = np.full(cfg.batch, cfg.context, np.int32)
+    alg = algorithmic_bytes(cfg, args.kbits, args.vbits, lens_np)
+    nbuf = args.buffers or max(2, math.ceil(2.5 * MALL_BYTES / alg))
+    caches, tags_np = build_caches(ctx, cfg, nbuf, args.kbits, args.vbits)
+    write_path = time_write_path(ctx, cfg, tags_np)
+
+    q = torch.from_numpy(synth.queries(cfg, 1)).cuda()
+    lens = torch.from_numpy(lens_np).cuda()
+    T = cfg.context
+    ws = torch.empty(ctx.workspace_size(cfg.batch, T, args.splits), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.batch, cfg.q_heads, d), dtype=torch.float32, device="cuda")
+
+    def step(i, evs=None):
+        c = caches[i % nbuf]
+        if evs is not None:
+            evs[0].record()
+        ctx.decode_partial(q, lens, T, c, ws, num_splits=args.splits)
+        if evs is not None:
+            evs[1].record()
+        ctx.decode_combine(lens, cfg.batch, T, ws, out, num_splits=args.splits)
+        if evs is not None:
+            evs[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = [e[0].elapsed_time(e[1]) for e in events]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in events]
+    step_ms = [e[0].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    us_step_med = float(np.median(step_ms)) * 1e3
+    part_avg_s = float(np.mean(part_ms)) / 1e3
+
+    value = alg / (ms_per_step / 1e3) / 1e9
+    achieved = alg / part_avg_s / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name} decode step (config {cfg.cid})",
+            "batch": cfg.batch, "q_heads": cfg.q_heads, "kv_heads": cfg.kv_heads, "head_dim": d,
+            "context": cfg.context, "codec": f"K{args.kbits}V{args.vbits}", "window": 32,
+            "cache_buffers": nbuf, "algorithmic_bytes_per_step": int(alg),
+        },
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_median_events": round(us_step_med, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernels_us": {"decode_partial_avg": round(part_avg_s * 1e6, 2),
+                       "decode_combine_avg": round(float(np.mean(comb_ms)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "write_path": write_path,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.kbits, args.vbits, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

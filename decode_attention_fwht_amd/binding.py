@@ -22,7 +22,7 @@ F32, BF16 = 0, 1
 EXPORTED = (
     "omnikv_create", "omnikv_destroy", "omnikv_value_codebook", "omnikv_quantize_keys",
     "omnikv_quantize_values", "omnikv_decode_workspace_size", "omnikv_decode_attention",
-    "omnikv_last_error",
+    "omnikv_decode_partial", "omnikv_decode_combine", "omnikv_last_error",
 )
 
 
@@ -57,7 +57,12 @@ def load() -> ctypes.CDLL:
     L.omnikv_decode_workspace_size.argtypes = [vp, i32, i64, i32, ctypes.POINTER(sz)]
     L.omnikv_decode_attention.argtypes = [vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, i64,
                                           ctypes.c_float, i32, vp, sz, vp, vp]
-    for name in EXPORTED[:-1]:
+    L.omnikv_decode_partial.argtypes = [vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, i64,
+                                        ctypes.c_float, i32, vp, sz, vp]
+    L.omnikv_decode_combine.argtypes = [vp, vp, i32, i64, i32, vp, sz, vp, vp]
+    for name in EXPORTED:
+        if name == "omnikv_last_error":
+            continue
         getattr(L, name).restype = ctypes.c_int
     L.omnikv_last_error.restype = ctypes.c_char_p
     L.omnikv_last_error.argtypes = []
@@ -174,4 +179,18 @@ class Context:
             _ptr(cache["k_scale"]), _ptr(cache["v_codes"]), _ptr(cache["v_scale"]), _ptr(cache["modality"]),
             cache["t_cap"], softmax_scale, num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
             _stream(stream)))
+        return out
+
+    def decode_partial(self, q, seq_lens, max_len: int, cache: dict, workspace, softmax_scale: float = 0.0,
+                       num_splits: int = 0, stream=None):
+        _check(load().omnikv_decode_partial(
+            self._h, _ptr(q), _ptr(seq_lens), int(q.shape[0]), max_len, _ptr(cache["k_codes"]),
+            _ptr(cache["k_min"]), _ptr(cache["k_scale"]), _ptr(cache["v_codes"]), _ptr(cache["v_scale"]),
+            _ptr(cache["modality"]), cache["t_cap"], softmax_scale, num_splits, _ptr(workspace),
+            workspace.numel(), _stream(stream)))
+
+    def decode_combine(self, seq_lens, batch: int, max_len: int, workspace, out, num_splits: int = 0,
+                       stream=None):
+        _check(load().omnikv_decode_combine(self._h, _ptr(seq_lens), batch, max_len, num_splits,
+                                            _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
         return out

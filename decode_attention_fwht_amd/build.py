@@ -14,6 +14,11 @@ LIB = os.path.join(PKG, "libomnikv.so")
 
 SOURCES = ["api.hip", "quantize_keys.hip", "quantize_values.hip", "decode.hip"]
 
+# The decode kernel keeps its matrix-core accumulators in ordinary VGPRs: with the
+# accumulation-register form the compiler shuttles all of them between register files
+# every window.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # the codec's fp32 order is part of its definition: no contraction into fma
@@ -51,7 +56,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"

@@ -75,6 +75,7 @@ omnikv_status upload(T** dst, const T* src, size_t count) {
 void free_tables(omnikv::DeviceTables& tb) {
   if (tb.signs) (void)hipFree(tb.signs);
   if (tb.rotations) (void)hipFree(tb.rotations);
+  if (tb.rotations_t) (void)hipFree(tb.rotations_t);
   if (tb.boundaries) (void)hipFree(tb.boundaries);
   if (tb.pair_table) (void)hipFree(tb.pair_table);
   tb = omnikv::DeviceTables{};
@@ -154,6 +155,11 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
   for (int m = 0; m < omnikv::kMaxModalities; ++m)
     std::copy(value_rotations + static_cast<size_t>(m < M ? m : 0) * d * d,
               value_rotations + static_cast<size_t>((m < M ? m : 0) + 1) * d * d, rot.begin() + static_cast<size_t>(m) * d * d);
+  std::vector<float> rot_t(rot.size());
+  for (int m = 0; m < omnikv::kMaxModalities; ++m)
+    for (int r = 0; r < d; ++r)
+      for (int c = 0; c < d; ++c)
+        rot_t[(static_cast<size_t>(m) * d + c) * d + r] = rot[(static_cast<size_t>(m) * d + r) * d + c];
   std::vector<float> bnd(nl - 1);
   for (int j = 0; j + 1 < nl; ++j) bnd[j] = (host_f16_value(levels[j]) + host_f16_value(levels[j + 1])) / 2.0f;
   const int np = 1 << (2 * cfg->value_bits);
@@ -164,6 +170,7 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
   omnikv_status st;
   if ((st = upload(&ctx->tb.signs, sg.data(), sg.size())) != OMNIKV_OK ||
       (st = upload(&ctx->tb.rotations, rot.data(), rot.size())) != OMNIKV_OK ||
+      (st = upload(&ctx->tb.rotations_t, rot_t.data(), rot_t.size())) != OMNIKV_OK ||
       (st = upload(&ctx->tb.boundaries, bnd.data(), bnd.size())) != OMNIKV_OK ||
       (st = upload(&ctx->tb.pair_table, pairs.data(), pairs.size())) != OMNIKV_OK) {
     free_tables(ctx->tb);
@@ -232,31 +239,91 @@ omnikv_status omnikv_decode_workspace_size(const omnikv_ctx* ctx, int32_t batch,
   return OMNIKV_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+omnikv_status check_decode(const omnikv_ctx* ctx, int32_t batch, int64_t max_len, int64_t t_cap, int32_t num_splits,
+                           size_t workspace_bytes, omnikv::DecodePlan* plan) {
+  if (batch <= 0) return fail(OMNIKV_EINVAL, "batch must be positive (got %d)", batch);
+  if (t_cap <= 0 || t_cap % omnikv::kWindow) return fail(OMNIKV_EINVAL, "t_cap must be a positive multiple of 32");
+  if (max_len < 0 || max_len > t_cap) return fail(OMNIKV_EINVAL, "max_len must be in [0, t_cap] (got %lld)", (long long)max_len);
+  if (num_splits < 0) return fail(OMNIKV_EINVAL, "num_splits must be >= 0");
+  *plan = omnikv::plan_decode(ctx->sh, batch, max_len, num_splits);
+  if (workspace_bytes < plan->workspace_bytes)
+    return fail(OMNIKV_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, plan->workspace_bytes);
+  return OMNIKV_OK;
+}
+
+omnikv_status decode_partial(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens, int32_t batch,
+                             int64_t max_len, const uint32_t* k_codes, const uint16_t* k_min, const uint16_t* k_scale,
+                             const uint32_t* v_codes, const uint16_t* v_scale, const uint8_t* modality, int64_t t_cap,
+                             float softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!q || !seq_lens || !k_codes || !k_min || !k_scale || !v_codes || !v_scale || !modality || !workspace)
+    return fail(OMNIKV_EINVAL, "decode: NULL device pointer");
+  const void* ptrs[] = {q, seq_lens, k_codes, k_min, k_scale, v_codes, v_scale, modality, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(OMNIKV_EINVAL, "decode: device pointers must be 16-byte aligned");
+  if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale)) return fail(OMNIKV_EINVAL, "softmax_scale must be finite and >= 0");
+  omnikv::DecodePlan plan;
+  if ((st = check_decode(ctx, batch, max_len, t_cap, num_splits, workspace_bytes, &plan)) != OMNIKV_OK) return st;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(ctx->sh.d));
+  const hipError_t e = omnikv::launch_decode_partial(ctx->sh, ctx->tb, plan, q, seq_lens, batch, max_len, k_codes, k_min,
+                                                     k_scale, v_codes, v_scale, modality, t_cap, scale, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
+  return OMNIKV_OK;
+}
+
+omnikv_status decode_combine(const omnikv_ctx* ctx, const int32_t* seq_lens, int32_t batch, int64_t max_len,
+                             int32_t num_splits, const void* workspace, size_t workspace_bytes, float* out,
+                             hipStream_t stream) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!seq_lens || !workspace || !out) return fail(OMNIKV_EINVAL, "decode_combine: NULL device pointer");
+  if (!aligned16(seq_lens) || !aligned16(workspace) || !aligned16(out))
+    return fail(OMNIKV_EINVAL, "decode_combine: device pointers must be 16-byte aligned");
+  omnikv::DecodePlan plan;
+  if ((st = check_decode(ctx, batch, max_len, max_len > 0 ? ((max_len + 31) / 32) * 32 : 32, num_splits,
+                         workspace_bytes, &plan)) != OMNIKV_OK)
+    return st;
+  const hipError_t e = omnikv::launch_decode_combine(ctx->sh, ctx->tb, plan, seq_lens, batch, workspace, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_combine launch");
+  return OMNIKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+omnikv_status omnikv_decode_partial(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens, int32_t batch,
+                                    int64_t max_len, const uint32_t* k_codes, const uint16_t* k_min,
+                                    const uint16_t* k_scale, const uint32_t* v_codes, const uint16_t* v_scale,
+                                    const uint8_t* modality, int64_t t_cap, float softmax_scale, int32_t num_splits,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_partial(ctx, q, seq_lens, batch, max_len, k_codes, k_min, k_scale, v_codes, v_scale, modality, t_cap,
+                        softmax_scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+omnikv_status omnikv_decode_combine(const omnikv_ctx* ctx, const int32_t* seq_lens, int32_t batch, int64_t max_len,
+                                    int32_t num_splits, const void* workspace, size_t workspace_bytes, float* out,
+                                    hipStream_t stream) {
+  return decode_combine(ctx, seq_lens, batch, max_len, num_splits, workspace, workspace_bytes, out, stream);
+}
+
 omnikv_status omnikv_decode_attention(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens, int32_t batch,
                                       int64_t max_len, const uint32_t* k_codes, const uint16_t* k_min,
                                       const uint16_t* k_scale, const uint32_t* v_codes, const uint16_t* v_scale,
                                       const uint8_t* modality, int64_t t_cap, float softmax_scale, int32_t num_splits,
                                       void* workspace, size_t workspace_bytes, float* out, hipStream_t stream) {
-  omnikv_status st;
-  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
-  if (!q || !seq_lens || !k_codes || !k_min || !k_scale || !v_codes || !v_scale || !modality || !out || !workspace)
-    return fail(OMNIKV_EINVAL, "decode_attention: NULL device pointer");
-  const void* ptrs[] = {q, seq_lens, k_codes, k_min, k_scale, v_codes, v_scale, modality, workspace, out};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(OMNIKV_EINVAL, "decode_attention: device pointers must be 16-byte aligned");
-  if (batch <= 0) return fail(OMNIKV_EINVAL, "batch must be positive (got %d)", batch);
-  if (t_cap <= 0 || t_cap % omnikv::kWindow) return fail(OMNIKV_EINVAL, "t_cap must be a positive multiple of 32");
-  if (max_len < 0 || max_len > t_cap) return fail(OMNIKV_EINVAL, "max_len must be in [0, t_cap] (got %lld)", (long long)max_len);
-  if (num_splits < 0) return fail(OMNIKV_EINVAL, "num_splits must be >= 0");
-  if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale)) return fail(OMNIKV_EINVAL, "softmax_scale must be finite and >= 0");
-  const omnikv::DecodePlan plan = omnikv::plan_decode(ctx->sh, batch, max_len, num_splits);
-  if (workspace_bytes < plan.workspace_bytes)
-    return fail(OMNIKV_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, plan.workspace_bytes);
-  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(ctx->sh.d));
-  const hipError_t e = omnikv::launch_decode(ctx->sh, ctx->tb, plan, q, seq_lens, batch, max_len, k_codes, k_min,
-                                             k_scale, v_codes, v_scale, modality, t_cap, scale, workspace, out, stream);
-  if (e != hipSuccess) return hip_fail(e, "decode_attention launch");
-  return OMNIKV_OK;
+  if (!out) return fail(OMNIKV_EINVAL, "decode_attention: NULL device pointer");
+  if (!aligned16(out)) return fail(OMNIKV_EINVAL, "decode_attention: device pointers must be 16-byte aligned");
+  const omnikv_status st = decode_partial(ctx, q, seq_lens, batch, max_len, k_codes, k_min, k_scale, v_codes, v_scale,
+                                          modality, t_cap, softmax_scale, num_splits, workspace, workspace_bytes, stream);
+  if (st != OMNIKV_OK) return st;
+  return decode_combine(ctx, seq_lens, batch, max_len, num_splits, workspace, workspace_bytes, out, stream);
 }
 
 const char* omnikv_last_error(void) { return g_error.c_str(); }

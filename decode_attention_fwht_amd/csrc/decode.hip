@@ -7,9 +7,11 @@
 // are batched across head outputs; no dense FP16 cache is built ([abstract]).
 //
 // Split-KV: kernel 1 (decode_partial) gives every (sequence, KV head, split of
-// consecutive windows) one 64-lane wave and writes (running max, sum, three
-// per-modality accumulators in rotated space); kernel 2 (decode_combine) merges
-// the splits with the log-sum-exp rule and applies sum_m U_m A_m once per head.
+// consecutive windows) one workgroup of four 64-lane waves, each wave a
+// contiguous run of windows; the block merges its waves and writes (running max,
+// sum, three per-modality accumulators in rotated space); kernel 2
+// (decode_combine) merges the splits with the log-sum-exp rule and applies
+// sum_m U_m A_m once per head.
 //
 // Per 32-token window the wave issues two matrix-core contractions
 // (v_mfma_f32_16x16x32_f16):
@@ -29,6 +31,8 @@
 //   Value levels come from a per-context table of fp16 level pairs indexed by
 //   two packed codes (LDS, conflict-free for 2-bit).
 #include <math.h>
+
+#include <type_traits>
 
 #include "omnikv_internal.h"
 
@@ -92,6 +96,25 @@ __device__ __forceinline__ float group_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// 2^x by the hardware instruction (results below 2^-126 flush to zero; the softmax
+// weights it produces are relative to a running max, so those are negligible)
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp16 pair (lo half, hi half) = (fp16(p0 s0 - c0), fp16(p1 s1 - c1)): each half one fused
+// multiply-add of an fp32 by an fp16 (both halves of s) minus an fp16 (halves of c),
+// rounded once to fp16 (v_fma_mix{lo,hi}_f16).  The leading wait state covers an operand
+// just written by a transcendental instruction (the hazard recognizer does not look
+// inside asm).
+__device__ __forceinline__ uint32_t mix_pair(float p0, float p1, uint32_t s, uint32_t c) {
+  uint32_t d = 0u;
+  asm("s_nop 0\n\t"
+      "v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %0, %4, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
+      : "+&v"(d)
+      : "v"(p0), "v"(s), "v"(c), "v"(p1));
+  return d;
+}
+
 template <int D>
 struct RhtConst;
 template <>
@@ -143,104 +166,214 @@ struct PartialArgs {
   int64_t t_cap;
   int64_t max_len;   // host bound of seq_lens; device lengths are clamped to it
   float scale_log2;  // softmax scale * log2(e)
-  int wps, splits;
+  int wpw, splits;   // windows per wave; splits (= workgroups) per (sequence, KV head)
   float2* ws_ml;     // [unit][split][8] (max, sum) in log2 units
   uint32_t* ws_mask; // [unit][split] modalities present
   float* ws_acc;     // [unit][split][M][8][D]
 };
 
-template <int M>
-__device__ __forceinline__ void acc_mfma(float4_t (&acc)[kMaxModalities][8], const uint4_t (&av)[8],
-                                         uint4_t bv, int nu) {
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (u < nu) acc[M][u] = mfma16(av[u], bv, acc[M][u]);
-}
+// ---------------------------------------------------------------------------------------
+// Window staging.  Each wave owns a ring of LDS slots; a slot holds everything one
+// 32-token window needs: [key block | value block | k_scale | k_min | v_scale | tags].
+// Slots are filled by asynchronous global->LDS copies (global_load_lds_dwordx4, 16 bytes
+// per lane), ring depth - 1 windows ahead of the one being computed, so no registers are
+// held by loads in flight.  The copies are tracked by the vmcnt counter only; the waits
+// before reading a slot are explicit.
+constexpr int kWaves = 4;  // waves per workgroup; each owns its own consecutive windows
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
+struct Slot {
+  static constexpr int KBYTES = 4 * D * KB;  // 32 tokens x D codes x KB bits
+  static constexpr int VBYTES = 4 * D * VB;
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_V = KBYTES;
+  static constexpr int OFF_S = KBYTES + VBYTES;      // k_scale, 2 D bytes
+  static constexpr int OFF_M = OFF_S + 2 * D;        // k_min, 2 D bytes
+  static constexpr int OFF_SIG = OFF_M + 2 * D;      // v_scale of the 32 tokens, 64 bytes
+  static constexpr int OFF_TAG = OFF_SIG + 64;       // modality of the 32 tokens, 32 bytes
+  static constexpr int BYTES = ((OFF_TAG + 32) + 127) / 128 * 128;
+  static constexpr int NK = (KBYTES + 1023) / 1024;  // copies of the key block
+  static constexpr int NV = (VBYTES + 1023) / 1024;
+  static constexpr int MISC_LANES = D / 8 + D / 8 + 4 + 2;
+  static constexpr int COPIES = NK + NV + 1;          // copy instructions per window
+};
+
+// One 16-byte-per-lane global->LDS copy (lane l writes lds_addr + 16 l).  Issued in asm so
+// the compiler's wait insertion does not see it: it cannot tell ring slots apart and would
+// drain every copy in flight before each slot read.  The copy writes no VGPR; its only
+// consumers are the slot reads that follow an explicit wait_vmcnt.
+// M0 (which the copy reads at issue for its LDS base) is saved and restored inside the
+// asm, so the compiler's view of M0 is unchanged.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Ring depth: the deepest of 4, 3, 2 slots per wave that keeps two workgroups per CU
+// within the 160 KB of LDS (ring + accumulator stash + small tables).
+template <int D, int KB, int VB>
+struct Lds {
+  static constexpr int STASH = kWaves * 2 * kMaxGroup * D * 4;  // two fp32 [8][D] slots per wave
+  static constexpr int fits(int ring) { return kWaves * ring * Slot<D, KB, VB>::BYTES + STASH + 2048 <= 80 * 1024; }
+  static constexpr int RING = fits(4) ? 4 : (fits(3) ? 3 : 2);
+  static constexpr int RING_BYTES = kWaves * RING * Slot<D, KB, VB>::BYTES;
+  static constexpr int DYN = RING_BYTES + STASH;
+};
+
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs a) {
+  using SG = Slot<D, KB, VB>;
+  using KO = KeyOp<D, KB>;
+  constexpr int RING = Lds<D, KB, VB>::RING;
   constexpr int NC = D / 64;        // channels per lane in the query rotation
   constexpr int NS = D / 32;        // K-steps of the score contraction
   constexpr int NU = D / 16;        // channel tiles of the value contraction
-  constexpr int KW = KeyOp<D, KB>::words;
+  constexpr int KW = KO::words;     // key words per lane
   constexpr int VW = D * VB / 64;   // value words per lane
   constexpr int PPW = 16 / VB;      // value code pairs per word
   constexpr uint32_t PMASK = (1u << (2 * VB)) - 1u;
-  using KO = KeyOp<D, KB>;
+  constexpr int L = SG::COPIES;
 
-  __shared__ float q_lds[kMaxGroup][D];
-  __shared__ float a_lds[16][kMaxGroup];
+  // Dynamic LDS: [ring: kWaves x RING slots][stash: kWaves x 2 x [8][D] fp32].  Only the
+  // asm copies write the ring, and a static LDS array that no visible code stores to
+  // would let the optimizer treat its contents as undefined and fold the slot reads.
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring_mem[];
+  auto ring_slot = [&](int wv, int slot) -> uint8_t* { return ring_mem + (wv * RING + slot) * SG::BYTES; };
+  float* const stash_mem = reinterpret_cast<float*>(ring_mem + Lds<D, KB, VB>::RING_BYTES);
+  // the rotated queries live in the stash area until the window loop starts
+  float (*q_lds)[D] = reinterpret_cast<float (*)[D]>(stash_mem);
+  __shared__ float zmax_lds[kMaxGroup];
   __shared__ uint32_t vtab[1 << (2 * VB)];
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int unit = blockIdx.y;                     // b * hkv + kvh
-  const int split = blockIdx.x;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int len = static_cast<int>(min<int64_t>(max<int64_t>(a.seq_lens[b], 0), a.max_len));
+  const int len = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(min<int64_t>(max<int64_t>(a.seq_lens[b], 0), a.max_len)));
   const int nwin = (len + kWindow - 1) / kWindow;
-  const int wbeg = split * a.wps;
-  const int wend = min(nwin, wbeg + a.wps);
-  const size_t pidx = static_cast<size_t>(unit) * a.splits + split;
-  if (wbeg >= wend) {
-    if (lane < kMaxGroup) a.ws_ml[pidx * kMaxGroup + lane] = make_float2(-INFINITY, 0.0f);
-    if (lane == 0) a.ws_mask[pidx] = 0u;
-    return;
-  }
+  const int wbeg = (blockIdx.x * kWaves + wave) * a.wpw;  // this wave's run of windows
+  const int wend = min(nwin, wbeg + a.wpw);
+  const int nw = max(0, wend - wbeg);
   const int n = lane & 15, g = lane >> 4, h = n & 7, part = n >> 3;
-  const bool head_ok = h < a.group;
   const int64_t nwin_cap = a.t_cap / kWindow;
+  const size_t unit_win = static_cast<size_t>(unit) * nwin_cap;
 
-  for (int i = lane; i < (1 << (2 * VB)); i += 64) vtab[i] = a.pair_table[i];
+  // ---- per-lane copy descriptors: source = base + window * stride (bytes)
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit_win * SG::KBYTES + 16 * lane;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit_win * SG::VBYTES + 16 * lane;
+  const uint8_t* mbase = nullptr;
+  uint32_t mstride = 0;
+  {
+    const int l0 = D / 8, l1 = D / 4, l2 = D / 4 + 4;
+    if (lane < l0) {
+      mbase = reinterpret_cast<const uint8_t*>(a.k_scale) + unit_win * (2 * D) + 16 * lane;
+      mstride = 2 * D;
+    } else if (lane < l1) {
+      mbase = reinterpret_cast<const uint8_t*>(a.k_min) + unit_win * (2 * D) + 16 * (lane - l0);
+      mstride = 2 * D;
+    } else if (lane < l2) {
+      mbase = reinterpret_cast<const uint8_t*>(a.v_scale) + static_cast<size_t>(unit) * a.t_cap * 2 + 16 * (lane - l1);
+      mstride = 64;
+    } else {
+      mbase = a.modality + static_cast<size_t>(b) * a.t_cap + 16 * (lane - l2);
+      mstride = 32;
+    }
+  }
+  auto issue = [&](int w, int slot) {
+    const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_slot(wave, slot)));
+#pragma unroll
+    for (int x = 0; x < SG::NK; ++x)
+      if (1024 * x + 16 * lane < SG::KBYTES)
+        copy16_to_lds(kbase + static_cast<size_t>(w) * SG::KBYTES + 1024 * x, dst + SG::OFF_K + 1024 * x);
+#pragma unroll
+    for (int x = 0; x < SG::NV; ++x)
+      if (1024 * x + 16 * lane < SG::VBYTES)
+        copy16_to_lds(vbase + static_cast<size_t>(w) * SG::VBYTES + 1024 * x, dst + SG::OFF_V + 1024 * x);
+    if (lane < SG::MISC_LANES) copy16_to_lds(mbase + static_cast<size_t>(w) * mstride, dst + SG::OFF_S);
+  };
 
-  // ---- query rotation q' = c_d H D q, once per head, scaled to log2 units
-  float zmax_mine = 0.0f;
+  // ---- the queries of this wave's two heads
+  const int h0 = 2 * wave;
+  float qv[2][NC];
   {
     float sg[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) sg[c] = a.signs[lane + 64 * c];
-    for (int hh = 0; hh < kMaxGroup; ++hh) {
-      float z[NC];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int hh = h0 + j;
       const bool ok = hh < a.group;
       const float* qp = a.q + (static_cast<size_t>(b) * a.hq + kvh * a.group + (ok ? hh : 0)) * D;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) z[c] = ok ? qp[lane + 64 * c] * sg[c] : 0.0f;
-#pragma unroll
-      for (int st = 1; st < 64; st <<= 1) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const float p = __shfl_xor(z[c], st, 64);
-          z[c] = (lane & st) ? (p - z[c]) : (z[c] + p);
-        }
-      }
-      if constexpr (NC == 2) {
-        const float x0 = z[0] + z[1], x1 = z[0] - z[1];
-        z[0] = x0;
-        z[1] = x1;
-      }
-      float am = 0.0f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        z[c] = z[c] * RhtConst<D>::value * a.scale_log2;
-        q_lds[hh][lane + 64 * c] = z[c];
-        am = fmaxf(am, fabsf(z[c]));
-      }
-#pragma unroll
-      for (int st = 32; st >= 1; st >>= 1) am = fmaxf(am, __shfl_xor(am, st, 64));
-      if (hh == h) zmax_mine = am;
+      for (int c = 0; c < NC; ++c) qv[j][c] = qp[lane + 64 * c] * (ok ? sg[c] : 0.0f);
     }
   }
+
+  for (int i = tid; i < (1 << (2 * VB)); i += kWaves * 64) vtab[i] = a.pair_table[i];
+
+  // ---- query rotation q' = c_d H D q (two heads per wave), scaled to log2 units
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float z[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) z[c] = qv[j][c];
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float p = __shfl_xor(z[c], st, 64);
+        z[c] = (lane & st) ? (p - z[c]) : (z[c] + p);
+      }
+    }
+    if constexpr (NC == 2) {
+      const float x0 = z[0] + z[1], x1 = z[0] - z[1];
+      z[0] = x0;
+      z[1] = x1;
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      z[c] = z[c] * RhtConst<D>::value * a.scale_log2;
+      q_lds[h0 + j][lane + 64 * c] = z[c];
+      am = fmaxf(am, fabsf(z[c]));
+    }
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1) am = fmaxf(am, __shfl_xor(am, st, 64));
+    if (lane == 0) zmax_lds[h0 + j] = am;
+  }
   __syncthreads();
+
   // Z_h: power of two with |q'/Z_h| <= 1
   int zexp = 0;
-  if (zmax_mine > 0.0f) (void)frexpf(zmax_mine, &zexp);
+  {
+    const float zm = zmax_lds[h];
+    if (zm > 0.0f) (void)frexpf(zm, &zexp);
+  }
   const float zinv = ldexpf(1.0f, -zexp);
   const float zh = ldexpf(1.0f, zexp);
   const float zfac = ldexpf(1.0f, zexp + 24);
 
-  // ---- per-lane operand constants.  Lane (n, g) feeds column n: head h, part hi/lo.
-  // score operand for K-step s, dword i = channels c0, c0+1 with c0 = g*D/4 + 8 s + 2 i
+  // ---- operand constants.  Lane (n, g) feeds column n: head h, part hi (0) or lo (1);
+  // K-step s, dword i hold channels c0, c0 + 1 with c0 = g*D/4 + 8 s + 2 i.
+  //   alpha/beta/gamma: score operand  fp16 split of (q^ s) scaled by 2^-(KB*peff(s))
+  //   bqa:              k_min operand  q^ hi (part 0) or lo (part 1)
   half2_t alpha[NS][4], beta[NS][4], gamma[NS][4];
-  uint4_t bqa[NS];  // q^ hi (part 0) or lo (part 1) for the k_min contraction
+  uint4_t bqa[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     uint32_t bw[4];
@@ -249,17 +382,15 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
       half2_t al, be, ga, qa;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int c = g * (D / 4) + 8 * s + 2 * i + e;
-        const float qh = q_lds[h][c] * zinv;                               // |qh| <= 1
-        const float qt = qh * ldexpf(1.0f, -KB * KO::peff(s));              // exact scaling
+        const float qh = q_lds[h][g * (D / 4) + 8 * s + 2 * i + e] * zinv;   // |qh| <= 1
+        const float qt = qh * ldexpf(1.0f, -KB * KO::peff(s));               // exact scaling
         const _Float16 th = static_cast<_Float16>(qt);
         const _Float16 tl = static_cast<_Float16>(qt - static_cast<float>(th));
         al[e] = th;
         be[e] = part ? th : static_cast<_Float16>(0.0f);
         ga[e] = part ? tl : static_cast<_Float16>(0.0f);
         const _Float16 hh = static_cast<_Float16>(qh);
-        const _Float16 hl = static_cast<_Float16>(qh - static_cast<float>(hh));
-        qa[e] = part ? hl : hh;
+        qa[e] = part ? static_cast<_Float16>(qh - static_cast<float>(hh)) : hh;
       }
       alpha[s][i] = al;
       beta[s][i] = be;
@@ -268,239 +399,350 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(PartialArgs a) {
     }
     bqa[s] = uint4_t{bw[0], bw[1], bw[2], bw[3]};
   }
+  __syncthreads();  // q_lds is stash space from here on
 
+  // ---- running state.  Scores, l_part and the accumulators are relative to m_ref (per
+  // column, log2 units).  One modality's accumulator is resident in registers; the
+  // others wait in this wave's two stash slots, each with the m_ref it was stored at.
   float m_ref = -INFINITY;
   float l_part = 0.0f;
-  float4_t acc[kMaxModalities][8];
+  float4_t acc[NU];
 #pragma unroll
-  for (int m = 0; m < kMaxModalities; ++m)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[m][u] = float4_t{0.f, 0.f, 0.f, 0.f};
-  uint32_t seen = 0u;
+  for (int u = 0; u < NU; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+  int cur = -1;                   // resident modality (wave-uniform); -1 before the first window
+  int occ0 = -1, occ1 = -1;       // modality held by stash slot 0 / 1 (wave-uniform)
+  float mst0 = 0.0f, mst1 = 0.0f; // m_ref at which slot 0 / 1 was stored (per column)
+  float* const my_stash = stash_mem + wave * (2 * kMaxGroup * D);
+  const uint32_t lo_mask = part ? 0xFFFFFFFFu : 0u;
 
-  const size_t unit_win = static_cast<size_t>(unit) * nwin_cap;
-  const uint16_t* vsc = a.v_scale + static_cast<size_t>(unit) * a.t_cap;
-  const uint8_t* tags = a.modality + static_cast<size_t>(b) * a.t_cap;
-
-  for (int wb = wbeg; wb < wend; wb += 16) {
-    // ---- q^ . m_w for 16 windows: rows = windows, K = channels
-    {
-      float4_t ca = float4_t{0.f, 0.f, 0.f, 0.f};
-      const int wr = wb + n;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        uint4_t am = uint4_t{0u, 0u, 0u, 0u};
-        if (wr < wend)
-          am = *reinterpret_cast<const uint4_t*>(a.k_min + (unit_win + wr) * D + g * (D / 4) + 8 * s);
-        ca = mfma16(am, bqa[s], ca);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = ca[i] + row_ror8(ca[i]);
-        if (part == 0) a_lds[4 * g + i][h] = v * zh;
-      }
+  // Lane (n, g) of tile u holds channels 16u + 4g .. +3 of column n; a stash slot keeps
+  // the hi + lo sum, and a restored tile goes back into the hi columns.
+  auto make_resident = [&](int t) {
+    if (cur < 0) {
+      cur = t;
+      return;
     }
-    __syncthreads();
-    const int wlast = min(wend, wb + 16);
-    for (int w = wb; w < wlast; ++w) {
-      const size_t wi = unit_win + w;
-      // ---- loads
-      uint32_t kw[KW];
-      {
-        const uint4_t* kp = reinterpret_cast<const uint4_t*>(a.k_codes + wi * (D * KB) + lane * KW);
-#pragma unroll
-        for (int x = 0; x < KW / 4; ++x) {
-          const uint4_t t = kp[x];
-          kw[4 * x] = t[0]; kw[4 * x + 1] = t[1]; kw[4 * x + 2] = t[2]; kw[4 * x + 3] = t[3];
-        }
-        if constexpr (KW == 2) {
-          const uint2 t = *reinterpret_cast<const uint2*>(a.k_codes + wi * (D * KB) + lane * KW);
-          kw[0] = t.x; kw[1] = t.y;
-        }
-      }
-      uint32_t sw[D / 8];  // k_scale pairs for channels g*D/4 .. g*D/4 + D/4 - 1
-      {
-        const uint4_t* sp = reinterpret_cast<const uint4_t*>(a.k_scale + wi * D + g * (D / 4));
-#pragma unroll
-        for (int x = 0; x < D / 32; ++x) {
-          const uint4_t t = sp[x];
-          sw[4 * x] = t[0]; sw[4 * x + 1] = t[1]; sw[4 * x + 2] = t[2]; sw[4 * x + 3] = t[3];
-        }
-      }
-      uint32_t vw[VW];
-      {
-        if constexpr (VW >= 4) {
-          const uint4_t* vp = reinterpret_cast<const uint4_t*>(a.v_codes + wi * (D * VB) + lane * VW);
-#pragma unroll
-          for (int x = 0; x < VW / 4; ++x) {
-            const uint4_t t = vp[x];
-            vw[4 * x] = t[0]; vw[4 * x + 1] = t[1]; vw[4 * x + 2] = t[2]; vw[4 * x + 3] = t[3];
-          }
-        } else {
-          const uint2 t = *reinterpret_cast<const uint2*>(a.v_codes + wi * (D * VB) + lane * VW);
-          vw[0] = t.x; vw[1] = t.y;
-        }
-      }
-      const int tokb = w * kWindow;
-      uint2 sig2[2];
-      uint32_t tg[2];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        sig2[tau] = *reinterpret_cast<const uint2*>(vsc + tokb + 16 * tau + 4 * g);
-        tg[tau] = *reinterpret_cast<const uint32_t*>(tags + tokb + 16 * tau + 4 * g);
-      }
-
-      // ---- scores
-      float4_t cs[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        uint32_t bq[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const half2_t sv = __builtin_bit_cast(half2_t, sw[4 * s + i]);
-          const half2_t t1 = beta[s][i] * sv;
-          const half2_t t2 = __builtin_elementwise_fma(alpha[s][i], sv, -t1);
-          bq[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(gamma[s][i], sv, t2));
-        }
-        const uint4_t bqv = uint4_t{bq[0], bq[1], bq[2], bq[3]};
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          uint4_t ak;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ak[i] = (kw[KO::word(tau, s, i)] >> KO::shift(tau, s, i)) & KO::mask(s);
-          cs[tau] = mfma16(ak, bqv, cs[tau]);
-        }
-      }
-      const float aw = a_lds[w - wb][h];
-      float sc[2][4];
-      float wmax = -INFINITY;
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = cs[tau][i] + row_ror8(cs[tau][i]);
-          float x = fmaf(v, zfac, aw);
-          if (tokb + 16 * tau + 4 * g + i >= len) x = -INFINITY;
-          sc[tau][i] = x;
-          wmax = fmaxf(wmax, x);
-        }
-      }
-      wmax = group_max(wmax);
-      const float m_new = fmaxf(m_ref, wmax);
-      const bool grow = m_new > m_ref + kLazyRescale;
-      if (__any(grow)) {
-        const float alf = grow ? exp2f(m_ref - m_new) : 1.0f;
-        if (grow) m_ref = m_new;
-        l_part *= alf;
-#pragma unroll
-        for (int m = 0; m < kMaxModalities; ++m)
-#pragma unroll
-          for (int u = 0; u < NU; ++u) acc[m][u] *= alf;
-      }
-      // ---- probabilities (relative to m_ref) times the value scale, split hi/lo
-      float pt[2][4];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool valid = tokb + 16 * tau + 4 * g + i < len;
-          const float p = valid ? exp2f(sc[tau][i] - m_ref) : 0.0f;
-          l_part += p;
-          const uint32_t sbits = (i < 2 ? sig2[tau].x : sig2[tau].y) >> (16 * (i & 1));
-          // tokens past the length may hold any bits: keep them out of the products
-          pt[tau][i] = valid ? p * f16_value(static_cast<uint16_t>(sbits & 0xFFFFu)) : 0.0f;
-        }
-      }
-      uint32_t bvw[4];
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        half2_t hv;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float x = pt[qd >> 1][2 * (qd & 1) + e];
-          const _Float16 hi = static_cast<_Float16>(x);
-          const float rest = part ? static_cast<float>(hi) : 0.0f;
-          hv[e] = static_cast<_Float16>(x - rest);
-        }
-        bvw[qd] = __builtin_bit_cast(uint32_t, hv);
-      }
-      // ---- value levels: one table read per pair of codes
-      uint4_t av[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (u < NU) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int p = 4 * u + i;
-            av[u][i] = vtab[(vw[p / PPW] >> (2 * VB * (p % PPW))) & PMASK];
-          }
-        } else {
-          av[u] = uint4_t{0u, 0u, 0u, 0u};
-        }
-      }
-      // ---- modality routing
-      const uint32_t t0tag = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(tg[0] & 0xFFu));
-      const uint32_t rep = t0tag * 0x01010101u;
-      const bool uniform = __all((tg[0] == rep) && (tg[1] == rep));
-      if (uniform) {
-        const uint4_t bv = uint4_t{bvw[0], bvw[1], bvw[2], bvw[3]};
-        if (t0tag == 0) acc_mfma<0>(acc, av, bv, NU);
-        else if (t0tag == 1) acc_mfma<1>(acc, av, bv, NU);
-        else acc_mfma<2>(acc, av, bv, NU);
-        seen |= 1u << t0tag;
-      } else {
-#pragma unroll
-        for (int m = 0; m < kMaxModalities; ++m) {
-          // keep the fp16 halves of tokens whose tag is m
-          uint32_t bm[4];
-          bool any = false;
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const uint32_t tw = tg[qd >> 1];
-            const uint32_t t0 = (tw >> (16 * (qd & 1))) & 0xFFu;
-            const uint32_t t1 = (tw >> (16 * (qd & 1) + 8)) & 0xFFu;
-            const uint32_t msk = (t0 == static_cast<uint32_t>(m) ? 0x0000FFFFu : 0u) |
-                                 (t1 == static_cast<uint32_t>(m) ? 0xFFFF0000u : 0u);
-            any = any || (msk != 0u);
-            bm[qd] = bvw[qd] & msk;
-          }
-          if (__any(any)) {
-            const uint4_t bv = uint4_t{bm[0], bm[1], bm[2], bm[3]};
-            if (m == 0) acc_mfma<0>(acc, av, bv, NU);
-            else if (m == 1) acc_mfma<1>(acc, av, bv, NU);
-            else acc_mfma<2>(acc, av, bv, NU);
-            seen |= 1u << m;
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: partial results of this split
-  const float l = group_sum(l_part);
-  if (lane < kMaxGroup && lane < a.group) a.ws_ml[pidx * kMaxGroup + lane] = make_float2(m_ref, l);
-  if (lane == 0) a.ws_mask[pidx] = seen;
-#pragma unroll
-  for (int m = 0; m < kMaxModalities; ++m) {
-    if (!(seen & (1u << m))) continue;
+    const int x = (occ0 == t) ? 0 : (occ1 == t) ? 1 : (occ0 < 0 ? 0 : 1);
+    const bool restore = (x == 0 ? occ0 : occ1) == t;
+    const float f = restore ? exp2f((x == 0 ? mst0 : mst1) - m_ref) : 0.0f;  // <= 1
+    float* sp = my_stash + (x * kMaxGroup + h) * D + 4 * g;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       float4_t v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[m][u][i] + row_ror8(acc[m][u][i]);
-      if (part == 0 && head_ok) {
-        float* dst = a.ws_acc + ((pidx * kMaxModalities + m) * kMaxGroup + h) * D + 16 * u + 4 * g;
-        *reinterpret_cast<float4_t*>(dst) = v;
+      for (int i = 0; i < 4; ++i) v[i] = acc[u][i] + row_ror8(acc[u][i]);
+      float4_t* tp = reinterpret_cast<float4_t*>(sp + 16 * u);
+      float4_t old = float4_t{0.f, 0.f, 0.f, 0.f};
+      if (restore) old = *tp;
+      if (part == 0) *tp = v;
+      const float fp = part == 0 ? f : 0.0f;
+      acc[u] = float4_t{old[0] * fp, old[1] * fp, old[2] * fp, old[3] * fp};
+    }
+    if (x == 0) {
+      occ0 = cur;
+      mst0 = m_ref;
+    } else {
+      occ1 = cur;
+      mst1 = m_ref;
+    }
+    cur = t;
+  };
+
+  // One visit of a 32-token window for modality m.  Only tokens of modality m (and inside
+  // the sequence) count; a window holding several modalities is visited once per
+  // modality.  The all-tokens-count case runs straight through.
+  auto window = [&](const uint8_t* slot, int tokb, int m) {
+    const uint32_t tg0 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 4 * g);
+    const uint32_t tg1 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 16 + 4 * g);
+    // ---- k_min term: every A row is m_w, so each lane's results all equal q^ . m_w
+    float4_t cm = float4_t{0.f, 0.f, 0.f, 0.f};
+    // ---- scores^T = codes . (q^ (.) s_w)
+    float4_t cs[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
+    uint32_t kw[KW];
+#pragma unroll
+    for (int x = 0; x < KW / 4; ++x) {
+      const uint4_t t = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_K + 16 * (KW / 4) * lane + 16 * x);
+      kw[4 * x] = t[0]; kw[4 * x + 1] = t[1]; kw[4 * x + 2] = t[2]; kw[4 * x + 3] = t[3];
+    }
+    if constexpr (KW == 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_K + 8 * lane);
+      kw[0] = t.x; kw[1] = t.y;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint4_t sv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_S + g * (D / 2) + 16 * s);
+      const uint4_t mv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_M + g * (D / 2) + 16 * s);
+      cm = mfma16(mv4, bqa[s], cm);
+      uint32_t bq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // copy the element out first: bit_cast of an ext-vector element subscript is
+        // lowered as element 0 by this compiler
+        const uint32_t svw = sv4[i];
+        const half2_t sv = __builtin_bit_cast(half2_t, svw);
+        const half2_t t1 = beta[s][i] * sv;
+        const half2_t t2 = __builtin_elementwise_fma(alpha[s][i], sv, -t1);
+        bq[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(gamma[s][i], sv, t2));
       }
+      const uint4_t bqv = uint4_t{bq[0], bq[1], bq[2], bq[3]};
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        uint4_t ak;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ak[i] = (kw[KO::word(tau, s, i)] >> KO::shift(tau, s, i)) & KO::mask(s);
+        cs[tau] = mfma16(ak, bqv, cs[tau]);
+      }
+    }
+    // ---- which tokens count: all of them unless the window is partial or mixed
+    const uint32_t rep = static_cast<uint32_t>(m) * 0x01010101u;
+    const bool all_count = (tokb + kWindow <= len) && __all((tg0 == rep) && (tg1 == rep));
+    // ---- scores relative to m_ref (the first window of a wave takes absolute scores)
+    const float aw = (cm[0] + row_ror8(cm[0])) * zh;
+    const bool fresh = m_ref == -INFINITY;
+    const float base = fresh ? aw : aw - m_ref;
+    float sc[2][4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[tau][i] = fmaf(cs[tau][i] + row_ror8(cs[tau][i]), zfac, base);
+    uint32_t keep[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    if (!all_count) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const uint32_t tw = tau ? tg1 : tg0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (tokb + 16 * tau + 4 * g + i < len) && ((tw >> (8 * i)) & 0xFFu) == static_cast<uint32_t>(m);
+          if (!ok) sc[tau][i] = -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          keep[2 * tau + e] = (sc[tau][2 * e] == -INFINITY ? 0u : 0x0000FFFFu) |
+                              (sc[tau][2 * e + 1] == -INFINITY ? 0u : 0xFFFF0000u);
+        }
+      }
+    }
+    float wmax = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wmax = fmaxf(wmax, sc[tau][i]);
+    // every visit has a counted token, so wmax is finite
+    wmax = group_max(wmax);
+    const bool grow = fresh || wmax > kLazyRescale;
+    if (__any(grow)) {
+      const float delta = grow ? wmax : 0.0f;
+      // the first window's accumulators are still zero (and -delta may overflow exp2)
+      const float alf = fresh ? 0.0f : exp2_raw(-delta);
+      if (grow) m_ref = (fresh ? 0.0f : m_ref) + delta;
+      l_part *= alf;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] *= alf;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[tau][i] -= delta;
+    }
+    // ---- probabilities times the value scale, as fp16 hi (part 0) or lo (part 1)
+    const uint2 sig0 = *reinterpret_cast<const uint2*>(slot + SG::OFF_SIG + 2 * (4 * g));
+    const uint2 sig1 = *reinterpret_cast<const uint2*>(slot + SG::OFF_SIG + 2 * (16 + 4 * g));
+    uint32_t bvw[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int tau = qd >> 1;
+      const uint32_t sw = qd == 0 ? sig0.x : qd == 1 ? sig0.y : qd == 2 ? sig1.x : sig1.y;
+      const float p0 = exp2_raw(sc[tau][2 * (qd & 1)]);
+      const float p1 = exp2_raw(sc[tau][2 * (qd & 1) + 1]);
+      l_part += p0;
+      l_part += p1;
+      // hi = fp16(p sigma); part 1 lanes then take lo = fp16(p sigma - hi).  Tokens that
+      // do not count have p = 0 but may hold any scale bits: the keep mask clears them.
+      const uint32_t hi = mix_pair(p0, p1, sw, 0u);
+      bvw[qd] = mix_pair(p0, p1, sw, hi & lo_mask) & keep[qd];
+    }
+    // ---- value contraction into the resident accumulator, one channel tile at a time
+    uint32_t vw[VW];
+#pragma unroll
+    for (int x = 0; x < VW / 4; ++x) {
+      const uint4_t t = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_V + 16 * (VW / 4) * lane + 16 * x);
+      vw[4 * x] = t[0]; vw[4 * x + 1] = t[1]; vw[4 * x + 2] = t[2]; vw[4 * x + 3] = t[3];
+    }
+    if constexpr (VW == 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_V + 8 * lane);
+      vw[0] = t.x; vw[1] = t.y;
+    }
+    // byte offsets of the pair-table entries: 2-bit values take four offsets per dword
+    // at once (low nibbles of the bytes, then high nibbles)
+    uint32_t vx[VW], vy[VW];
+    if constexpr (VB == 2) {
+#pragma unroll
+      for (int x = 0; x < VW; ++x) {
+        vx[x] = (vw[x] << 2) & 0x3C3C3C3Cu;
+        vy[x] = (vw[x] >> 2) & 0x3C3C3C3Cu;
+      }
+    }
+    auto entry = [&](int pp) -> uint32_t {
+      if constexpr (VB == 2) {
+        const uint32_t src = (pp & 1) ? vy[pp / 8] : vx[pp / 8];
+        const int byte = (pp % 8) / 2;
+        const uint32_t off = byte == 3 ? (src >> 24) : ((src >> (8 * byte)) & 0xFFu);
+        return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(vtab) + off);
+      } else {
+        return vtab[(vw[pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
+      }
+    };
+    const uint4_t bv = uint4_t{bvw[0], bvw[1], bvw[2], bvw[3]};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      uint4_t av;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = entry(4 * u + i);
+      acc[u] = mfma16(av, bv, acc[u]);
+    }
+  };
+
+  // ---- visit order.  The wave's windows go in chunks of up to 64; within a chunk, one
+  // pass per modality present (the resident one first) over the windows holding it, in
+  // window order.  The ring is filled along the same sequence of visits, across passes.
+  for (int c0 = 0; c0 < nw; c0 += 64) {
+    const int cn = min(64, nw - c0);
+    uint64_t pm[kMaxModalities];
+    {
+      uint32_t bits = 0u;
+      if (lane < cn) {
+        const int tok0 = (wbeg + c0 + lane) * kWindow;
+        const uint4_t* tp = reinterpret_cast<const uint4_t*>(a.modality + static_cast<size_t>(b) * a.t_cap + tok0);
+        const uint4_t t01 = tp[0], t23 = tp[1];
+        const uint32_t tw[8] = {t01[0], t01[1], t01[2], t01[3], t23[0], t23[1], t23[2], t23[3]};
+#pragma unroll
+        for (int j = 0; j < kWindow; ++j) {
+          const uint32_t tg = (tw[j / 4] >> (8 * (j % 4))) & 0xFFu;
+          if (tok0 + j < len && tg < static_cast<uint32_t>(kMaxModalities)) bits |= 1u << tg;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < kMaxModalities; ++m) pm[m] = __ballot((bits >> m) & 1u);
+    }
+    // pass order: the resident modality first, then the others
+    int ord[kMaxModalities];
+    {
+      const int c = cur < 0 ? 0 : cur;
+#pragma unroll
+      for (int k = 0; k < kMaxModalities; ++k) ord[k] = (c + k) % kMaxModalities;
+    }
+    int total = 0;
+#pragma unroll
+    for (int m = 0; m < kMaxModalities; ++m) total += __builtin_popcountll(pm[m]);
+    // cursors over the visit sequence: (pass k, windows left in that pass)
+    int fk = 0, ck = 0;
+    uint64_t fmask = pm[ord[0]], cmask = pm[ord[0]];
+    auto advance = [&](int& k, uint64_t& mask, int& mod) -> int {
+      while (mask == 0u) {
+        ++k;
+        mask = pm[ord[k < kMaxModalities ? k : 0]];
+      }
+      mod = ord[k];
+      const int w = __builtin_ctzll(mask);
+      mask &= mask - 1u;
+      return w;
+    };
+    auto issue_next = [&](int item) {
+      int mod;
+      const int w = advance(fk, fmask, mod);
+      issue(wbeg + c0 + w, item % RING);
+    };
+#pragma unroll
+    for (int i = 0; i < RING - 1; ++i)
+      if (i < total) issue_next(i);
+    for (int i = 0; i < total; ++i) {
+      if (i + RING - 1 < total) issue_next(i + RING - 1);
+      // wait for this visit's copies: later visits' copies may stay in flight
+      const int ahead = min(RING - 1, total - 1 - i);
+      if (ahead >= 3) wait_vmcnt<3 * L>();
+      else if (ahead == 2) wait_vmcnt<2 * L>();
+      else if (ahead == 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+      int m;
+      const int w = advance(ck, cmask, m);
+      if (m != cur) make_resident(m);
+      window(ring_slot(wave, i % RING), (wbeg + c0 + w) * kWindow, m);
+    }
+  }
+
+  // ---- epilogue: merge the block's waves into one partial.  Every copy of this wave
+  // has been waited for, so its own ring region is free: the resident accumulator goes
+  // there, next to the two stash slots.
+  __shared__ float2 ml_lds[kWaves][kMaxGroup];
+  __shared__ float ref_lds[kWaves][3][kMaxGroup];  // reference max of: resident, slot 0, slot 1
+  __shared__ int mod_lds[kWaves][3];                // their modalities (-1: none)
+  const float l = group_sum(l_part);
+  if (lane < kMaxGroup) {  // lane < 8: column = head, part 0
+    ml_lds[wave][lane] = make_float2(m_ref, l);
+    ref_lds[wave][0][lane] = m_ref;
+    ref_lds[wave][1][lane] = mst0;
+    ref_lds[wave][2][lane] = mst1;
+  }
+  if (lane == 0) {
+    mod_lds[wave][0] = cur;
+    mod_lds[wave][1] = occ0;
+    mod_lds[wave][2] = occ1;
+  }
+  float* const res_mem = reinterpret_cast<float*>(ring_slot(wave, 0));  // [8][D]
+  if (cur >= 0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      float4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = acc[u][i] + row_ror8(acc[u][i]);
+      if (part == 0) *reinterpret_cast<float4_t*>(res_mem + h * D + 16 * u + 4 * g) = v;
+    }
+  }
+  __syncthreads();
+  const size_t pidx = static_cast<size_t>(unit) * a.splits + blockIdx.x;
+  uint32_t present = 0u;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (mod_lds[v][j] >= 0) present |= 1u << mod_lds[v][j];
+  if (tid < kMaxGroup) {
+    float lsum = 0.0f, mb = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+      if (ml_lds[v][tid].y > 0.0f) mb = fmaxf(mb, ml_lds[v][tid].x);
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+      if (ml_lds[v][tid].y > 0.0f) lsum += exp2f(ml_lds[v][tid].x - mb) * ml_lds[v][tid].y;
+    if (tid < a.group) a.ws_ml[pidx * kMaxGroup + tid] = make_float2(mb, lsum);
+  }
+  if (tid == 0) a.ws_mask[pidx] = present;
+#pragma unroll
+  for (int m = 0; m < kMaxModalities; ++m) {
+    if (!(present & (1u << m))) continue;
+    for (int e = tid; e < a.group * D; e += kWaves * 64) {
+      const int hh = e / D;
+      float mb = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v)
+        if (ml_lds[v][hh].y > 0.0f) mb = fmaxf(mb, ml_lds[v][hh].x);
+      float sum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          if (mod_lds[v][j] != m) continue;
+          const float* src = j == 0 ? reinterpret_cast<const float*>(ring_slot(v, 0))
+                                    : stash_mem + (v * 2 + (j - 1)) * kMaxGroup * D;
+          sum += src[e] * exp2f(ref_lds[v][j][hh] - mb);
+        }
+      }
+      a.ws_acc[(pidx * kMaxModalities + m) * kMaxGroup * D + e] = sum;
     }
   }
 }
 
 struct CombineArgs {
-  const int32_t* seq_lens;
-  const float* rotations;  // [M][d][d]
+  const float* rotations_t;  // [3][d][d], Ut[m][k][c] = U_m[c][k]
   int hq, hkv, group, modalities, splits;
   const float2* ws_ml;
   const uint32_t* ws_mask;
@@ -508,75 +750,129 @@ struct CombineArgs {
   float* out;
 };
 
-// One block per (sequence, KV head): merge the splits, then out = sum_m U_m A_m.
+// One block per (query head, sequence x KV head), one thread per channel:
+// log-sum-exp merge of the splits, then out = sum_m U_m A_m for this head.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
-  __shared__ float A[kMaxModalities][kMaxGroup][D];
-  __shared__ float wsum[kMaxGroup];
-  const int unit = blockIdx.x;
+__global__ __launch_bounds__(D) void decode_combine_kernel(CombineArgs a) {
+  constexpr int CH = D;  // splits handled per chunk (one per thread)
+  __shared__ float A[kMaxModalities][D];
+  __shared__ float wgt[CH];
+  __shared__ uint32_t msk[CH];
+  __shared__ float red[D / 64];
+  const int h = blockIdx.x, unit = blockIdx.y;
+  if (h >= a.group) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int tid = threadIdx.x;
+  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
   const size_t base = static_cast<size_t>(unit) * a.splits;
-  // (head, channel) pairs handled by this thread
-  for (int e = tid; e < kMaxGroup * D; e += blockDim.x) {
-    const int h = e / D, c = e % D;
-    float mx = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) {
-      const float2 ml = a.ws_ml[(base + s) * kMaxGroup + h];
-      if (h < a.group && ml.y > 0.0f) mx = fmaxf(mx, ml.x);
-    }
-    float lsum = 0.0f;
-    float acc[kMaxModalities] = {0.0f, 0.0f, 0.0f};
-    if (h < a.group && mx > -INFINITY) {
-      for (int s = 0; s < a.splits; ++s) {
-        const float2 ml = a.ws_ml[(base + s) * kMaxGroup + h];
-        if (!(ml.y > 0.0f)) continue;
-        const float wgt = exp2f(ml.x - mx);
-        lsum += wgt * ml.y;
-        const uint32_t msk = a.ws_mask[base + s];
-#pragma unroll
-        for (int m = 0; m < kMaxModalities; ++m)
-          if (msk & (1u << m))
-            acc[m] += wgt * a.ws_acc[(((base + s) * kMaxModalities + m) * kMaxGroup + h) * D + c];
-      }
-    }
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-#pragma unroll
-    for (int m = 0; m < kMaxModalities; ++m) A[m][h][c] = acc[m] * inv;
+
+  float mx = -INFINITY;
+  for (int s = c; s < a.splits; s += D) {
+    const float2 ml = a.ws_ml[(base + s) * kMaxGroup + h];
+    if (ml.y > 0.0f) mx = fmaxf(mx, ml.x);
   }
+#pragma unroll
+  for (int st = 32; st >= 1; st >>= 1) mx = fmaxf(mx, __shfl_xor(mx, st, 64));
+  if (lane == 0) red[wv] = mx;
   __syncthreads();
-  for (int e = tid; e < a.group * D; e += blockDim.x) {
-    const int h = e / D, c = e % D;
-    float o = 0.0f;
-    for (int m = 0; m < a.modalities; ++m) {
-      const float* Ur = a.rotations + (static_cast<size_t>(m) * D + c) * D;  // row c of U_m
-      for (int kk = 0; kk < D; ++kk) o = fmaf(Ur[kk], A[m][h][kk], o);
+  mx = red[0];
+#pragma unroll
+  for (int i = 1; i < D / 64; ++i) mx = fmaxf(mx, red[i]);
+
+  float lsum = 0.0f;
+  float acc[kMaxModalities] = {0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < a.splits; s0 += CH) {
+    __syncthreads();
+    {
+      const int s = s0 + c;
+      float w = 0.0f;
+      uint32_t mk = 0u;
+      if (s < a.splits) {
+        const float2 ml = a.ws_ml[(base + s) * kMaxGroup + h];
+        if (ml.y > 0.0f) {
+          w = exp2f(ml.x - mx);
+          mk = a.ws_mask[base + s];
+        }
+        lsum += w * (ml.y > 0.0f ? ml.y : 0.0f);
+      }
+      wgt[c] = w;
+      msk[c] = mk;
     }
-    a.out[(static_cast<size_t>(b) * a.hq + kvh * a.group + h) * D + c] = o;
+    __syncthreads();
+    const int n = min(CH, a.splits - s0);
+    for (int j = 0; j < n; ++j) {
+      const uint32_t mk = msk[j];
+      if (!mk) continue;
+      const float w = wgt[j];
+      const float* src = a.ws_acc + ((base + s0 + j) * kMaxModalities * kMaxGroup + h) * D + c;
+#pragma unroll
+      for (int m = 0; m < kMaxModalities; ++m)
+        if (mk & (1u << m)) acc[m] += w * src[static_cast<size_t>(m) * kMaxGroup * D];
+    }
   }
+  // total softmax sum over the block
+#pragma unroll
+  for (int st = 32; st >= 1; st >>= 1) lsum += __shfl_xor(lsum, st, 64);
+  __syncthreads();
+  if (lane == 0) red[wv] = lsum;
+  __syncthreads();
+  lsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) lsum += red[i];
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+  for (int m = 0; m < kMaxModalities; ++m) A[m][c] = acc[m] * inv;
+  __syncthreads();
+  float o = 0.0f;
+  for (int m = 0; m < a.modalities; ++m) {
+    const float* Ut = a.rotations_t + static_cast<size_t>(m) * D * D + c;
+#pragma unroll 8
+    for (int kk = 0; kk < D; ++kk) o = fmaf(Ut[static_cast<size_t>(kk) * D], A[m][kk], o);
+  }
+  a.out[(static_cast<size_t>(b) * a.hq + kvh * a.group + h) * D + c] = o;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+struct WorkspaceView {
+  float2* ml;
+  uint32_t* mask;
+  float* acc;
+};
+
+WorkspaceView carve(const void* ws, size_t parts) {
+  char* w = static_cast<char*>(const_cast<void*>(ws));
+  WorkspaceView v;
+  v.ml = reinterpret_cast<float2*>(w);
+  w += align256(parts * kMaxGroup * sizeof(float2));
+  v.mask = reinterpret_cast<uint32_t*>(w);
+  w += align256(parts * sizeof(uint32_t));
+  v.acc = reinterpret_cast<float*>(w);
+  return v;
+}
+
 }  // namespace
 
 DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested) {
+  // A split is one workgroup of kWaves waves; each wave takes wpw consecutive windows
+  // and the block merges its waves' partials before writing one.  Default: about two
+  // waves per SIMD (256 CUs x 4 SIMDs x 2) with at least 8 windows per wave.
   DecodePlan p{};
   const int64_t nwin = (max_len + kWindow - 1) / kWindow;
   const int64_t units = static_cast<int64_t>(batch) * sh.hkv;
-  int64_t splits;
+  int64_t want;  // splits
   if (requested > 0) {
-    splits = requested;
+    want = requested;
   } else {
-    const int64_t target = 2048;  // ~2 waves per SIMD on 256 CUs
-    splits = (target + units - 1) / units;
-    splits = std::min<int64_t>(splits, std::max<int64_t>(1, (nwin + 7) / 8));
+    const int64_t target_waves = 2048;
+    want = (target_waves / kWaves + units - 1) / units;
+    want = std::min<int64_t>(want, std::max<int64_t>(1, (nwin + 8 * kWaves - 1) / (8 * kWaves)));
   }
-  splits = std::max<int64_t>(1, std::min<int64_t>(splits, std::max<int64_t>(1, nwin)));
-  const int64_t wps = std::max<int64_t>(1, (nwin + splits - 1) / splits);
-  if (requested <= 0) splits = std::max<int64_t>(1, (nwin + wps - 1) / wps);
+  want = std::max<int64_t>(1, std::min<int64_t>(want, std::max<int64_t>(1, nwin)));
+  const int64_t wpw = std::max<int64_t>(1, (nwin + kWaves * want - 1) / (kWaves * want));
+  const int64_t waves = std::max<int64_t>(1, (nwin + wpw - 1) / wpw);
+  const int64_t splits = (waves + kWaves - 1) / kWaves;
   p.splits = static_cast<int>(splits);
-  p.windows_per_split = static_cast<int>(wps);
+  p.windows_per_wave = static_cast<int>(wpw);
   const size_t parts = static_cast<size_t>(units) * splits;
   p.workspace_bytes = align256(parts * kMaxGroup * sizeof(float2)) + align256(parts * sizeof(uint32_t)) +
                       align256(parts * kMaxModalities * kMaxGroup * sh.d * sizeof(float));
@@ -584,40 +880,36 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
 }
 
 template <int D, int KB, int VB>
-static hipError_t launch_decode_t(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
-                                  const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
-                                  const uint32_t* kc, const uint16_t* km, const uint16_t* ks,
-                                  const uint32_t* vc, const uint16_t* vs, const uint8_t* mod,
-                                  int64_t t_cap, float scale, void* ws, float* out, hipStream_t st) {
-  const size_t parts = static_cast<size_t>(batch) * sh.hkv * plan.splits;
-  char* w = static_cast<char*>(ws);
-  float2* ml = reinterpret_cast<float2*>(w);
-  w += align256(parts * kMaxGroup * sizeof(float2));
-  uint32_t* mask = reinterpret_cast<uint32_t*>(w);
-  w += align256(parts * sizeof(uint32_t));
-  float* accw = reinterpret_cast<float*>(w);
-
+static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
+                                   const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
+                                   const uint32_t* kc, const uint16_t* km, const uint16_t* ks,
+                                   const uint32_t* vc, const uint16_t* vs, const uint8_t* mod,
+                                   int64_t t_cap, float scale, void* ws, hipStream_t st) {
+  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits);
   PartialArgs pa{q, seq_lens, kc, km, ks, vc, vs, mod, tb.signs, tb.pair_table, sh.hq, sh.hkv, sh.group,
-                 sh.modalities, t_cap, max_len, scale * 1.4426950408889634f, plan.windows_per_split, plan.splits,
-                 ml, mask, accw};
+                 sh.modalities, t_cap, max_len, scale * 1.4426950408889634f, plan.windows_per_wave, plan.splits,
+                 w.ml, w.mask, w.acc};
   const dim3 grid(static_cast<unsigned>(plan.splits), static_cast<unsigned>(batch * sh.hkv));
-  decode_partial_kernel<D, KB, VB><<<grid, 64, 0, st>>>(pa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  CombineArgs ca{seq_lens, tb.rotations, sh.hq, sh.hkv, sh.group, sh.modalities, plan.splits, ml, mask, accw, out};
-  decode_combine_kernel<D><<<dim3(static_cast<unsigned>(batch * sh.hkv)), 256, 0, st>>>(ca);
+  constexpr size_t dyn_bytes = Lds<D, KB, VB>::DYN;
+  static bool attr_set = false;  // dynamic LDS above the 64 KB default needs the attribute
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, KB, VB>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn_bytes));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  decode_partial_kernel<D, KB, VB><<<grid, kWaves * 64, dyn_bytes, st>>>(pa);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan, const float* q,
-                         const int32_t* seq_lens, int batch, int64_t max_len, const uint32_t* kc,
-                         const uint16_t* km, const uint16_t* ks, const uint32_t* vc, const uint16_t* vs,
-                         const uint8_t* mod, int64_t t_cap, float scale, void* ws, float* out,
-                         hipStream_t st) {
-#define OMNIKV_DEC(D_, KB_, VB_)                                                                          \
-  if (sh.d == D_ && sh.kbits == KB_ && sh.vbits == VB_)                                                   \
-    return launch_decode_t<D_, KB_, VB_>(sh, tb, plan, q, seq_lens, batch, max_len, kc, km, ks, vc, vs, mod, t_cap, \
-                                         scale, ws, out, st);
+hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan, const float* q,
+                                 const int32_t* seq_lens, int batch, int64_t max_len, const uint32_t* kc,
+                                 const uint16_t* km, const uint16_t* ks, const uint32_t* vc, const uint16_t* vs,
+                                 const uint8_t* mod, int64_t t_cap, float scale, void* ws, hipStream_t st) {
+#define OMNIKV_DEC(D_, KB_, VB_)                                                                           \
+  if (sh.d == D_ && sh.kbits == KB_ && sh.vbits == VB_)                                                    \
+    return launch_partial_t<D_, KB_, VB_>(sh, tb, plan, q, seq_lens, batch, max_len, kc, km, ks, vc, vs, mod, \
+                                          t_cap, scale, ws, st);
   OMNIKV_DEC(128, 2, 2)
   OMNIKV_DEC(128, 4, 4)
   OMNIKV_DEC(128, 2, 4)
@@ -628,6 +920,18 @@ hipError_t launch_decode(const Shape& sh, const DeviceTables& tb, const DecodePl
   OMNIKV_DEC(64, 4, 2)
 #undef OMNIKV_DEC
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
+                                 const int32_t* seq_lens, int batch, const void* ws, float* out, hipStream_t st) {
+  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits);
+  CombineArgs ca{tb.rotations_t, sh.hq, sh.hkv, sh.group, sh.modalities, plan.splits, w.ml, w.mask, w.acc, out};
+  const dim3 grid(static_cast<unsigned>(sh.group), static_cast<unsigned>(batch * sh.hkv));
+  if (sh.d == 128)
+    decode_combine_kernel<128><<<grid, 128, 0, st>>>(ca);
+  else
+    decode_combine_kernel<64><<<grid, 64, 0, st>>>(ca);
+  return hipGetLastError();
 }
 
 }  // namespace omnikv

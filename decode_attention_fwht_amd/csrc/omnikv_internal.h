@@ -17,6 +17,7 @@ constexpr int kMaxModalities = 3;
 struct DeviceTables {
   float* signs = nullptr;          // [d] +-1.0f, the diagonal D of R = c_d H D
   float* rotations = nullptr;      // [M][d][d] row-major U_m
+  float* rotations_t = nullptr;    // [M][d][d] U_m transposed (Ut[m][k][c] = U[m][c][k])
   float* boundaries = nullptr;     // [2^vb - 1] fp32 midpoints of fp16 levels
   uint32_t* pair_table = nullptr;  // [4^vb] fp16 level pairs: (l[lo code], l[hi code])
 };
@@ -38,18 +39,21 @@ hipError_t launch_quantize_values(const Shape& sh, const DeviceTables& tb, const
 // Split-KV decode: partial results per (sequence, KV head, split) followed by the
 // log-sum-exp merge and the batched inverse value rotation.
 struct DecodePlan {
-  int splits;             // splits per (sequence, KV head)
-  int windows_per_split;  // consecutive 32-token windows per split
+  int splits;            // splits (one workgroup each) per (sequence, KV head)
+  int windows_per_wave;  // consecutive 32-token windows per wave of a split
   size_t workspace_bytes;
 };
 
 DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested_splits);
 
-hipError_t launch_decode(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
-                         const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
-                         const uint32_t* k_codes, const uint16_t* k_min, const uint16_t* k_scale,
-                         const uint32_t* v_codes, const uint16_t* v_scale, const uint8_t* modality,
-                         int64_t t_cap, float softmax_scale, void* workspace, float* out,
-                         hipStream_t stream);
+hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
+                                 const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
+                                 const uint32_t* k_codes, const uint16_t* k_min, const uint16_t* k_scale,
+                                 const uint32_t* v_codes, const uint16_t* v_scale, const uint8_t* modality,
+                                 int64_t t_cap, float softmax_scale, void* workspace, hipStream_t stream);
+
+hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
+                                 const int32_t* seq_lens, int batch, const void* workspace, float* out,
+                                 hipStream_t stream);
 
 }  // namespace omnikv

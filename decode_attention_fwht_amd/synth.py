@@ -239,3 +239,31 @@ def modality_clusters(d: int, seed: int, n: int = 8192, heavy_tail: bool = False
         cal.append(draw(n))
         held.append(draw(n))
     return cal, held
+
+
+def drifting_tensor_device(cfg: Config, tags, seed: int, stream: int, t0: int, n: int, device="cuda"):
+    """Same recipe as drifting_tensor, drawn with torch's generator on `device`.
+
+    Returns a contiguous [batch][n][kv_heads][head_dim] tensor (bf16, or fp32 for
+    fp32 configs).  Draws differ from the numpy version; the distribution is
+    the same.  `tags`: uint8 tensor or array [batch][>= t0+n].
+    """
+    import torch
+    assert t0 % WINDOW == 0 and n % WINDOW == 0
+    d, H, B = cfg.head_dim, cfg.kv_heads, cfg.batch
+    nw = n // WINDOW
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([cfg.cid, seed, stream, t0]).generate_state(1)[0]))
+    tg = torch.as_tensor(np.asarray(tags) if not isinstance(tags, torch.Tensor) else tags.cpu().numpy())
+    first = tg[:, t0:t0 + n:WINDOW].to(device)                                   # [B][nw]
+    z = torch.randn((B, nw, WINDOW, H, d), generator=g, device=device)
+    mu = 0.5 * torch.randn((B, nw, 1, H, d), generator=g, device=device)
+    sig = torch.where(first == TEXT, cfg.drift_text, cfg.drift_av).to(torch.float32)
+    lam = torch.exp(sig[:, :, None] * torch.randn((B, nw, H), generator=g, device=device))
+    x = lam[:, :, None, :, None] * (z + mu)
+    gain = torch.ones((H, d), device=device)
+    for h in range(H):
+        idx = torch.randperm(d, generator=g, device=device)[: cfg.outliers]
+        gain[h, idx] = cfg.outlier_gain
+    x = (x * gain).reshape(B, n, H, d)
+    return x.contiguous() if cfg.fp32_inputs else x.to(torch.bfloat16).contiguous()

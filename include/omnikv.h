@@ -169,7 +169,10 @@ omnikv_status omnikv_quantize_values(const omnikv_ctx* ctx, const void* v, omnik
                                      uint16_t* v_scale, hipStream_t stream);
 
 /* Bytes of device workspace omnikv_decode_attention needs for (batch, max_len,
- * num_splits); num_splits 0 = the library's choice.  bytes: host out. */
+ * num_splits).  num_splits: how many splits of consecutive 32-token windows each
+ * (sequence, KV head) is cut into, one partial result each; 0 = the library's
+ * choice; larger requests are clamped to what the window count allows (the plan
+ * may use fewer).  bytes: host out. */
 omnikv_status omnikv_decode_workspace_size(const omnikv_ctx* ctx, int32_t batch, int64_t max_len,
                                            int32_t num_splits, size_t* bytes);
 
@@ -191,6 +194,27 @@ omnikv_status omnikv_decode_attention(const omnikv_ctx* ctx, const float* q, con
                                       const uint8_t* modality, int64_t t_cap, float softmax_scale,
                                       int32_t num_splits, void* workspace, size_t workspace_bytes,
                                       float* out, hipStream_t stream);
+
+/* The two halves of omnikv_decode_attention, with the same arguments and
+ * rules.  omnikv_decode_partial runs the split-KV pass: for every (sequence,
+ * KV head, split of consecutive 32-token windows) it writes the running max,
+ * the softmax sum and one value accumulator per modality, in rotated space,
+ * into the workspace.  omnikv_decode_combine merges those partials with the
+ * log-sum-exp rule and applies the batched inverse value rotation
+ * out = sum_m U_m A_m ([paper] §1, Fig. 1(d)).  Calling partial then combine on
+ * one stream with the same (batch, max_len, num_splits, workspace) gives the
+ * result of omnikv_decode_attention; the split lets a caller time, overlap or
+ * exchange the partials (they are linear in the inverse rotation). */
+omnikv_status omnikv_decode_partial(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens,
+                                    int32_t batch, int64_t max_len, const uint32_t* k_codes,
+                                    const uint16_t* k_min, const uint16_t* k_scale,
+                                    const uint32_t* v_codes, const uint16_t* v_scale,
+                                    const uint8_t* modality, int64_t t_cap, float softmax_scale,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+omnikv_status omnikv_decode_combine(const omnikv_ctx* ctx, const int32_t* seq_lens, int32_t batch,
+                                    int64_t max_len, int32_t num_splits, const void* workspace,
+                                    size_t workspace_bytes, float* out, hipStream_t stream);
 
 /* Thread-local text describing the last non-OK status of this thread. */
 const char* omnikv_last_error(void);
