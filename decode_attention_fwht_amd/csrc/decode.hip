@@ -295,7 +295,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
     }
   }
   auto issue = [&](int w, int slot) {
-    const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_slot(wave, slot)));
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_slot(wave, slot))));
 #pragma unroll
     for (int x = 0; x < SG::NK; ++x)
       if (1024 * x + 16 * lane < SG::KBYTES)
@@ -322,6 +323,56 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
 #pragma unroll
       for (int c = 0; c < NC; ++c) qv[j][c] = qp[lane + 64 * c] * (ok ? sg[c] : 0.0f);
     }
+  }
+
+  // ---- visit order.  The wave's windows go in chunks of up to 64; within a chunk, one
+  // pass per modality present (the resident one first) over the windows holding it, in
+  // window order, two at a time.  The ring is filled along the same sequence of visits,
+  // across passes: visit i goes to slot i % RING once visit i - RING has been computed.
+  // The first chunk's first copies go out before the query set-up, which hides their
+  // latency.
+  int cur = -1;  // resident modality (wave-uniform); -1 before the first visit
+  uint64_t ps0 = 0u, ps1 = 0u, ps2 = 0u;  // windows of passes 0, 1, 2 (bit = window of the chunk)
+  int pmod0 = 0;                          // modality of pass 0; passes k take (pmod0 + k) % 3
+  int total = 0, issued = 0, fk = 0, ck = 0, chunk0 = 0;
+  uint64_t fmask = 0u, cmask = 0u;
+  auto pass_mask = [&](int k) -> uint64_t { return k == 0 ? ps0 : (k == 1 ? ps1 : ps2); };
+  auto begin_chunk = [&](int c0) {
+    const int cn = min(64, nw - c0);
+    uint32_t bits = 0u;
+    if (lane < cn) {
+      const int tok0 = (wbeg + c0 + lane) * kWindow;
+      const uint4_t* tp = reinterpret_cast<const uint4_t*>(a.modality + static_cast<size_t>(b) * a.t_cap + tok0);
+      const uint4_t t01 = tp[0], t23 = tp[1];
+      const uint32_t tw[8] = {t01[0], t01[1], t01[2], t01[3], t23[0], t23[1], t23[2], t23[3]};
+#pragma unroll
+      for (int j = 0; j < kWindow; ++j) {
+        const uint32_t tg = (tw[j / 4] >> (8 * (j % 4))) & 0xFFu;
+        if (tok0 + j < len && tg < static_cast<uint32_t>(kMaxModalities)) bits |= 1u << tg;
+      }
+    }
+    const uint64_t pm0 = __ballot(bits & 1u), pm1 = __ballot((bits >> 1) & 1u), pm2 = __ballot((bits >> 2) & 1u);
+    total = __builtin_popcountll(pm0) + __builtin_popcountll(pm1) + __builtin_popcountll(pm2);
+    // pass order: the resident modality first, then the others
+    pmod0 = cur < 0 ? 0 : cur;
+    ps0 = pmod0 == 0 ? pm0 : (pmod0 == 1 ? pm1 : pm2);
+    ps1 = pmod0 == 0 ? pm1 : (pmod0 == 1 ? pm2 : pm0);
+    ps2 = pmod0 == 0 ? pm2 : (pmod0 == 1 ? pm0 : pm1);
+    chunk0 = c0;
+    issued = fk = ck = 0;
+    fmask = cmask = ps0;
+  };
+  auto issue_upto = [&](int lim) {
+    for (; issued < lim; ++issued) {
+      while (fmask == 0u) fmask = pass_mask(++fk);
+      const int w = __builtin_ctzll(fmask);
+      fmask &= fmask - 1u;
+      issue(wbeg + chunk0 + w, issued % RING);
+    }
+  };
+  if (nw > 0) {
+    begin_chunk(0);
+    issue_upto(min(total, RING - 1));
   }
 
   for (int i = tid; i < (1 << (2 * VB)); i += kWaves * 64) vtab[i] = a.pair_table[i];
@@ -409,7 +460,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
   float4_t acc[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-  int cur = -1;                   // resident modality (wave-uniform); -1 before the first window
   int occ0 = -1, occ1 = -1;       // modality held by stash slot 0 / 1 (wave-uniform)
   float mst0 = 0.0f, mst1 = 0.0f; // m_ref at which slot 0 / 1 was stored (per column)
   float* const my_stash = stash_mem + wave * (2 * kMaxGroup * D);
@@ -448,224 +498,229 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
     cur = t;
   };
 
-  // One visit of a 32-token window for modality m.  Only tokens of modality m (and inside
-  // the sequence) count; a window holding several modalities is visited once per
-  // modality.  The all-tokens-count case runs straight through.
-  auto window = [&](const uint8_t* slot, int tokb, int m) {
-    const uint32_t tg0 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 4 * g);
-    const uint32_t tg1 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 16 + 4 * g);
-    // ---- k_min term: every A row is m_w, so each lane's results all equal q^ . m_w
-    float4_t cm = float4_t{0.f, 0.f, 0.f, 0.f};
-    // ---- scores^T = codes . (q^ (.) s_w)
-    float4_t cs[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
-    uint32_t kw[KW];
+  // NP (1 or 2) visits of 32-token windows for modality m, computed side by side so the
+  // two dependency chains interleave; one online-softmax step covers both.  Only tokens
+  // of modality m (and inside the sequence) count: a window holding several modalities is
+  // visited once per modality.  The all-tokens-count case runs straight through.
+  auto visit = [&](auto np_tag, const uint8_t* const (&slot)[2], const int (&tokb)[2], int m) {
+    constexpr int NP = decltype(np_tag)::value;
+    uint32_t tg0[NP], tg1[NP];
+    float4_t cm[NP], cs[NP][2];
+    uint32_t kw[NP][KW];
 #pragma unroll
-    for (int x = 0; x < KW / 4; ++x) {
-      const uint4_t t = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_K + 16 * (KW / 4) * lane + 16 * x);
-      kw[4 * x] = t[0]; kw[4 * x + 1] = t[1]; kw[4 * x + 2] = t[2]; kw[4 * x + 3] = t[3];
+    for (int j = 0; j < NP; ++j) {
+      tg0[j] = *reinterpret_cast<const uint32_t*>(slot[j] + SG::OFF_TAG + 4 * g);
+      tg1[j] = *reinterpret_cast<const uint32_t*>(slot[j] + SG::OFF_TAG + 16 + 4 * g);
+      cm[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+      cs[j][0] = cs[j][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < KW / 4; ++x) {
+        const uint4_t t = *reinterpret_cast<const uint4_t*>(slot[j] + SG::OFF_K + 16 * (KW / 4) * lane + 16 * x);
+        kw[j][4 * x] = t[0]; kw[j][4 * x + 1] = t[1]; kw[j][4 * x + 2] = t[2]; kw[j][4 * x + 3] = t[3];
+      }
+      if constexpr (KW == 2) {
+        const uint2 t = *reinterpret_cast<const uint2*>(slot[j] + SG::OFF_K + 8 * lane);
+        kw[j][0] = t.x; kw[j][1] = t.y;
+      }
     }
-    if constexpr (KW == 2) {
-      const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_K + 8 * lane);
-      kw[0] = t.x; kw[1] = t.y;
-    }
+    // ---- k_min term (every A row is m_w, so each lane's results all equal q^ . m_w) and
+    // scores^T = codes . (q^ (.) s_w)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const uint4_t sv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_S + g * (D / 2) + 16 * s);
-      const uint4_t mv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_M + g * (D / 2) + 16 * s);
-      cm = mfma16(mv4, bqa[s], cm);
-      uint32_t bq[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // copy the element out first: bit_cast of an ext-vector element subscript is
-        // lowered as element 0 by this compiler
-        const uint32_t svw = sv4[i];
-        const half2_t sv = __builtin_bit_cast(half2_t, svw);
-        const half2_t t1 = beta[s][i] * sv;
-        const half2_t t2 = __builtin_elementwise_fma(alpha[s][i], sv, -t1);
-        bq[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(gamma[s][i], sv, t2));
-      }
-      const uint4_t bqv = uint4_t{bq[0], bq[1], bq[2], bq[3]};
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        uint4_t ak;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ak[i] = (kw[KO::word(tau, s, i)] >> KO::shift(tau, s, i)) & KO::mask(s);
-        cs[tau] = mfma16(ak, bqv, cs[tau]);
-      }
-    }
-    // ---- which tokens count: all of them unless the window is partial or mixed
-    const uint32_t rep = static_cast<uint32_t>(m) * 0x01010101u;
-    const bool all_count = (tokb + kWindow <= len) && __all((tg0 == rep) && (tg1 == rep));
-    // ---- scores relative to m_ref (the first window of a wave takes absolute scores)
-    const float aw = (cm[0] + row_ror8(cm[0])) * zh;
-    const bool fresh = m_ref == -INFINITY;
-    const float base = fresh ? aw : aw - m_ref;
-    float sc[2][4];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[tau][i] = fmaf(cs[tau][i] + row_ror8(cs[tau][i]), zfac, base);
-    uint32_t keep[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-    if (!all_count) {
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const uint32_t tw = tau ? tg1 : tg0;
+      for (int j = 0; j < NP; ++j) {
+        const uint4_t sv4 = *reinterpret_cast<const uint4_t*>(slot[j] + SG::OFF_S + g * (D / 2) + 16 * s);
+        const uint4_t mv4 = *reinterpret_cast<const uint4_t*>(slot[j] + SG::OFF_M + g * (D / 2) + 16 * s);
+        cm[j] = mfma16(mv4, bqa[s], cm[j]);
+        uint32_t bq[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = (tokb + 16 * tau + 4 * g + i < len) && ((tw >> (8 * i)) & 0xFFu) == static_cast<uint32_t>(m);
-          if (!ok) sc[tau][i] = -INFINITY;
+          // copy the element out first: bit_cast of an ext-vector element subscript is
+          // lowered as element 0 by this compiler
+          const uint32_t svw = sv4[i];
+          const half2_t sv = __builtin_bit_cast(half2_t, svw);
+          const half2_t t1 = beta[s][i] * sv;
+          const half2_t t2 = __builtin_elementwise_fma(alpha[s][i], sv, -t1);
+          bq[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(gamma[s][i], sv, t2));
         }
+        const uint4_t bqv = uint4_t{bq[0], bq[1], bq[2], bq[3]};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          keep[2 * tau + e] = (sc[tau][2 * e] == -INFINITY ? 0u : 0x0000FFFFu) |
-                              (sc[tau][2 * e + 1] == -INFINITY ? 0u : 0xFFFF0000u);
+        for (int tau = 0; tau < 2; ++tau) {
+          uint4_t ak;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ak[i] = (kw[j][KO::word(tau, s, i)] >> KO::shift(tau, s, i)) & KO::mask(s);
+          cs[j][tau] = mfma16(ak, bqv, cs[j][tau]);
+        }
+      }
+    }
+    // ---- which tokens count: all of them unless a window is partial or mixed
+    const uint32_t rep = static_cast<uint32_t>(m) * 0x01010101u;
+    bool full = true, same = true;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      full = full && (tokb[j] + kWindow <= len);
+      same = same && (tg0[j] == rep) && (tg1[j] == rep);
+    }
+    const bool all_count = full && __all(same);
+    // ---- scores relative to m_ref (the first visit of a wave takes absolute scores)
+    const bool fresh = m_ref == -INFINITY;
+    float sc[NP][2][4];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const float aw = (cm[j][0] + row_ror8(cm[j][0])) * zh;
+      const float base = fresh ? aw : aw - m_ref;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[j][tau][i] = fmaf(cs[j][tau][i] + row_ror8(cs[j][tau][i]), zfac, base);
+    }
+    // value scales of this lane's tokens, fp16 pairs (tokens 4g.., then 16 + 4g..)
+    uint32_t sgw[NP][4];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const uint2 sig0 = *reinterpret_cast<const uint2*>(slot[j] + SG::OFF_SIG + 2 * (4 * g));
+      const uint2 sig1 = *reinterpret_cast<const uint2*>(slot[j] + SG::OFF_SIG + 2 * (16 + 4 * g));
+      sgw[j][0] = sig0.x; sgw[j][1] = sig0.y; sgw[j][2] = sig1.x; sgw[j][3] = sig1.y;
+    }
+    if (!all_count) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          const uint32_t tw = tau ? tg1[j] : tg0[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = (tokb[j] + 16 * tau + 4 * g + i < len) &&
+                            ((tw >> (8 * i)) & 0xFFu) == static_cast<uint32_t>(m);
+            if (!ok) sc[j][tau][i] = -INFINITY;
+          }
+          // tokens that do not count get p = 0 and, as their scale bits may be anything, a
+          // zero scale
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            sgw[j][2 * tau + e] &= (sc[j][tau][2 * e] == -INFINITY ? 0u : 0x0000FFFFu) |
+                                   (sc[j][tau][2 * e + 1] == -INFINITY ? 0u : 0xFFFF0000u);
+          }
         }
       }
     }
     float wmax = -INFINITY;
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+    for (int j = 0; j < NP; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wmax = fmaxf(wmax, sc[tau][i]);
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wmax = fmaxf(wmax, sc[j][tau][i]);
     // every visit has a counted token, so wmax is finite
     wmax = group_max(wmax);
     const bool grow = fresh || wmax > kLazyRescale;
     if (__any(grow)) {
       const float delta = grow ? wmax : 0.0f;
-      // the first window's accumulators are still zero (and -delta may overflow exp2)
+      // the first visit's accumulators are still zero (and -delta may overflow exp2)
       const float alf = fresh ? 0.0f : exp2_raw(-delta);
       if (grow) m_ref = (fresh ? 0.0f : m_ref) + delta;
       l_part *= alf;
 #pragma unroll
       for (int u = 0; u < NU; ++u) acc[u] *= alf;
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
+      for (int j = 0; j < NP; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[tau][i] -= delta;
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[j][tau][i] -= delta;
     }
     // ---- probabilities times the value scale, as fp16 hi (part 0) or lo (part 1)
-    const uint2 sig0 = *reinterpret_cast<const uint2*>(slot + SG::OFF_SIG + 2 * (4 * g));
-    const uint2 sig1 = *reinterpret_cast<const uint2*>(slot + SG::OFF_SIG + 2 * (16 + 4 * g));
-    uint32_t bvw[4];
+    uint32_t bvw[NP][4];
+    uint32_t vw[NP][VW];
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int tau = qd >> 1;
-      const uint32_t sw = qd == 0 ? sig0.x : qd == 1 ? sig0.y : qd == 2 ? sig1.x : sig1.y;
-      const float p0 = exp2_raw(sc[tau][2 * (qd & 1)]);
-      const float p1 = exp2_raw(sc[tau][2 * (qd & 1) + 1]);
-      l_part += p0;
-      l_part += p1;
-      // hi = fp16(p sigma); part 1 lanes then take lo = fp16(p sigma - hi).  Tokens that
-      // do not count have p = 0 but may hold any scale bits: the keep mask clears them.
-      const uint32_t hi = mix_pair(p0, p1, sw, 0u);
-      bvw[qd] = mix_pair(p0, p1, sw, hi & lo_mask) & keep[qd];
-    }
-    // ---- value contraction into the resident accumulator, one channel tile at a time
-    uint32_t vw[VW];
+    for (int j = 0; j < NP; ++j) {
 #pragma unroll
-    for (int x = 0; x < VW / 4; ++x) {
-      const uint4_t t = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_V + 16 * (VW / 4) * lane + 16 * x);
-      vw[4 * x] = t[0]; vw[4 * x + 1] = t[1]; vw[4 * x + 2] = t[2]; vw[4 * x + 3] = t[3];
+      for (int qd = 0; qd < 4; ++qd) {
+        const int tau = qd >> 1;
+        const uint32_t sw = sgw[j][qd];
+        const float p0 = exp2_raw(sc[j][tau][2 * (qd & 1)]);
+        const float p1 = exp2_raw(sc[j][tau][2 * (qd & 1) + 1]);
+        l_part += p0;
+        l_part += p1;
+        // hi = fp16(p sigma); part 1 lanes then take lo = fp16(p sigma - hi)
+        const uint32_t hi = mix_pair(p0, p1, sw, 0u);
+        bvw[j][qd] = mix_pair(p0, p1, sw, hi & lo_mask);
+      }
+#pragma unroll
+      for (int x = 0; x < VW / 4; ++x) {
+        const uint4_t t = *reinterpret_cast<const uint4_t*>(slot[j] + SG::OFF_V + 16 * (VW / 4) * lane + 16 * x);
+        vw[j][4 * x] = t[0]; vw[j][4 * x + 1] = t[1]; vw[j][4 * x + 2] = t[2]; vw[j][4 * x + 3] = t[3];
+      }
+      if constexpr (VW == 2) {
+        const uint2 t = *reinterpret_cast<const uint2*>(slot[j] + SG::OFF_V + 8 * lane);
+        vw[j][0] = t.x; vw[j][1] = t.y;
+      }
     }
-    if constexpr (VW == 2) {
-      const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_V + 8 * lane);
-      vw[0] = t.x; vw[1] = t.y;
-    }
-    // byte offsets of the pair-table entries: 2-bit values take four offsets per dword
-    // at once (low nibbles of the bytes, then high nibbles)
-    uint32_t vx[VW], vy[VW];
+    // ---- value contraction into the resident accumulator, one channel tile at a time.
+    // Byte offsets of the pair-table entries: 2-bit values take four offsets per dword at
+    // once (low nibbles of the bytes, then high nibbles).
+    uint32_t vx[NP][VW], vy[NP][VW];
     if constexpr (VB == 2) {
 #pragma unroll
-      for (int x = 0; x < VW; ++x) {
-        vx[x] = (vw[x] << 2) & 0x3C3C3C3Cu;
-        vy[x] = (vw[x] >> 2) & 0x3C3C3C3Cu;
-      }
+      for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int x = 0; x < VW; ++x) {
+          vx[j][x] = (vw[j][x] << 2) & 0x3C3C3C3Cu;
+          vy[j][x] = (vw[j][x] >> 2) & 0x3C3C3C3Cu;
+        }
     }
-    auto entry = [&](int pp) -> uint32_t {
+    auto entry = [&](int j, int pp) -> uint32_t {
       if constexpr (VB == 2) {
-        const uint32_t src = (pp & 1) ? vy[pp / 8] : vx[pp / 8];
+        const uint32_t src = (pp & 1) ? vy[j][pp / 8] : vx[j][pp / 8];
         const int byte = (pp % 8) / 2;
-        const uint32_t off = byte == 3 ? (src >> 24) : ((src >> (8 * byte)) & 0xFFu);
+        // one byte-select per offset (v_perm_b32: byte `byte` of src, upper bytes zero)
+        const uint32_t off = __builtin_amdgcn_perm(0u, src, 0x0C0C0C00u | static_cast<uint32_t>(byte));
         return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(vtab) + off);
       } else {
-        return vtab[(vw[pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
+        return vtab[(vw[j][pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
       }
     };
-    const uint4_t bv = uint4_t{bvw[0], bvw[1], bvw[2], bvw[3]};
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      uint4_t av;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = entry(4 * u + i);
-      acc[u] = mfma16(av, bv, acc[u]);
+      for (int j = 0; j < NP; ++j) {
+        uint4_t av;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = entry(j, 4 * u + i);
+        acc[u] = mfma16(av, uint4_t{bvw[j][0], bvw[j][1], bvw[j][2], bvw[j][3]}, acc[u]);
+      }
     }
   };
 
-  // ---- visit order.  The wave's windows go in chunks of up to 64; within a chunk, one
-  // pass per modality present (the resident one first) over the windows holding it, in
-  // window order.  The ring is filled along the same sequence of visits, across passes.
+  // ---- the visits, chunk by chunk
   for (int c0 = 0; c0 < nw; c0 += 64) {
-    const int cn = min(64, nw - c0);
-    uint64_t pm[kMaxModalities];
-    {
-      uint32_t bits = 0u;
-      if (lane < cn) {
-        const int tok0 = (wbeg + c0 + lane) * kWindow;
-        const uint4_t* tp = reinterpret_cast<const uint4_t*>(a.modality + static_cast<size_t>(b) * a.t_cap + tok0);
-        const uint4_t t01 = tp[0], t23 = tp[1];
-        const uint32_t tw[8] = {t01[0], t01[1], t01[2], t01[3], t23[0], t23[1], t23[2], t23[3]};
-#pragma unroll
-        for (int j = 0; j < kWindow; ++j) {
-          const uint32_t tg = (tw[j / 4] >> (8 * (j % 4))) & 0xFFu;
-          if (tok0 + j < len && tg < static_cast<uint32_t>(kMaxModalities)) bits |= 1u << tg;
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < kMaxModalities; ++m) pm[m] = __ballot((bits >> m) & 1u);
-    }
-    // pass order: the resident modality first, then the others
-    int ord[kMaxModalities];
-    {
-      const int c = cur < 0 ? 0 : cur;
-#pragma unroll
-      for (int k = 0; k < kMaxModalities; ++k) ord[k] = (c + k) % kMaxModalities;
-    }
-    int total = 0;
-#pragma unroll
-    for (int m = 0; m < kMaxModalities; ++m) total += __builtin_popcountll(pm[m]);
-    // cursors over the visit sequence: (pass k, windows left in that pass)
-    int fk = 0, ck = 0;
-    uint64_t fmask = pm[ord[0]], cmask = pm[ord[0]];
-    auto advance = [&](int& k, uint64_t& mask, int& mod) -> int {
-      while (mask == 0u) {
-        ++k;
-        mask = pm[ord[k < kMaxModalities ? k : 0]];
-      }
-      mod = ord[k];
-      const int w = __builtin_ctzll(mask);
-      mask &= mask - 1u;
-      return w;
-    };
-    auto issue_next = [&](int item) {
-      int mod;
-      const int w = advance(fk, fmask, mod);
-      issue(wbeg + c0 + w, item % RING);
-    };
-#pragma unroll
-    for (int i = 0; i < RING - 1; ++i)
-      if (i < total) issue_next(i);
-    for (int i = 0; i < total; ++i) {
-      if (i + RING - 1 < total) issue_next(i + RING - 1);
-      // wait for this visit's copies: later visits' copies may stay in flight
-      const int ahead = min(RING - 1, total - 1 - i);
+    if (c0 > 0) begin_chunk(c0);
+    for (int i = 0; i < total;) {
+      while (cmask == 0u) cmask = pass_mask(++ck);
+      const int m = (pmod0 + ck) % kMaxModalities;
+      const bool two = __builtin_popcountll(cmask) >= 2;
+      const int n = two ? 2 : 1;
+      issue_upto(min(total, i + RING));
+      // wait for this step's copies: later visits' copies may stay in flight
+      const int ahead = issued - (i + n);
       if (ahead >= 3) wait_vmcnt<3 * L>();
       else if (ahead == 2) wait_vmcnt<2 * L>();
       else if (ahead == 1) wait_vmcnt<L>();
       else wait_vmcnt<0>();
-      int m;
-      const int w = advance(ck, cmask, m);
       if (m != cur) make_resident(m);
-      window(ring_slot(wave, i % RING), (wbeg + c0 + w) * kWindow, m);
+      const int w0 = __builtin_ctzll(cmask);
+      cmask &= cmask - 1u;
+      const uint8_t* const sl[2] = {ring_slot(wave, i % RING), ring_slot(wave, (i + 1) % RING)};
+      if (two) {
+        const int w1 = __builtin_ctzll(cmask);
+        cmask &= cmask - 1u;
+        const int tb[2] = {(wbeg + c0 + w0) * kWindow, (wbeg + c0 + w1) * kWindow};
+        visit(std::integral_constant<int, 2>{}, sl, tb, m);
+      } else {
+        const int tb[2] = {(wbeg + c0 + w0) * kWindow, 0};
+        visit(std::integral_constant<int, 1>{}, sl, tb, m);
+      }
+      i += n;
     }
   }
 
@@ -698,6 +753,19 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
     }
   }
   __syncthreads();
+  // per (wave, source, head): the factor that brings the source to the block's max
+  __shared__ float fac_lds[kWaves][3][kMaxGroup];
+  __shared__ float mb_lds[kMaxGroup];
+  if (tid < kWaves * 3 * kMaxGroup) {
+    const int v = tid / (3 * kMaxGroup), j = (tid / kMaxGroup) % 3, hh = tid % kMaxGroup;
+    float mb = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x)
+      if (ml_lds[x][hh].y > 0.0f) mb = fmaxf(mb, ml_lds[x][hh].x);
+    fac_lds[v][j][hh] = (mod_lds[v][j] >= 0 && ml_lds[v][hh].y > 0.0f) ? exp2f(ref_lds[v][j][hh] - mb) : 0.0f;
+    if (v == 0 && j == 0) mb_lds[hh] = mb;
+  }
+  __syncthreads();
   const size_t pidx = static_cast<size_t>(unit) * a.splits + blockIdx.x;
   uint32_t present = 0u;
 #pragma unroll
@@ -706,26 +774,22 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
     for (int j = 0; j < 3; ++j)
       if (mod_lds[v][j] >= 0) present |= 1u << mod_lds[v][j];
   if (tid < kMaxGroup) {
-    float lsum = 0.0f, mb = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-      if (ml_lds[v][tid].y > 0.0f) mb = fmaxf(mb, ml_lds[v][tid].x);
+    const float mb = mb_lds[tid];
+    float lsum = 0.0f;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v)
       if (ml_lds[v][tid].y > 0.0f) lsum += exp2f(ml_lds[v][tid].x - mb) * ml_lds[v][tid].y;
     if (tid < a.group) a.ws_ml[pidx * kMaxGroup + tid] = make_float2(mb, lsum);
   }
   if (tid == 0) a.ws_mask[pidx] = present;
+  // four consecutive elements of [8][D] per thread
+  const int e4 = 4 * tid;
+  if (e4 < a.group * D) {
+    const int hh = e4 / D;
 #pragma unroll
-  for (int m = 0; m < kMaxModalities; ++m) {
-    if (!(present & (1u << m))) continue;
-    for (int e = tid; e < a.group * D; e += kWaves * 64) {
-      const int hh = e / D;
-      float mb = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v)
-        if (ml_lds[v][hh].y > 0.0f) mb = fmaxf(mb, ml_lds[v][hh].x);
-      float sum = 0.0f;
+    for (int m = 0; m < kMaxModalities; ++m) {
+      if (!(present & (1u << m))) continue;
+      float4_t sum = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
 #pragma unroll
@@ -733,10 +797,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
           if (mod_lds[v][j] != m) continue;
           const float* src = j == 0 ? reinterpret_cast<const float*>(ring_slot(v, 0))
                                     : stash_mem + (v * 2 + (j - 1)) * kMaxGroup * D;
-          sum += src[e] * exp2f(ref_lds[v][j][hh] - mb);
+          const float f = fac_lds[v][j][hh];
+          const float4_t x = *reinterpret_cast<const float4_t*>(src + e4);
+          sum += x * f;
         }
       }
-      a.ws_acc[(pidx * kMaxModalities + m) * kMaxGroup * D + e] = sum;
+      *reinterpret_cast<float4_t*>(a.ws_acc + (pidx * kMaxModalities + m) * kMaxGroup * D + e4) = sum;
     }
   }
 }
@@ -750,85 +816,116 @@ struct CombineArgs {
   float* out;
 };
 
-// One block per (query head, sequence x KV head), one thread per channel:
-// log-sum-exp merge of the splits, then out = sum_m U_m A_m for this head.
+// One block per (query head, sequence x KV head); thread (k-group, channel).  Every
+// global load that does not depend on another one is issued first (the head's rotation
+// columns, the first batch of split accumulators, the split maxima and sums), so the
+// kernel waits for memory about once: (0) largest split max and total softmax sum;
+// (1) log-sum-exp merge of the splits' rotated-space accumulators into LDS;
+// (2) out = sum_m U_m A_m over k-groups, summed through LDS, then normalised.
+constexpr int kCombineThreads = 1024;
+constexpr int kCombineBatch = 16;    // splits whose accumulators are loaded up front
+constexpr int kMaxSplits = 1024;     // splits per (sequence, KV head)
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(CombineArgs a) {
-  constexpr int CH = D;  // splits handled per chunk (one per thread)
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a) {
+  constexpr int KG = kCombineThreads / D;   // k-groups of the rotation
+  constexpr int KPG = D / KG;               // k per group
+  constexpr int PSTRIDE = kMaxModalities * kMaxGroup * D;  // floats per split
+  __shared__ float2 ml_lds[kMaxSplits];
+  __shared__ float wgt[kMaxSplits];
+  __shared__ uint32_t msk[kMaxSplits];
   __shared__ float A[kMaxModalities][D];
-  __shared__ float wgt[CH];
-  __shared__ uint32_t msk[CH];
-  __shared__ float red[D / 64];
+  __shared__ float red[KG][D];
+  __shared__ float mx_lds, inv_l;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = blockIdx.x, unit = blockIdx.y;
   if (h >= a.group) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
   const size_t base = static_cast<size_t>(unit) * a.splits;
+  const int S = a.splits;
+  const int kg = tid / D, c = tid % D;
 
-  float mx = -INFINITY;
-  for (int s = c; s < a.splits; s += D) {
-    const float2 ml = a.ws_ml[(base + s) * kMaxGroup + h];
-    if (ml.y > 0.0f) mx = fmaxf(mx, ml.x);
+  // ---- loads that depend on nothing
+  float u[kMaxModalities][KPG];
+#pragma unroll
+  for (int m = 0; m < kMaxModalities; ++m)
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk)
+      u[m][kk] = m < a.modalities ? a.rotations_t[(static_cast<size_t>(m) * D + kg * KPG + kk) * D + c] : 0.0f;
+  const bool merger = tid < kMaxModalities * D && (tid / D) < a.modalities;  // item (m, k)
+  const int im = tid / D, ik = tid % D;
+  const int nb0 = min(S, kCombineBatch);
+  float x[kCombineBatch];
+  const float* src = a.ws_acc + base * PSTRIDE + (im * kMaxGroup + h) * D + ik;
+#pragma unroll
+  for (int j = 0; j < kCombineBatch; ++j) x[j] = (merger && j < nb0) ? src[static_cast<size_t>(j) * PSTRIDE] : 0.0f;
+  for (int s = tid; s < S; s += kCombineThreads) {
+    ml_lds[s] = a.ws_ml[(base + s) * kMaxGroup + h];
+    msk[s] = a.ws_mask[base + s];
   }
-#pragma unroll
-  for (int st = 32; st >= 1; st >>= 1) mx = fmaxf(mx, __shfl_xor(mx, st, 64));
-  if (lane == 0) red[wv] = mx;
   __syncthreads();
-  mx = red[0];
-#pragma unroll
-  for (int i = 1; i < D / 64; ++i) mx = fmaxf(mx, red[i]);
 
-  float lsum = 0.0f;
-  float acc[kMaxModalities] = {0.0f, 0.0f, 0.0f};
-  for (int s0 = 0; s0 < a.splits; s0 += CH) {
-    __syncthreads();
-    {
-      const int s = s0 + c;
-      float w = 0.0f;
-      uint32_t mk = 0u;
-      if (s < a.splits) {
-        const float2 ml = a.ws_ml[(base + s) * kMaxGroup + h];
-        if (ml.y > 0.0f) {
-          w = exp2f(ml.x - mx);
-          mk = a.ws_mask[base + s];
-        }
-        lsum += w * (ml.y > 0.0f ? ml.y : 0.0f);
+  // ---- (0) wave 0: largest max, weights, total sum
+  if (wv == 0) {
+    float mx = -INFINITY;
+    for (int s = lane; s < S; s += 64)
+      if (ml_lds[s].y > 0.0f) mx = fmaxf(mx, ml_lds[s].x);
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1) mx = fmaxf(mx, __shfl_xor(mx, st, 64));
+    float ls = 0.0f;
+    for (int s = lane; s < S; s += 64) {
+      const float2 ml = ml_lds[s];
+      const float w = ml.y > 0.0f ? exp2f(ml.x - mx) : 0.0f;
+      wgt[s] = w;
+      ls += w * (ml.y > 0.0f ? ml.y : 0.0f);
+    }
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1) ls += __shfl_xor(ls, st, 64);
+    if (lane == 0) {
+      mx_lds = mx;
+      inv_l = ls > 0.0f ? 1.0f / ls : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // ---- (1) merge.  A split without modality m left that block unwritten: the mask
+  // selects, it never multiplies.
+  if (tid < kMaxModalities * D) {
+    float acc = 0.0f;
+    if (merger) {
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j)
+        if (j < nb0 && ((msk[j] >> im) & 1u)) acc = fmaf(wgt[j], x[j], acc);
+      for (int j0 = kCombineBatch; j0 < S; j0 += kCombineBatch) {
+        float y[kCombineBatch];
+#pragma unroll
+        for (int t = 0; t < kCombineBatch; ++t)
+          y[t] = (j0 + t < S && ((msk[j0 + t] >> im) & 1u)) ? src[static_cast<size_t>(j0 + t) * PSTRIDE] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < kCombineBatch; ++t)
+          if (j0 + t < S) acc = fmaf(wgt[j0 + t], y[t], acc);
       }
-      wgt[c] = w;
-      msk[c] = mk;
     }
-    __syncthreads();
-    const int n = min(CH, a.splits - s0);
-    for (int j = 0; j < n; ++j) {
-      const uint32_t mk = msk[j];
-      if (!mk) continue;
-      const float w = wgt[j];
-      const float* src = a.ws_acc + ((base + s0 + j) * kMaxModalities * kMaxGroup + h) * D + c;
-#pragma unroll
-      for (int m = 0; m < kMaxModalities; ++m)
-        if (mk & (1u << m)) acc[m] += w * src[static_cast<size_t>(m) * kMaxGroup * D];
-    }
+    A[im][ik] = acc;
   }
-  // total softmax sum over the block
-#pragma unroll
-  for (int st = 32; st >= 1; st >>= 1) lsum += __shfl_xor(lsum, st, 64);
   __syncthreads();
-  if (lane == 0) red[wv] = lsum;
-  __syncthreads();
-  lsum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) lsum += red[i];
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-#pragma unroll
-  for (int m = 0; m < kMaxModalities; ++m) A[m][c] = acc[m] * inv;
-  __syncthreads();
+
+  // ---- (2) rotation
   float o = 0.0f;
-  for (int m = 0; m < a.modalities; ++m) {
-    const float* Ut = a.rotations_t + static_cast<size_t>(m) * D * D + c;
-#pragma unroll 8
-    for (int kk = 0; kk < D; ++kk) o = fmaf(Ut[static_cast<size_t>(kk) * D], A[m][kk], o);
+#pragma unroll
+  for (int m = 0; m < kMaxModalities; ++m) {
+    if (m >= a.modalities) break;
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) o = fmaf(u[m][kk], A[m][kg * KPG + kk], o);
   }
-  a.out[(static_cast<size_t>(b) * a.hq + kvh * a.group + h) * D + c] = o;
+  red[kg][c] = o;
+  __syncthreads();
+  if (tid < D) {
+    float r = 0.0f;
+#pragma unroll
+    for (int g2 = 0; g2 < KG; ++g2) r += red[g2][tid];
+    a.out[(static_cast<size_t>(b) * a.hq + kvh * a.group + h) * D + tid] = r * inv_l;
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -867,7 +964,7 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
     want = (target_waves / kWaves + units - 1) / units;
     want = std::min<int64_t>(want, std::max<int64_t>(1, (nwin + 8 * kWaves - 1) / (8 * kWaves)));
   }
-  want = std::max<int64_t>(1, std::min<int64_t>(want, std::max<int64_t>(1, nwin)));
+  want = std::max<int64_t>(1, std::min<int64_t>({want, std::max<int64_t>(1, nwin), static_cast<int64_t>(kMaxSplits)}));
   const int64_t wpw = std::max<int64_t>(1, (nwin + kWaves * want - 1) / (kWaves * want));
   const int64_t waves = std::max<int64_t>(1, (nwin + wpw - 1) / wpw);
   const int64_t splits = (waves + kWaves - 1) / kWaves;
@@ -928,9 +1025,9 @@ hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const 
   CombineArgs ca{tb.rotations_t, sh.hq, sh.hkv, sh.group, sh.modalities, plan.splits, w.ml, w.mask, w.acc, out};
   const dim3 grid(static_cast<unsigned>(sh.group), static_cast<unsigned>(batch * sh.hkv));
   if (sh.d == 128)
-    decode_combine_kernel<128><<<grid, 128, 0, st>>>(ca);
+    decode_combine_kernel<128><<<grid, kCombineThreads, 0, st>>>(ca);
   else
-    decode_combine_kernel<64><<<grid, 64, 0, st>>>(ca);
+    decode_combine_kernel<64><<<grid, kCombineThreads, 0, st>>>(ca);
   return hipGetLastError();
 }
 

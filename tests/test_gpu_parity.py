@@ -204,6 +204,42 @@ def test_decode_split_invariance():
     ctx.close()
 
 
+def test_decode_graph_replay_matches_eager():
+    """The decode step captured in a HIP graph (as the benchmark times it) gives the
+    eager result bit for bit on every replay, with eager work between replays."""
+    import torch
+    cfg = synth.CONFIGS[2]
+    T = 4096
+    ctx, signs, U, lv = make_context(cfg)
+    caches = [cache_to_device(synth.random_packed_cache(cfg, 20 + i, length=T)) for i in range(2)]
+    q = to_dev(synth.queries(cfg, 5))
+    lens = to_dev(np.array([T - 9], np.int32))
+    ws = torch.empty(ctx.workspace_size(cfg.batch, T), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((cfg.batch, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+            for _ in range(2)]
+    eager = []
+    for i in range(2):
+        ctx.decode(q, lens, T, caches[i], out=outs[i], workspace=ws)
+        eager.append(outs[i].clone())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(2):
+            ctx.decode_partial(q, lens, T, caches[i], ws)
+            ctx.decode_combine(lens, cfg.batch, T, ws, outs[i])
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+        # eager work between replays, on other buffers
+        ctx.decode(q, lens, T, caches[(rep + 1) % 2])
+        torch.cuda.synchronize()
+    ctx.close()
+
+
 # ----------------------------------------------------------------------------- decode at full size, sampled rows
 @pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (4, 2, 2), (5, 2, 2), (4, 4, 4)])
 def test_decode_parity_full_size_sampled(cid, kbits, vbits):
