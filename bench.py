@@ -96,6 +96,31 @@ def time_write_path(ctx, cfg, tags_np, reps=20, seed=3):
     return res
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_16x32k_k2v2_hbm_traffic.txt")
+DECODE_SOURCE = os.path.join(ROOT, "decode_attention_fwht_amd", "csrc", "decode.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode_partial launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, scaled by the copy reference; None unless the summary was taken on this
+    workload with the current kernel source."""
+    import hashlib
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        with open(DECODE_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("decode_source_sha256") != sha or kv.get("workload") != workload:
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, kbits, vbits, budget_s=15.0, seed=11):
     """The CPU oracle (float64 brute force over the dequantized cache) on a bounded
     sample of the same workload: whole (sequence, KV head) units of a synthetic
@@ -148,6 +173,9 @@ def main():
     ap.add_argument("--buffers", type=int, default=0, help="independent caches cycled (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-reference-mib", type=int, default=0,
+                    help="also run a plain device copy (out = 1 * in, fp32) of this many MiB, the "
+                         "reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -245,9 +273,19 @@ def main():
         "kernels_us": {"decode_partial_avg": round(part_avg_s * 1e6, 2),
                        "decode_combine_avg": round(comb_ms / args.steps * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"{cfg.name} K{args.kbits}V{args.vbits} splits {args.splits}")},
         "write_path": write_path,
     }
+    if args.copy_reference_mib:
+        n = args.copy_reference_mib * (1 << 20) // 4
+        src = torch.rand(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        res["copy_reference_mib"] = args.copy_reference_mib
+        del src, dst
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.kbits, args.vbits, args.cpu_seconds)
     else:
