@@ -8,6 +8,8 @@
 #include <string>
 #include <vector>
 
+#include <climits>
+
 #include "omnikv_internal.h"
 
 struct omnikv_ctx {
@@ -249,6 +251,13 @@ omnikv_status check_decode(const omnikv_ctx* ctx, int32_t batch, int64_t max_len
   if (t_cap <= 0 || t_cap % omnikv::kWindow) return fail(OMNIKV_EINVAL, "t_cap must be a positive multiple of 32");
   if (max_len < 0 || max_len > t_cap) return fail(OMNIKV_EINVAL, "max_len must be in [0, t_cap] (got %lld)", (long long)max_len);
   if (num_splits < 0) return fail(OMNIKV_EINVAL, "num_splits must be >= 0");
+  {
+    // the decode kernel addresses a (sequence, KV head)'s code blocks with 32-bit offsets
+    const int64_t bits = ctx->sh.kbits > ctx->sh.vbits ? ctx->sh.kbits : ctx->sh.vbits;
+    if (t_cap / omnikv::kWindow * (4 * static_cast<int64_t>(ctx->sh.d) * bits) > INT32_MAX)
+      return fail(OMNIKV_EUNSUPPORTED, "t_cap %lld too large: one KV head's code blocks must stay below 2 GiB",
+                  (long long)t_cap);
+  }
   *plan = omnikv::plan_decode(ctx->sh, batch, max_len, num_splits);
   if (workspace_bytes < plan->workspace_bytes)
     return fail(OMNIKV_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, plan->workspace_bytes);

@@ -170,6 +170,7 @@ struct PartialArgs {
   float2* ws_ml;     // [unit][split][8] (max, sum) in log2 units
   uint32_t* ws_mask; // [unit][split] modalities present
   float* ws_acc;     // [unit][split][M][8][D]
+  float* ws_stash;   // [unit][split][wave][2][8][D]
 };
 
 // ---------------------------------------------------------------------------------------
@@ -217,25 +218,42 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr
       : "memory");
 }
 
+// The same copy from a wave-uniform 64-bit base plus a 32-bit per-lane byte offset (the
+// scalar-base form of the global address), which keeps the address math in 32 bits.
+__device__ __forceinline__ void copy16_to_lds_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Ring depth: the deepest of 4, 3, 2 slots per wave that keeps two workgroups per CU
-// within the 160 KB of LDS (ring + accumulator stash + small tables).
+// Ring depth: the deepest of 4, 3, 2 slots per wave that keeps three workgroups per CU
+// (three waves per SIMD) within the 160 KB of LDS (ring + rotated queries + small tables).
+constexpr int kBlocksPerCU = 3;
 template <int D, int KB, int VB>
 struct Lds {
-  static constexpr int STASH = kWaves * 2 * kMaxGroup * D * 4;  // two fp32 [8][D] slots per wave
-  static constexpr int fits(int ring) { return kWaves * ring * Slot<D, KB, VB>::BYTES + STASH + 2048 <= 80 * 1024; }
+  static constexpr int fits(int ring) {
+    return kWaves * ring * Slot<D, KB, VB>::BYTES + kMaxGroup * D * 4 + 2048 <= 160 * 1024 / kBlocksPerCU;
+  }
   static constexpr int RING = fits(4) ? 4 : (fits(3) ? 3 : 2);
   static constexpr int RING_BYTES = kWaves * RING * Slot<D, KB, VB>::BYTES;
-  static constexpr int DYN = RING_BYTES + STASH;
+  static constexpr int DYN = RING_BYTES;
 };
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs a) {
+__global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kernel(PartialArgs a) {
   using SG = Slot<D, KB, VB>;
   using KO = KeyOp<D, KB>;
   constexpr int RING = Lds<D, KB, VB>::RING;
@@ -248,14 +266,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
   constexpr uint32_t PMASK = (1u << (2 * VB)) - 1u;
   constexpr int L = SG::COPIES;
 
-  // Dynamic LDS: [ring: kWaves x RING slots][stash: kWaves x 2 x [8][D] fp32].  Only the
-  // asm copies write the ring, and a static LDS array that no visible code stores to
-  // would let the optimizer treat its contents as undefined and fold the slot reads.
+  // Dynamic LDS: the ring, kWaves x RING slots.  Only the asm copies write it, and a
+  // static LDS array that no visible code stores to would let the optimizer treat its
+  // contents as undefined and fold the slot reads.
   extern __shared__ __attribute__((aligned(16))) uint8_t ring_mem[];
   auto ring_slot = [&](int wv, int slot) -> uint8_t* { return ring_mem + (wv * RING + slot) * SG::BYTES; };
-  float* const stash_mem = reinterpret_cast<float*>(ring_mem + Lds<D, KB, VB>::RING_BYTES);
-  // the rotated queries live in the stash area until the window loop starts
-  float (*q_lds)[D] = reinterpret_cast<float (*)[D]>(stash_mem);
+  __shared__ __attribute__((aligned(16))) float q_lds[kMaxGroup][D];
   __shared__ float zmax_lds[kMaxGroup];
   __shared__ uint32_t vtab[1 << (2 * VB)];
 
@@ -274,8 +290,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
   const size_t unit_win = static_cast<size_t>(unit) * nwin_cap;
 
   // ---- per-lane copy descriptors: source = base + window * stride (bytes)
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit_win * SG::KBYTES + 16 * lane;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit_win * SG::VBYTES + 16 * lane;
+  // key and value blocks: wave-uniform base of this unit + 32-bit offsets (a unit's blocks
+  // span at most t_cap / 32 windows of a few KB)
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit_win * SG::KBYTES;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit_win * SG::VBYTES;
   const uint8_t* mbase = nullptr;
   uint32_t mstride = 0;
   {
@@ -300,11 +318,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
 #pragma unroll
     for (int x = 0; x < SG::NK; ++x)
       if (1024 * x + 16 * lane < SG::KBYTES)
-        copy16_to_lds(kbase + static_cast<size_t>(w) * SG::KBYTES + 1024 * x, dst + SG::OFF_K + 1024 * x);
+        copy16_to_lds_sbase(kbase, static_cast<uint32_t>(w * SG::KBYTES + 1024 * x + 16 * lane), dst + SG::OFF_K + 1024 * x);
 #pragma unroll
     for (int x = 0; x < SG::NV; ++x)
       if (1024 * x + 16 * lane < SG::VBYTES)
-        copy16_to_lds(vbase + static_cast<size_t>(w) * SG::VBYTES + 1024 * x, dst + SG::OFF_V + 1024 * x);
+        copy16_to_lds_sbase(vbase, static_cast<uint32_t>(w * SG::VBYTES + 1024 * x + 16 * lane), dst + SG::OFF_V + 1024 * x);
     if (lane < SG::MISC_LANES) copy16_to_lds(mbase + static_cast<size_t>(w) * mstride, dst + SG::OFF_S);
   };
 
@@ -422,7 +440,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
   // ---- operand constants.  Lane (n, g) feeds column n: head h, part hi (0) or lo (1);
   // K-step s, dword i hold channels c0, c0 + 1 with c0 = g*D/4 + 8 s + 2 i.
   //   alpha/beta/gamma: score operand  fp16 split of (q^ s) scaled by 2^-(KB*peff(s))
-  //   bqa:              k_min operand  q^ hi (part 0) or lo (part 1)
+  //   bqa:              k_min operand  q^ hi (part 0) or lo (part 1); the same in every wave
+  //                     of the block, so it is kept in LDS (over q_lds) rather than in
+  //                     registers
   half2_t alpha[NS][4], beta[NS][4], gamma[NS][4];
   uint4_t bqa[NS];
 #pragma unroll
@@ -450,11 +470,19 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
     }
     bqa[s] = uint4_t{bw[0], bw[1], bw[2], bw[3]};
   }
-  __syncthreads();  // q_lds is stash space from here on
+  static_assert(NS * 64 * 16 <= kMaxGroup * D * 4, "k_min operand table must fit over q_lds");
+  uint4_t* const bqa_lds = reinterpret_cast<uint4_t*>(&q_lds[0][0]);  // [NS][64 lanes]
+  __syncthreads();  // every wave has read q_lds
+  if (wave == 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) bqa_lds[s * 64 + lane] = bqa[s];
+  }
+  __syncthreads();
 
   // ---- running state.  Scores, l_part and the accumulators are relative to m_ref (per
   // column, log2 units).  One modality's accumulator is resident in registers; the
-  // others wait in this wave's two stash slots, each with the m_ref it was stored at.
+  // others wait in this wave's two stash slots (workspace memory, touched only when the
+  // wave changes modality pass), each with the m_ref it was stored at.
   float m_ref = -INFINITY;
   float l_part = 0.0f;
   float4_t acc[NU];
@@ -462,7 +490,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
   for (int u = 0; u < NU; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
   int occ0 = -1, occ1 = -1;       // modality held by stash slot 0 / 1 (wave-uniform)
   float mst0 = 0.0f, mst1 = 0.0f; // m_ref at which slot 0 / 1 was stored (per column)
-  float* const my_stash = stash_mem + wave * (2 * kMaxGroup * D);
+  float* const my_stash =
+      a.ws_stash + ((static_cast<size_t>(unit) * a.splits + blockIdx.x) * kWaves + wave) * (2 * kMaxGroup * D);
   const uint32_t lo_mask = part ? 0xFFFFFFFFu : 0u;
 
   // Lane (n, g) of tile u holds channels 16u + 4g .. +3 of column n; a stash slot keeps
@@ -498,123 +527,104 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
     cur = t;
   };
 
-  // NP (1 or 2) visits of 32-token windows for modality m, computed side by side so the
-  // two dependency chains interleave; one online-softmax step covers both.  Only tokens
-  // of modality m (and inside the sequence) count: a window holding several modalities is
-  // visited once per modality.  The all-tokens-count case runs straight through.
-  auto visit = [&](auto np_tag, const uint8_t* const (&slot)[2], const int (&tokb)[2], int m) {
-    constexpr int NP = decltype(np_tag)::value;
-    uint32_t tg0[NP], tg1[NP];
-    float4_t cm[NP], cs[NP][2];
-    uint32_t kw[NP][KW];
+  // ---- score contractions of the window in `slot` (modality-independent): the k_min
+  // term cm (every A row is m_w, so each lane's results all equal q^ . m_w) and
+  // scores^T = codes . (q^ (.) s_w), hi and lo columns still separate
+  auto score_mma = [&](const uint8_t* slot, float4_t (&cs)[2], float4_t& cm) {
+    cm = float4_t{0.f, 0.f, 0.f, 0.f};
+    cs[0] = cs[1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    uint32_t kw[KW];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      tg0[j] = *reinterpret_cast<const uint32_t*>(slot[j] + SG::OFF_TAG + 4 * g);
-      tg1[j] = *reinterpret_cast<const uint32_t*>(slot[j] + SG::OFF_TAG + 16 + 4 * g);
-      cm[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-      cs[j][0] = cs[j][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int x = 0; x < KW / 4; ++x) {
-        const uint4_t t = *reinterpret_cast<const uint4_t*>(slot[j] + SG::OFF_K + 16 * (KW / 4) * lane + 16 * x);
-        kw[j][4 * x] = t[0]; kw[j][4 * x + 1] = t[1]; kw[j][4 * x + 2] = t[2]; kw[j][4 * x + 3] = t[3];
-      }
-      if constexpr (KW == 2) {
-        const uint2 t = *reinterpret_cast<const uint2*>(slot[j] + SG::OFF_K + 8 * lane);
-        kw[j][0] = t.x; kw[j][1] = t.y;
-      }
+    for (int x = 0; x < KW / 4; ++x) {
+      const uint4_t t = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_K + 16 * (KW / 4) * lane + 16 * x);
+      kw[4 * x] = t[0]; kw[4 * x + 1] = t[1]; kw[4 * x + 2] = t[2]; kw[4 * x + 3] = t[3];
     }
-    // ---- k_min term (every A row is m_w, so each lane's results all equal q^ . m_w) and
-    // scores^T = codes . (q^ (.) s_w)
+    if constexpr (KW == 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_K + 8 * lane);
+      kw[0] = t.x; kw[1] = t.y;
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
+      const uint4_t sv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_S + g * (D / 2) + 16 * s);
+      const uint4_t mv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_M + g * (D / 2) + 16 * s);
+      cm = mfma16(mv4, bqa_lds[s * 64 + lane], cm);
+      uint32_t bq[4];
 #pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        const uint4_t sv4 = *reinterpret_cast<const uint4_t*>(slot[j] + SG::OFF_S + g * (D / 2) + 16 * s);
-        const uint4_t mv4 = *reinterpret_cast<const uint4_t*>(slot[j] + SG::OFF_M + g * (D / 2) + 16 * s);
-        cm[j] = mfma16(mv4, bqa[s], cm[j]);
-        uint32_t bq[4];
+      for (int i = 0; i < 4; ++i) {
+        // copy the element out first: bit_cast of an ext-vector element subscript is
+        // lowered as element 0 by this compiler
+        const uint32_t svw = sv4[i];
+        const half2_t sv = __builtin_bit_cast(half2_t, svw);
+        const half2_t t1 = beta[s][i] * sv;
+        const half2_t t2 = __builtin_elementwise_fma(alpha[s][i], sv, -t1);
+        bq[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(gamma[s][i], sv, t2));
+      }
+      const uint4_t bqv = uint4_t{bq[0], bq[1], bq[2], bq[3]};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // copy the element out first: bit_cast of an ext-vector element subscript is
-          // lowered as element 0 by this compiler
-          const uint32_t svw = sv4[i];
-          const half2_t sv = __builtin_bit_cast(half2_t, svw);
-          const half2_t t1 = beta[s][i] * sv;
-          const half2_t t2 = __builtin_elementwise_fma(alpha[s][i], sv, -t1);
-          bq[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(gamma[s][i], sv, t2));
-        }
-        const uint4_t bqv = uint4_t{bq[0], bq[1], bq[2], bq[3]};
+      for (int tau = 0; tau < 2; ++tau) {
+        uint4_t ak;
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          uint4_t ak;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ak[i] = (kw[j][KO::word(tau, s, i)] >> KO::shift(tau, s, i)) & KO::mask(s);
-          cs[j][tau] = mfma16(ak, bqv, cs[j][tau]);
-        }
+        for (int i = 0; i < 4; ++i) ak[i] = (kw[KO::word(tau, s, i)] >> KO::shift(tau, s, i)) & KO::mask(s);
+        cs[tau] = mfma16(ak, bqv, cs[tau]);
       }
     }
-    // ---- which tokens count: all of them unless a window is partial or mixed
+  };
+
+  // ---- the rest of one visit of a window for modality m, given its score contractions.
+  // Only tokens of modality m (and inside the sequence) count: a window holding several
+  // modalities is visited once per modality.  `overlap` runs inside the last basic block
+  // (after the rare branches), a place for independent work to interleave with it.
+  auto visit = [&](const uint8_t* slot, int tokb, int m, const float4_t (&cs)[2], const float4_t& cm,
+                   auto&& overlap) {
+    const uint32_t tg0 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 4 * g);
+    const uint32_t tg1 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 16 + 4 * g);
+    // value scales of this lane's tokens, fp16 pairs (tokens 4g.., then 16 + 4g..)
+    const uint2 sig0 = *reinterpret_cast<const uint2*>(slot + SG::OFF_SIG + 2 * (4 * g));
+    const uint2 sig1 = *reinterpret_cast<const uint2*>(slot + SG::OFF_SIG + 2 * (16 + 4 * g));
+    uint32_t sgw[4] = {sig0.x, sig0.y, sig1.x, sig1.y};
+    // ---- which tokens count: all of them unless the window is partial or mixed
     const uint32_t rep = static_cast<uint32_t>(m) * 0x01010101u;
-    bool full = true, same = true;
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      full = full && (tokb[j] + kWindow <= len);
-      same = same && (tg0[j] == rep) && (tg1[j] == rep);
-    }
-    const bool all_count = full && __all(same);
+    const bool all_count = (tokb + kWindow <= len) && __all((tg0 == rep) && (tg1 == rep));
     // ---- scores relative to m_ref (the first visit of a wave takes absolute scores)
     const bool fresh = m_ref == -INFINITY;
-    float sc[NP][2][4];
+    const float aw = (cm[0] + row_ror8(cm[0])) * zh;
+    const float base = fresh ? aw : aw - m_ref;
+    float sc[2][4];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const float aw = (cm[j][0] + row_ror8(cm[j][0])) * zh;
-      const float base = fresh ? aw : aw - m_ref;
+    for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[j][tau][i] = fmaf(cs[j][tau][i] + row_ror8(cs[j][tau][i]), zfac, base);
-    }
-    // value scales of this lane's tokens, fp16 pairs (tokens 4g.., then 16 + 4g..)
-    uint32_t sgw[NP][4];
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const uint2 sig0 = *reinterpret_cast<const uint2*>(slot[j] + SG::OFF_SIG + 2 * (4 * g));
-      const uint2 sig1 = *reinterpret_cast<const uint2*>(slot[j] + SG::OFF_SIG + 2 * (16 + 4 * g));
-      sgw[j][0] = sig0.x; sgw[j][1] = sig0.y; sgw[j][2] = sig1.x; sgw[j][3] = sig1.y;
-    }
+      for (int i = 0; i < 4; ++i) sc[tau][i] = fmaf(cs[tau][i] + row_ror8(cs[tau][i]), zfac, base);
     if (!all_count) {
+      // a real branch: the masking is rare, keep it off the common path
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int j = 0; j < NP; ++j) {
+      for (int tau = 0; tau < 2; ++tau) {
+        const uint32_t tw = tau ? tg1 : tg0;
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          const uint32_t tw = tau ? tg1[j] : tg0[j];
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (tokb + 16 * tau + 4 * g + i < len) && ((tw >> (8 * i)) & 0xFFu) == static_cast<uint32_t>(m);
+          if (!ok) sc[tau][i] = -INFINITY;
+        }
+        // tokens that do not count get p = 0 and, as their scale bits may be anything, a
+        // zero scale
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = (tokb[j] + 16 * tau + 4 * g + i < len) &&
-                            ((tw >> (8 * i)) & 0xFFu) == static_cast<uint32_t>(m);
-            if (!ok) sc[j][tau][i] = -INFINITY;
-          }
-          // tokens that do not count get p = 0 and, as their scale bits may be anything, a
-          // zero scale
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            sgw[j][2 * tau + e] &= (sc[j][tau][2 * e] == -INFINITY ? 0u : 0x0000FFFFu) |
-                                   (sc[j][tau][2 * e + 1] == -INFINITY ? 0u : 0xFFFF0000u);
-          }
+        for (int e = 0; e < 2; ++e) {
+          sgw[2 * tau + e] &= (sc[tau][2 * e] == -INFINITY ? 0u : 0x0000FFFFu) |
+                              (sc[tau][2 * e + 1] == -INFINITY ? 0u : 0xFFFF0000u);
         }
       }
     }
-    float wmax = -INFINITY;
+    float lmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NP; ++j)
+    for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wmax = fmaxf(wmax, sc[j][tau][i]);
-    // every visit has a counted token, so wmax is finite
-    wmax = group_max(wmax);
-    const bool grow = fresh || wmax > kLazyRescale;
-    if (__any(grow)) {
+      for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, sc[tau][i]);
+    // The reference max only has to move when some score exceeds it by more than the
+    // lazy margin; the column-wide max (a cross-lane reduction) is needed only then.
+    if (__any(fresh || lmax > kLazyRescale)) {
+      // every visit has a counted token, so the column max is finite
+      const float wmax = group_max(lmax);
+      const bool grow = fresh || wmax > kLazyRescale;
       const float delta = grow ? wmax : 0.0f;
       // the first visit's accumulators are still zero (and -delta may overflow exp2)
       const float alf = fresh ? 0.0f : exp2_raw(-delta);
@@ -623,104 +633,86 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
 #pragma unroll
       for (int u = 0; u < NU; ++u) acc[u] *= alf;
 #pragma unroll
-      for (int j = 0; j < NP; ++j)
+      for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc[j][tau][i] -= delta;
+        for (int i = 0; i < 4; ++i) sc[tau][i] -= delta;
     }
+    overlap();
     // ---- probabilities times the value scale, as fp16 hi (part 0) or lo (part 1)
-    uint32_t bvw[NP][4];
-    uint32_t vw[NP][VW];
+    uint32_t bvw[4];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int tau = qd >> 1;
-        const uint32_t sw = sgw[j][qd];
-        const float p0 = exp2_raw(sc[j][tau][2 * (qd & 1)]);
-        const float p1 = exp2_raw(sc[j][tau][2 * (qd & 1) + 1]);
-        l_part += p0;
-        l_part += p1;
-        // hi = fp16(p sigma); part 1 lanes then take lo = fp16(p sigma - hi)
-        const uint32_t hi = mix_pair(p0, p1, sw, 0u);
-        bvw[j][qd] = mix_pair(p0, p1, sw, hi & lo_mask);
-      }
-#pragma unroll
-      for (int x = 0; x < VW / 4; ++x) {
-        const uint4_t t = *reinterpret_cast<const uint4_t*>(slot[j] + SG::OFF_V + 16 * (VW / 4) * lane + 16 * x);
-        vw[j][4 * x] = t[0]; vw[j][4 * x + 1] = t[1]; vw[j][4 * x + 2] = t[2]; vw[j][4 * x + 3] = t[3];
-      }
-      if constexpr (VW == 2) {
-        const uint2 t = *reinterpret_cast<const uint2*>(slot[j] + SG::OFF_V + 8 * lane);
-        vw[j][0] = t.x; vw[j][1] = t.y;
-      }
+    for (int qd = 0; qd < 4; ++qd) {
+      const int tau = qd >> 1;
+      const float p0 = exp2_raw(sc[tau][2 * (qd & 1)]);
+      const float p1 = exp2_raw(sc[tau][2 * (qd & 1) + 1]);
+      l_part += p0;
+      l_part += p1;
+      // hi = fp16(p sigma); part 1 lanes then take lo = fp16(p sigma - hi)
+      const uint32_t hi = mix_pair(p0, p1, sgw[qd], 0u);
+      bvw[qd] = mix_pair(p0, p1, sgw[qd], hi & lo_mask);
     }
     // ---- value contraction into the resident accumulator, one channel tile at a time.
     // Byte offsets of the pair-table entries: 2-bit values take four offsets per dword at
     // once (low nibbles of the bytes, then high nibbles).
-    uint32_t vx[NP][VW], vy[NP][VW];
+    uint32_t vw[VW];
+#pragma unroll
+    for (int x = 0; x < VW / 4; ++x) {
+      const uint4_t t = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_V + 16 * (VW / 4) * lane + 16 * x);
+      vw[4 * x] = t[0]; vw[4 * x + 1] = t[1]; vw[4 * x + 2] = t[2]; vw[4 * x + 3] = t[3];
+    }
+    if constexpr (VW == 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_V + 8 * lane);
+      vw[0] = t.x; vw[1] = t.y;
+    }
+    uint32_t vx[VW], vy[VW];
     if constexpr (VB == 2) {
 #pragma unroll
-      for (int j = 0; j < NP; ++j)
-#pragma unroll
-        for (int x = 0; x < VW; ++x) {
-          vx[j][x] = (vw[j][x] << 2) & 0x3C3C3C3Cu;
-          vy[j][x] = (vw[j][x] >> 2) & 0x3C3C3C3Cu;
-        }
+      for (int x = 0; x < VW; ++x) {
+        vx[x] = (vw[x] << 2) & 0x3C3C3C3Cu;
+        vy[x] = (vw[x] >> 2) & 0x3C3C3C3Cu;
+      }
     }
-    auto entry = [&](int j, int pp) -> uint32_t {
+    auto entry = [&](int pp) -> uint32_t {
       if constexpr (VB == 2) {
-        const uint32_t src = (pp & 1) ? vy[j][pp / 8] : vx[j][pp / 8];
+        const uint32_t src = (pp & 1) ? vy[pp / 8] : vx[pp / 8];
         const int byte = (pp % 8) / 2;
         // one byte-select per offset (v_perm_b32: byte `byte` of src, upper bytes zero)
         const uint32_t off = __builtin_amdgcn_perm(0u, src, 0x0C0C0C00u | static_cast<uint32_t>(byte));
         return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(vtab) + off);
       } else {
-        return vtab[(vw[j][pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
+        return vtab[(vw[pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
       }
     };
+    const uint4_t bv = uint4_t{bvw[0], bvw[1], bvw[2], bvw[3]};
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+      uint4_t av;
 #pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        uint4_t av;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = entry(j, 4 * u + i);
-        acc[u] = mfma16(av, uint4_t{bvw[j][0], bvw[j][1], bvw[j][2], bvw[j][3]}, acc[u]);
-      }
+      for (int i = 0; i < 4; ++i) av[i] = entry(4 * u + i);
+      acc[u] = mfma16(av, bv, acc[u]);
     }
   };
 
   // ---- the visits, chunk by chunk
   for (int c0 = 0; c0 < nw; c0 += 64) {
     if (c0 > 0) begin_chunk(c0);
-    for (int i = 0; i < total;) {
+    for (int i = 0; i < total; ++i) {
       while (cmask == 0u) cmask = pass_mask(++ck);
       const int m = (pmod0 + ck) % kMaxModalities;
-      const bool two = __builtin_popcountll(cmask) >= 2;
-      const int n = two ? 2 : 1;
+      const int w0 = __builtin_ctzll(cmask);
+      cmask &= cmask - 1u;
       issue_upto(min(total, i + RING));
-      // wait for this step's copies: later visits' copies may stay in flight
-      const int ahead = issued - (i + n);
+      // wait for this visit's copies: later visits' copies may stay in flight
+      const int ahead = issued - (i + 1);
       if (ahead >= 3) wait_vmcnt<3 * L>();
       else if (ahead == 2) wait_vmcnt<2 * L>();
       else if (ahead == 1) wait_vmcnt<L>();
       else wait_vmcnt<0>();
       if (m != cur) make_resident(m);
-      const int w0 = __builtin_ctzll(cmask);
-      cmask &= cmask - 1u;
-      const uint8_t* const sl[2] = {ring_slot(wave, i % RING), ring_slot(wave, (i + 1) % RING)};
-      if (two) {
-        const int w1 = __builtin_ctzll(cmask);
-        cmask &= cmask - 1u;
-        const int tb[2] = {(wbeg + c0 + w0) * kWindow, (wbeg + c0 + w1) * kWindow};
-        visit(std::integral_constant<int, 2>{}, sl, tb, m);
-      } else {
-        const int tb[2] = {(wbeg + c0 + w0) * kWindow, 0};
-        visit(std::integral_constant<int, 1>{}, sl, tb, m);
-      }
-      i += n;
+      const uint8_t* slot = ring_slot(wave, i % RING);
+      float4_t cs[2], cm;
+      score_mma(slot, cs, cm);
+      visit(slot, (wbeg + c0 + w0) * kWindow, m, cs, cm, []() {});
     }
   }
 
@@ -795,8 +787,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(PartialArgs
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
           if (mod_lds[v][j] != m) continue;
+          // stash slots: written by wave v before the barrier (block-scope visibility)
           const float* src = j == 0 ? reinterpret_cast<const float*>(ring_slot(v, 0))
-                                    : stash_mem + (v * 2 + (j - 1)) * kMaxGroup * D;
+                                    : a.ws_stash + ((static_cast<size_t>(unit) * a.splits + blockIdx.x) * kWaves + v) *
+                                                       (2 * kMaxGroup * D) + (j - 1) * kMaxGroup * D;
           const float f = fac_lds[v][j][hh];
           const float4_t x = *reinterpret_cast<const float4_t*>(src + e4);
           sum += x * f;
@@ -934,9 +928,10 @@ struct WorkspaceView {
   float2* ml;
   uint32_t* mask;
   float* acc;
+  float* stash;
 };
 
-WorkspaceView carve(const void* ws, size_t parts) {
+WorkspaceView carve(const void* ws, size_t parts, int d) {
   char* w = static_cast<char*>(const_cast<void*>(ws));
   WorkspaceView v;
   v.ml = reinterpret_cast<float2*>(w);
@@ -944,6 +939,8 @@ WorkspaceView carve(const void* ws, size_t parts) {
   v.mask = reinterpret_cast<uint32_t*>(w);
   w += align256(parts * sizeof(uint32_t));
   v.acc = reinterpret_cast<float*>(w);
+  w += align256(parts * kMaxModalities * kMaxGroup * d * sizeof(float));
+  v.stash = reinterpret_cast<float*>(w);
   return v;
 }
 
@@ -951,8 +948,9 @@ WorkspaceView carve(const void* ws, size_t parts) {
 
 DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested) {
   // A split is one workgroup of kWaves waves; each wave takes wpw consecutive windows
-  // and the block merges its waves' partials before writing one.  Default: about two
-  // waves per SIMD (256 CUs x 4 SIMDs x 2) with at least 8 windows per wave.
+  // and the block merges its waves' partials before writing one.  Default: one wave per
+  // SIMD slot the kernel's resources allow (256 CUs x 4 SIMDs x kBlocksPerCU), with at
+  // least 8 windows per wave.
   DecodePlan p{};
   const int64_t nwin = (max_len + kWindow - 1) / kWindow;
   const int64_t units = static_cast<int64_t>(batch) * sh.hkv;
@@ -960,7 +958,7 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
   if (requested > 0) {
     want = requested;
   } else {
-    const int64_t target_waves = 2048;
+    const int64_t target_waves = 256 * 4 * kBlocksPerCU;
     want = (target_waves / kWaves + units - 1) / units;
     want = std::min<int64_t>(want, std::max<int64_t>(1, (nwin + 8 * kWaves - 1) / (8 * kWaves)));
   }
@@ -972,7 +970,8 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
   p.windows_per_wave = static_cast<int>(wpw);
   const size_t parts = static_cast<size_t>(units) * splits;
   p.workspace_bytes = align256(parts * kMaxGroup * sizeof(float2)) + align256(parts * sizeof(uint32_t)) +
-                      align256(parts * kMaxModalities * kMaxGroup * sh.d * sizeof(float));
+                      align256(parts * kMaxModalities * kMaxGroup * sh.d * sizeof(float)) +
+                      align256(parts * kWaves * 2 * kMaxGroup * sh.d * sizeof(float));
   return p;
 }
 
@@ -982,10 +981,10 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
                                    const uint32_t* kc, const uint16_t* km, const uint16_t* ks,
                                    const uint32_t* vc, const uint16_t* vs, const uint8_t* mod,
                                    int64_t t_cap, float scale, void* ws, hipStream_t st) {
-  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits);
+  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits, sh.d);
   PartialArgs pa{q, seq_lens, kc, km, ks, vc, vs, mod, tb.signs, tb.pair_table, sh.hq, sh.hkv, sh.group,
                  sh.modalities, t_cap, max_len, scale * 1.4426950408889634f, plan.windows_per_wave, plan.splits,
-                 w.ml, w.mask, w.acc};
+                 w.ml, w.mask, w.acc, w.stash};
   const dim3 grid(static_cast<unsigned>(plan.splits), static_cast<unsigned>(batch * sh.hkv));
   constexpr size_t dyn_bytes = Lds<D, KB, VB>::DYN;
   static bool attr_set = false;  // dynamic LDS above the 64 KB default needs the attribute
@@ -1021,7 +1020,7 @@ hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const 
 
 hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
                                  const int32_t* seq_lens, int batch, const void* ws, float* out, hipStream_t st) {
-  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits);
+  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits, sh.d);
   CombineArgs ca{tb.rotations_t, sh.hq, sh.hkv, sh.group, sh.modalities, plan.splits, w.ml, w.mask, w.acc, out};
   const dim3 grid(static_cast<unsigned>(sh.group), static_cast<unsigned>(batch * sh.hkv));
   if (sh.d == 128)
