@@ -5,6 +5,8 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <cmath>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -74,12 +76,27 @@ omnikv_status upload(T** dst, const T* src, size_t count) {
   return OMNIKV_OK;
 }
 
+// bf16 of a finite fp32, round to nearest even, and back
+uint16_t host_bf16_bits(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof(u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+float host_bf16_value(uint16_t b) {
+  const uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, sizeof(f));
+  return f;
+}
+
 void free_tables(omnikv::DeviceTables& tb) {
   if (tb.signs) (void)hipFree(tb.signs);
   if (tb.rotations) (void)hipFree(tb.rotations);
   if (tb.rotations_t) (void)hipFree(tb.rotations_t);
   if (tb.boundaries) (void)hipFree(tb.boundaries);
   if (tb.pair_table) (void)hipFree(tb.pair_table);
+  if (tb.rot_bf16) (void)hipFree(tb.rot_bf16);
   tb = omnikv::DeviceTables{};
 }
 
@@ -169,8 +186,45 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
   for (int idx = 0; idx < np; ++idx)
     pairs[idx] = static_cast<uint32_t>(levels[idx & (nl - 1)]) | (static_cast<uint32_t>(levels[idx >> cfg->value_bits]) << 16);
 
+  // three-part bf16 split of every U_m in the value quantizer's operand order
+  // (exact for every entry that is zero or of magnitude above 2^-100: each part keeps the
+  // next 8 significant bits, and the residuals are fp32-exact; checked below, and a
+  // split with a remainder or a subnormal part disables it)
+  const int nct = d / 16, nks = d / 32;
+  std::vector<uint16_t> rb16(static_cast<size_t>(omnikv::kMaxModalities) * 3 * nct * nks * 64 * 8);
+  bool split_exact = true;
+  for (int m = 0; m < omnikv::kMaxModalities; ++m)
+    for (int ct = 0; ct < nct; ++ct)
+      for (int ks = 0; ks < nks; ++ks)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int i = 0; i < 8; ++i) {
+            const int c = 16 * ct + (lane & 15), k = 32 * ks + 8 * (lane >> 4) + i;
+            float r = rot[(static_cast<size_t>(m) * d + k) * d + c];
+            for (int part = 0; part < 3; ++part) {
+              const uint16_t bits = host_bf16_bits(r);
+              const bool subnormal = (bits & 0x7F80u) == 0 && (bits & 0x7Fu) != 0;
+              if (subnormal || (bits & 0x7F80u) == 0x7F80u) split_exact = false;
+              r = r - host_bf16_value(bits);
+              rb16[(((((static_cast<size_t>(m) * 3 + part) * nct + ct) * nks + ks) * 64 + lane) * 8) + i] = bits;
+            }
+            if (r != 0.0f) split_exact = false;
+          }
+  double col_norm = 0.0;
+  for (int m = 0; m < omnikv::kMaxModalities; ++m)
+    for (int c = 0; c < d; ++c) {
+      double s2 = 0.0;
+      for (int k = 0; k < d; ++k) {
+        const double u = rot[(static_cast<size_t>(m) * d + k) * d + c];
+        s2 += u * u;
+      }
+      col_norm = std::max(col_norm, std::sqrt(s2));
+    }
+  if (!std::isfinite(col_norm)) split_exact = false;
+  ctx->tb.rot_col_norm = static_cast<float>(col_norm * (1.0 + 1e-6));
+
   omnikv_status st;
   if ((st = upload(&ctx->tb.signs, sg.data(), sg.size())) != OMNIKV_OK ||
+      (split_exact && (st = upload(&ctx->tb.rot_bf16, rb16.data(), rb16.size())) != OMNIKV_OK) ||
       (st = upload(&ctx->tb.rotations, rot.data(), rot.size())) != OMNIKV_OK ||
       (st = upload(&ctx->tb.rotations_t, rot_t.data(), rot_t.size())) != OMNIKV_OK ||
       (st = upload(&ctx->tb.boundaries, bnd.data(), bnd.size())) != OMNIKV_OK ||

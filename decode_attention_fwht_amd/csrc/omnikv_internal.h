@@ -20,6 +20,14 @@ struct DeviceTables {
   float* rotations_t = nullptr;    // [M][d][d] U_m transposed (Ut[m][k][c] = U[m][c][k])
   float* boundaries = nullptr;     // [2^vb - 1] fp32 midpoints of fp16 levels
   uint32_t* pair_table = nullptr;  // [4^vb] fp16 level pairs: (l[lo code], l[hi code])
+  // U_m as three bf16 parts (hi + mid + lo == U_m exactly), in the matrix-core operand
+  // order of the value quantizer: [3 modalities][3 parts][d/16 channel tiles][d/32 k-steps]
+  // [64 lanes][8] (lane 16 g + n: channel 16 ct + n, rows k = 32 ks + 8 g .. + 7)
+  // (null when some U_m does not split exactly; the sequential kernel is used then)
+  uint16_t* rot_bf16 = nullptr;
+  // host value: the largest column norm max_{m,c} ||U_m e_c||_2, which bounds the sum of
+  // |U_m[k][c] v_k| over k by that times ||v||_2
+  float rot_col_norm = 1.0f;
 };
 
 struct Shape {

@@ -95,6 +95,42 @@ def test_quantize_offset_chunk_writes_only_its_windows():
     ctx.close()
 
 
+def test_quantize_values_degenerate_tokens():
+    """Value codes for tokens at the edges of the bf16 matrix-core path: an all-zero window,
+    zero tokens, tokens whose squares underflow (sum of squares 0, so sigma = 0 and every
+    rotated value lies within the error bound of a threshold: 3 such tokens in a window are
+    recomputed one element at a time, 8 force the whole window through the sequential sum),
+    and a token whose sum of squares overflows to inf."""
+    import torch
+    cfg = synth.CONFIGS[2]
+    n = 256
+    say("[codec-degenerate] cfg2 n=256")
+    ctx, signs, U, lv = make_context(cfg)
+    tags, k, v = _inputs(cfg, n)
+    v = v.copy()
+    v[:, 0:32] = 0.0                      # window 0: all zero
+    v[:, 32:35] *= 1e-26                  # window 1: three underflowing tokens
+    v[:, 64:72] *= 1e-26                  # window 2: eight underflowing tokens
+    v[:, 96] = 0.0                        # window 3: a zero token and an overflowing one
+    v[:, 101] *= 1e19
+    v[:, 130, :, :64] = 0.0               # window 4: a half-zero token
+    v = torch.from_numpy(v).to(torch.bfloat16).float().numpy()   # what the bf16 path sees
+    cache = ctx.alloc_cache(cfg.batch, n)
+    cache["modality"].copy_(to_dev(tags[:, :n]))
+    ctx.quantize_values(bf16_tensor(v), 0, cache)
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        vc, vs = O.quantize_values(v, tags[:, :n], U, lv, 2)
+    assert np.array_equal(from_dev(cache["v_scale"], np.uint16), vs)
+    gv = from_dev(cache["v_codes"], np.uint32)
+    if not np.array_equal(gv, vc):
+        gcodes = O.unpack_windows(gv, "value", cfg.head_dim, 2)
+        ocodes = O.unpack_windows(vc, "value", cfg.head_dim, 2)
+        bad = np.argwhere(gcodes != ocodes)
+        raise AssertionError(f"{len(bad)} value codes differ, first at {bad[:4].tolist()}")
+    ctx.close()
+
+
 # ----------------------------------------------------------------------------- codec at full size, sampled
 @pytest.mark.parametrize("cid", [3, 5])
 def test_quantize_parity_prefill_sampled(cid):
