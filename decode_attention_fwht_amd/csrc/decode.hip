@@ -810,114 +810,129 @@ struct CombineArgs {
   float* out;
 };
 
-// One block per (query head, sequence x KV head); thread (k-group, channel).  Every
-// global load that does not depend on another one is issued first (the head's rotation
-// columns, the first batch of split accumulators, the split maxima and sums), so the
-// kernel waits for memory about once: (0) largest split max and total softmax sum;
-// (1) log-sum-exp merge of the splits' rotated-space accumulators into LDS;
-// (2) out = sum_m U_m A_m over k-groups, summed through LDS, then normalised.
+// One block per (query head, sequence x KV head).  Every global load that depends on
+// nothing is issued first - all of this thread's rotation rows, the first batch of split
+// accumulators, the first 64 splits' maxima, sums and masks - so the kernel waits for
+// memory about once.  Every wave derives the split weights itself (no barrier for them).
+// (1) log-sum-exp merge of the splits' rotated-space accumulators, one (m, k) item per
+// thread, into LDS; (2) out = sum_m U_m A_m, each thread a column c over one group of
+// stacked (m, k) rows, the groups summed through LDS, then normalised.
 constexpr int kCombineThreads = 1024;
-constexpr int kCombineBatch = 16;    // splits whose accumulators are loaded up front
-constexpr int kMaxSplits = 1024;     // splits per (sequence, KV head)
+constexpr int kCombineXB = 32;    // splits per batch of accumulator loads
+constexpr int kMaxSplits = 1024;  // splits per (sequence, KV head)
 
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a) {
-  constexpr int KG = kCombineThreads / D;   // k-groups of the rotation
-  constexpr int KPG = D / KG;               // k per group
+  constexpr int J = kMaxModalities * D;       // stacked rotation rows (m, k)
+  constexpr int KQ = kCombineThreads / D;     // row groups
+  constexpr int JPG = J / KQ;                 // rows per group
+  static_assert(J % KQ == 0 && JPG % 4 == 0 && J <= kCombineThreads, "combine tiling");
   constexpr int PSTRIDE = kMaxModalities * kMaxGroup * D;  // floats per split
-  __shared__ float2 ml_lds[kMaxSplits];
-  __shared__ float wgt[kMaxSplits];
-  __shared__ uint32_t msk[kMaxSplits];
-  __shared__ float A[kMaxModalities][D];
-  __shared__ float red[KG][D];
-  __shared__ float mx_lds, inv_l;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ __attribute__((aligned(16))) float A[J];
+  __shared__ float red[KQ][D];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int h = blockIdx.x, unit = blockIdx.y;
   if (h >= a.group) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
   const size_t base = static_cast<size_t>(unit) * a.splits;
   const int S = a.splits;
-  const int kg = tid / D, c = tid % D;
+  const int c = tid % D, kq = tid / D;
+  const int jrows = a.modalities * D;
 
   // ---- loads that depend on nothing
-  float u[kMaxModalities][KPG];
+  const int j0 = kq * JPG;
+  const float* up = a.rotations_t + static_cast<size_t>(j0) * D + c;
+  float u[JPG];
 #pragma unroll
-  for (int m = 0; m < kMaxModalities; ++m)
+  for (int i = 0; i < JPG; ++i) u[i] = (j0 + i < jrows) ? up[static_cast<size_t>(i) * D] : 0.0f;
+  const bool merger = tid < jrows;  // item (m, k) = (tid / D, tid % D)
+  const int im = tid / D;
+  const float* src = a.ws_acc + base * PSTRIDE + (im * kMaxGroup + h) * D + c;
+  float x[kCombineXB];
 #pragma unroll
-    for (int kk = 0; kk < KPG; ++kk)
-      u[m][kk] = m < a.modalities ? a.rotations_t[(static_cast<size_t>(m) * D + kg * KPG + kk) * D + c] : 0.0f;
-  const bool merger = tid < kMaxModalities * D && (tid / D) < a.modalities;  // item (m, k)
-  const int im = tid / D, ik = tid % D;
-  const int nb0 = min(S, kCombineBatch);
-  float x[kCombineBatch];
-  const float* src = a.ws_acc + base * PSTRIDE + (im * kMaxGroup + h) * D + ik;
-#pragma unroll
-  for (int j = 0; j < kCombineBatch; ++j) x[j] = (merger && j < nb0) ? src[static_cast<size_t>(j) * PSTRIDE] : 0.0f;
-  for (int s = tid; s < S; s += kCombineThreads) {
-    ml_lds[s] = a.ws_ml[(base + s) * kMaxGroup + h];
-    msk[s] = a.ws_mask[base + s];
+  for (int t = 0; t < kCombineXB; ++t) x[t] = (merger && t < S) ? src[static_cast<size_t>(t) * PSTRIDE] : 0.0f;
+  // lane t: split t's (max, sum) and modality mask (splits 64.. are read in the loop)
+  float2 ml0 = make_float2(-INFINITY, 0.0f);
+  uint32_t mk0 = 0u;
+  if (lane < S) {
+    ml0 = a.ws_ml[(base + lane) * kMaxGroup + h];
+    mk0 = a.ws_mask[base + lane];
   }
-  __syncthreads();
 
-  // ---- (0) wave 0: largest max, weights, total sum
-  if (wv == 0) {
-    float mx = -INFINITY;
-    for (int s = lane; s < S; s += 64)
-      if (ml_lds[s].y > 0.0f) mx = fmaxf(mx, ml_lds[s].x);
-#pragma unroll
-    for (int st = 32; st >= 1; st >>= 1) mx = fmaxf(mx, __shfl_xor(mx, st, 64));
-    float ls = 0.0f;
-    for (int s = lane; s < S; s += 64) {
-      const float2 ml = ml_lds[s];
-      const float w = ml.y > 0.0f ? exp2f(ml.x - mx) : 0.0f;
-      wgt[s] = w;
-      ls += w * (ml.y > 0.0f ? ml.y : 0.0f);
-    }
-#pragma unroll
-    for (int st = 32; st >= 1; st >>= 1) ls += __shfl_xor(ls, st, 64);
-    if (lane == 0) {
-      mx_lds = mx;
-      inv_l = ls > 0.0f ? 1.0f / ls : 0.0f;
-    }
+  // ---- largest split max (every wave alike)
+  float mx = ml0.y > 0.0f ? ml0.x : -INFINITY;
+  for (int s = 64 + lane; s < S; s += 64) {
+    const float2 ml = a.ws_ml[(base + s) * kMaxGroup + h];
+    if (ml.y > 0.0f) mx = fmaxf(mx, ml.x);
   }
-  __syncthreads();
+#pragma unroll
+  for (int st = 32; st >= 1; st >>= 1) mx = fmaxf(mx, __shfl_xor(mx, st, 64));
 
-  // ---- (1) merge.  A split without modality m left that block unwritten: the mask
-  // selects, it never multiplies.
-  if (tid < kMaxModalities * D) {
-    float acc = 0.0f;
-    if (merger) {
-#pragma unroll
-      for (int j = 0; j < kCombineBatch; ++j)
-        if (j < nb0 && ((msk[j] >> im) & 1u)) acc = fmaf(wgt[j], x[j], acc);
-      for (int j0 = kCombineBatch; j0 < S; j0 += kCombineBatch) {
-        float y[kCombineBatch];
-#pragma unroll
-        for (int t = 0; t < kCombineBatch; ++t)
-          y[t] = (j0 + t < S && ((msk[j0 + t] >> im) & 1u)) ? src[static_cast<size_t>(j0 + t) * PSTRIDE] : 0.0f;
-#pragma unroll
-        for (int t = 0; t < kCombineBatch; ++t)
-          if (j0 + t < S) acc = fmaf(wgt[j0 + t], y[t], acc);
+  // ---- (1) merge, 64 splits at a time: lane t holds split s0 + t's weight and mask.  A
+  // split without modality m left that block unwritten: the mask selects, it never
+  // multiplies.
+  float acc = 0.0f, lsum = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    float2 ml = ml0;
+    uint32_t mk = mk0;
+    if (s0 > 0) {
+      ml = make_float2(-INFINITY, 0.0f);
+      mk = 0u;
+      if (s0 + lane < S) {
+        ml = a.ws_ml[(base + s0 + lane) * kMaxGroup + h];
+        mk = a.ws_mask[base + s0 + lane];
       }
     }
-    A[im][ik] = acc;
+    float w = 0.0f;
+    if (ml.y > 0.0f) {
+      w = exp2f(ml.x - mx);
+      lsum += w * ml.y;
+    }
+    // splits 0 .. kCombineXB - 1 were loaded up front; later ones 8 at a time
+#pragma unroll
+    for (int t = 0; t < kCombineXB; ++t) {
+      if (s0 > 0 || t >= S) break;
+      const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t));
+      const uint32_t ms = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mk), t));
+      if ((ms >> im) & 1u) acc = fmaf(ws, x[t], acc);
+    }
+    for (int sb = s0 == 0 ? kCombineXB : s0; sb < min(S, s0 + 64); sb += 8) {
+      float y[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) y[t] = (merger && sb + t < S) ? src[static_cast<size_t>(sb + t) * PSTRIDE] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (sb + t >= S) break;
+        // lane index of split sb + t within this group of 64 (sb - s0 + t < 64: wave-uniform)
+        const int li = sb - s0 + t;
+        const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), li));
+        const uint32_t ms = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mk), li));
+        if ((ms >> im) & 1u) acc = fmaf(ws, y[t], acc);
+      }
+    }
   }
+#pragma unroll
+  for (int st = 32; st >= 1; st >>= 1) lsum += __shfl_xor(lsum, st, 64);
+  const float inv_l = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  if (tid < J) A[tid] = merger ? acc : 0.0f;
   __syncthreads();
 
-  // ---- (2) rotation
+  // ---- (2) rotation over this thread's row group
   float o = 0.0f;
 #pragma unroll
-  for (int m = 0; m < kMaxModalities; ++m) {
-    if (m >= a.modalities) break;
-#pragma unroll
-    for (int kk = 0; kk < KPG; ++kk) o = fmaf(u[m][kk], A[m][kg * KPG + kk], o);
+  for (int i = 0; i < JPG; i += 4) {
+    const float4 av = *reinterpret_cast<const float4*>(&A[j0 + i]);
+    o = fmaf(u[i], av.x, o);
+    o = fmaf(u[i + 1], av.y, o);
+    o = fmaf(u[i + 2], av.z, o);
+    o = fmaf(u[i + 3], av.w, o);
   }
-  red[kg][c] = o;
+  red[kq][c] = o;
   __syncthreads();
   if (tid < D) {
     float r = 0.0f;
 #pragma unroll
-    for (int g2 = 0; g2 < KG; ++g2) r += red[g2][tid];
+    for (int g2 = 0; g2 < KQ; ++g2) r += red[g2][tid];
     a.out[(static_cast<size_t>(b) * a.hq + kvh * a.group + h) * D + tid] = r * inv_l;
   }
 }
