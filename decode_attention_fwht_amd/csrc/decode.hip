@@ -239,9 +239,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Ring depth: the deepest of 4, 3, 2 slots per wave that keeps three workgroups per CU
-// (three waves per SIMD) within the 160 KB of LDS (ring + rotated queries + small tables).
-constexpr int kBlocksPerCU = 3;
+// Wait until at most `ahead` groups of L copies are still in flight (ahead <= A).
+template <int L, int A>
+__device__ __forceinline__ void wait_groups(int ahead) {
+  if constexpr (A <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= A) wait_vmcnt<A * L>();
+    else wait_groups<L, A - 1>(ahead);
+  }
+}
+
+// Ring depth: the deepest of 4, 3, 2 slots per wave that keeps kBlocksPerCU workgroups per
+// CU within the 160 KB of LDS (ring + rotated queries + small tables); deeper rings
+// measured slower.  Two workgroups per CU (two waves per SIMD) measured as fast as three
+// and leave each wave registers for the k_min operand.
+constexpr int kBlocksPerCU = 2;
+constexpr bool kBqaInRegs = kBlocksPerCU <= 2;
 template <int D, int KB, int VB>
 struct Lds {
   static constexpr int fits(int ring) {
@@ -441,8 +455,8 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   // K-step s, dword i hold channels c0, c0 + 1 with c0 = g*D/4 + 8 s + 2 i.
   //   alpha/beta/gamma: score operand  fp16 split of (q^ s) scaled by 2^-(KB*peff(s))
   //   bqa:              k_min operand  q^ hi (part 0) or lo (part 1); the same in every wave
-  //                     of the block, so it is kept in LDS (over q_lds) rather than in
-  //                     registers
+  //                     of the block: kept in registers when they allow, else in LDS (over
+  //                     q_lds)
   half2_t alpha[NS][4], beta[NS][4], gamma[NS][4];
   uint4_t bqa[NS];
 #pragma unroll
@@ -473,7 +487,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   static_assert(NS * 64 * 16 <= kMaxGroup * D * 4, "k_min operand table must fit over q_lds");
   uint4_t* const bqa_lds = reinterpret_cast<uint4_t*>(&q_lds[0][0]);  // [NS][64 lanes]
   __syncthreads();  // every wave has read q_lds
-  if (wave == 0) {
+  if (!kBqaInRegs && wave == 0) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) bqa_lds[s * 64 + lane] = bqa[s];
   }
@@ -547,7 +561,10 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     for (int s = 0; s < NS; ++s) {
       const uint4_t sv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_S + g * (D / 2) + 16 * s);
       const uint4_t mv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_M + g * (D / 2) + 16 * s);
-      cm = mfma16(mv4, bqa_lds[s * 64 + lane], cm);
+      if constexpr (kBqaInRegs)
+        cm = mfma16(mv4, bqa[s], cm);
+      else
+        cm = mfma16(mv4, bqa_lds[s * 64 + lane], cm);
       uint32_t bq[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -693,7 +710,8 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     }
   };
 
-  // ---- the visits, chunk by chunk
+  // ---- the visits, chunk by chunk (interleaving the next visit's score contractions
+  // with this one measured slower: the SIMD is issue-bound, not latency-bound)
   for (int c0 = 0; c0 < nw; c0 += 64) {
     if (c0 > 0) begin_chunk(c0);
     for (int i = 0; i < total; ++i) {
@@ -703,11 +721,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       cmask &= cmask - 1u;
       issue_upto(min(total, i + RING));
       // wait for this visit's copies: later visits' copies may stay in flight
-      const int ahead = issued - (i + 1);
-      if (ahead >= 3) wait_vmcnt<3 * L>();
-      else if (ahead == 2) wait_vmcnt<2 * L>();
-      else if (ahead == 1) wait_vmcnt<L>();
-      else wait_vmcnt<0>();
+      wait_groups<L, RING - 1>(issued - (i + 1));
       if (m != cur) make_resident(m);
       const uint8_t* slot = ring_slot(wave, i % RING);
       float4_t cs[2], cm;
