@@ -24,6 +24,10 @@ Source pages (cited by title and section):
 * Decode: attention over the dequantized cache.  The pages' fused kernel
   reorders this computation ([paper] §1, Fig. 1(d)); the oracle computes the
   plain definition, softmax(scale * q . k_hat) . v_hat, in float64.
+* Streaming generation ([paper] §3.1 Implementation details, captioning):
+  keys are quantized every 128 tokens in groups of 32; values stay in a
+  128-token sliding FP16 window before quantization.  Recent tokens enter the
+  attention as stored (no quantization).
 
 Fixed arithmetic of the codec (fp32, in this exact order, so that the GPU
 codes and metadata can be compared bit for bit):
@@ -396,6 +400,62 @@ def decode_attention(q, seq_lens, cache: dict, signs, U, levels16, scale: Option
         vals = dequantize_values(sl(cache["v_codes"]), cache["v_scale"][b:b + 1, kv:kv + 1, :nw * WINDOW],
                                  cache["modality"][b:b + 1], U, levels16, cache["value_bits"],
                                  length=n)[0, 0]
+        for h in heads:
+            out[b, h] = attention_f64(q[b, h], keys, vals, scale)
+    return out
+
+
+# ----------------------------------------------------------------------------- streaming
+def stream_packed_lengths(n: int):
+    """(key_packed, value_packed): how many leading tokens of an n-token stream have
+    quantized keys and values ([paper] §3.1 Implementation details, captioning).
+
+    Keys are quantized every 128 tokens, as four 32-token groups: the first
+    128 * floor(n / 128) tokens.  Values stay in a sliding FP16 window of the 128
+    most recent tokens and are quantized once they leave it; with values packed
+    in 32-token windows, a window is quantized when its last token has left, so
+    32 * floor(max(0, n - 128) / 32) tokens (reading: the pages do not say how the
+    sliding window meets the 32-token grouping).
+    """
+    n = int(n)
+    return (n // 128) * 128, (max(0, n - 128) // WINDOW) * WINDOW
+
+
+def decode_attention_streaming(q, seq_lens, cache: dict, k_recent, v_recent, signs, U, levels16,
+                               scale: Optional[float] = None, rows: Optional[Sequence] = None):
+    """Decode attention over a streamed cache, float64.
+
+    Token t of sequence b attends with the dequantized packed key when
+    t < key_packed and with k_recent[b, t, kv] (the stored key, as given)
+    otherwise; values likewise with value_packed; (key_packed, value_packed) =
+    stream_packed_lengths(seq_lens[b]).  k_recent, v_recent: [B][T][Hkv][d]
+    indexed by absolute token position (only the unquantized tokens are read).
+    """
+    B, Hq, d = q.shape
+    Hkv = cache["k_min"].shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if not scale else float(scale)
+    out = np.zeros((B, Hq, d))
+    want = [(b, h) for b in range(B) for h in range(Hq)] if rows is None else list(rows)
+    by_kv = {}
+    for b, h in want:
+        by_kv.setdefault((b, h // G), []).append(h)
+    for (b, kv), heads in sorted(by_kv.items()):
+        n = int(seq_lens[b])
+        kp, vp = stream_packed_lengths(n)
+        keys = np.asarray(k_recent[b, :n, kv], np.float64).copy()
+        vals = np.asarray(v_recent[b, :n, kv], np.float64).copy()
+        if kp > 0:
+            nw = kp // WINDOW
+            sl = lambda a: a[b:b + 1, kv:kv + 1, :nw]
+            keys[:kp] = dequantize_keys(sl(cache["k_codes"]), sl(cache["k_min"]), sl(cache["k_scale"]),
+                                        signs, cache["key_bits"], length=kp)[0, 0]
+        if vp > 0:
+            nw = vp // WINDOW
+            vals[:vp] = dequantize_values(cache["v_codes"][b:b + 1, kv:kv + 1, :nw],
+                                          cache["v_scale"][b:b + 1, kv:kv + 1, :vp],
+                                          cache["modality"][b:b + 1], U, levels16, cache["value_bits"],
+                                          length=vp)[0, 0]
         for h in heads:
             out[b, h] = attention_f64(q[b, h], keys, vals, scale)
     return out

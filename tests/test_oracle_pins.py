@@ -392,3 +392,77 @@ def test_gqa_head_mapping():
     for h in range(16):
         assert np.allclose(out[0, h], vals[0, h // 8].mean(0), atol=1e-12)
     assert not np.allclose(out[0, 0], out[0, 8])
+
+
+# ----------------------------------------------------------------------------- streaming
+def test_stream_schedule_follows_the_pages():
+    """[paper] §3.1 Implementation details: keys are quantized every 128 tokens in
+    groups of 32; values keep a 128-token sliding FP16 window.  Checked on every
+    length up to 1000: key_packed is the largest multiple of 128 <= n; every value
+    among the 128 most recent stays FP16 and at most 31 older ones wait for their
+    32-token window to complete."""
+    for n in range(1001):
+        kp, vp = O.stream_packed_lengths(n)
+        assert kp % 128 == 0 and kp <= n < kp + 128
+        assert vp % 32 == 0 and vp <= max(0, n - 128)
+        assert n - vp < 128 + 32 or n < 128
+        assert vp <= kp  # a token with a quantized value also has a quantized key
+    assert [O.stream_packed_lengths(n) for n in (0, 127, 128, 159, 160, 255, 256, 300, 384)] == [
+        (0, 0), (0, 0), (128, 0), (128, 0), (128, 32), (128, 96), (256, 128), (256, 160), (384, 256)]
+
+
+def test_key_groups_do_not_depend_on_flush_granularity():
+    """Quantizing 128 tokens at once or as four 32-token groups gives the same codes
+    and metadata: the range belongs to the group alone ([paper] §3.1, g = 32)."""
+    cfg = synth.CONFIGS[1]
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((1, 128, 1, cfg.head_dim)).astype(np.float32)
+    signs = synth.rademacher_signs(cfg.head_dim, 0)
+    whole = O.quantize_keys(k, signs, 2)
+    parts = [O.quantize_keys(k[:, 32 * i:32 * i + 32], signs, 2) for i in range(4)]
+    for j in range(3):
+        assert np.array_equal(whole[j], np.concatenate([p[j] for p in parts], axis=2))
+
+
+def test_streaming_attention_special_cases():
+    """No packed token: plain attention over the stored keys and values (brute force
+    over a tiny input).  Every token packed: the non-streaming decode."""
+    cfg = synth.CONFIGS[1]
+    d, G = cfg.head_dim, cfg.q_heads // cfg.kv_heads
+    rng = np.random.default_rng(5)
+    T = 96
+    k = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    v = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    q = rng.standard_normal((1, cfg.q_heads, d)).astype(np.float32)
+    signs = synth.rademacher_signs(d, 0)
+    U = synth.value_rotations(d, 0)
+    lv = O.value_codebook_f16(2)
+    tags = np.zeros((1, T), np.uint8)
+    kc, km, ks = O.quantize_keys(k, signs, 2)
+    vc, vs = O.quantize_values(v, tags, U, lv, 2)
+    cache = dict(k_codes=kc, k_min=km, k_scale=ks, v_codes=vc, v_scale=vs, modality=tags, key_bits=2, value_bits=2)
+    out = O.decode_attention_streaming(q, [T], cache, k, v, signs, U, lv)   # T < 128: nothing packed
+    for h in range(cfg.q_heads):
+        logits = [sum(float(q[0, h, c]) * float(k[0, t, 0, c]) for c in range(d)) / math.sqrt(d) for t in range(T)]
+        mx = max(logits)
+        w = [math.exp(x - mx) for x in logits]
+        ref = [sum(w[t] * float(v[0, t, 0, c]) for t in range(T)) / sum(w) for c in range(d)]
+        assert np.allclose(out[0, h], ref, rtol=1e-12, atol=1e-12)
+    # a 300-token stream: keys of tokens 256.. and values of tokens 160.. unquantized;
+    # against attention over explicitly assembled keys and values
+    T, n = 320, 300
+    k = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    v = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    tags = np.zeros((1, T), np.uint8)
+    kc, km, ks = O.quantize_keys(k, signs, 2)
+    vc, vs = O.quantize_values(v, tags, U, lv, 2)
+    cache = dict(k_codes=kc, k_min=km, k_scale=ks, v_codes=vc, v_scale=vs, modality=tags, key_bits=2, value_bits=2)
+    out = O.decode_attention_streaming(q, [n], cache, k, v, signs, U, lv)
+    kq = O.dequantize_keys(kc, km, ks, signs, 2)[0, 0]
+    vq = O.dequantize_values(vc, vs, tags, U, lv, 2)[0, 0]
+    keys = np.concatenate([kq[:256], k[0, 256:n, 0].astype(np.float64)])
+    vals = np.concatenate([vq[:160], v[0, 160:n, 0].astype(np.float64)])
+    for h in range(cfg.q_heads):
+        assert np.allclose(out[0, h], O.attention_f64(q[0, h], keys, vals, 1.0 / math.sqrt(d)), rtol=1e-12, atol=1e-14)
+    full = O.decode_attention(q, [n], cache, signs, U, lv)
+    assert not np.allclose(out, full)  # the unquantized tokens matter
