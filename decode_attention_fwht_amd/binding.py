@@ -22,7 +22,8 @@ F32, BF16 = 0, 1
 EXPORTED = (
     "omnikv_create", "omnikv_destroy", "omnikv_value_codebook", "omnikv_quantize_keys",
     "omnikv_quantize_values", "omnikv_decode_workspace_size", "omnikv_decode_attention",
-    "omnikv_decode_partial", "omnikv_decode_combine", "omnikv_last_error",
+    "omnikv_decode_partial", "omnikv_decode_combine", "omnikv_stream_packed_lengths", "omnikv_stream_append",
+    "omnikv_decode_attention_streaming", "omnikv_last_error",
 )
 
 
@@ -60,6 +61,12 @@ def load() -> ctypes.CDLL:
     L.omnikv_decode_partial.argtypes = [vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, i64,
                                         ctypes.c_float, i32, vp, sz, vp]
     L.omnikv_decode_combine.argtypes = [vp, vp, i32, i64, i32, vp, sz, vp, vp]
+    L.omnikv_stream_packed_lengths.argtypes = [i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.omnikv_stream_append.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i32, vp, vp, i32,
+                                       vp, vp, vp, vp, vp, vp, i64, vp]
+    L.omnikv_decode_attention_streaming.argtypes = [vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, i64,
+                                                    vp, vp, ctypes.c_int, i32, ctypes.c_float, i32, vp, sz,
+                                                    vp, vp]
     for name in EXPORTED:
         if name == "omnikv_last_error":
             continue
@@ -193,4 +200,51 @@ class Context:
                        stream=None):
         _check(load().omnikv_decode_combine(self._h, _ptr(seq_lens), batch, max_len, num_splits,
                                             _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+        return out
+
+    # -- streaming generation
+    def alloc_rings(self, batch: int, ring_cap: int = 256, dtype=None, device="cuda"):
+        """Rings of recent keys and values [B][ring_cap][Hkv][d] (plain storage)."""
+        import torch
+        dtype = torch.bfloat16 if dtype is None else dtype
+        shape = (batch, ring_cap, self.num_kv_heads, self.head_dim)
+        return dict(k=torch.zeros(shape, dtype=dtype, device=device), v=torch.zeros(shape, dtype=dtype, device=device),
+                    cap=ring_cap)
+
+    @staticmethod
+    def stream_packed_lengths(n: int):
+        kp, vp = ctypes.c_int64(), ctypes.c_int64()
+        _check(load().omnikv_stream_packed_lengths(n, ctypes.byref(kp), ctypes.byref(vp)))
+        return kp.value, vp.value
+
+    def stream_append(self, k_new, v_new, tags_new, lens, lens_host, cache: dict, rings: dict, stream=None):
+        """One token per sequence: k_new, v_new [B][Hkv][d]; tags_new uint8 [B]; lens int32 [B]
+        (device) and lens_host (host sequence of ints) are the lengths before the append."""
+        import torch
+        if k_new.dtype != rings["k"].dtype or v_new.dtype != rings["v"].dtype:
+            raise ValueError("k_new / v_new must have the rings' dtype")
+        dt = BF16 if k_new.dtype == torch.bfloat16 else F32
+        B = int(k_new.shape[0])
+        lh = (ctypes.c_int64 * B)(*[int(x) for x in lens_host])
+        _check(load().omnikv_stream_append(
+            self._h, _ptr(k_new), _ptr(v_new), dt, _ptr(tags_new), _ptr(lens), lh, B, _ptr(rings["k"]),
+            _ptr(rings["v"]), rings["cap"], _ptr(cache["k_codes"]), _ptr(cache["k_min"]), _ptr(cache["k_scale"]),
+            _ptr(cache["v_codes"]), _ptr(cache["v_scale"]), _ptr(cache["modality"]), cache["t_cap"],
+            _stream(stream)))
+
+    def decode_streaming(self, q, seq_lens, max_len: int, cache: dict, rings: dict, out=None, workspace=None,
+                         softmax_scale: float = 0.0, num_splits: int = 0, stream=None):
+        import torch
+        B = int(q.shape[0])
+        if out is None:
+            out = torch.empty((B, self.num_q_heads, self.head_dim), dtype=torch.float32, device=q.device)
+        need = self.workspace_size(B, max_len, num_splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        dt = BF16 if rings["k"].dtype == torch.bfloat16 else F32
+        _check(load().omnikv_decode_attention_streaming(
+            self._h, _ptr(q), _ptr(seq_lens), B, max_len, _ptr(cache["k_codes"]), _ptr(cache["k_min"]),
+            _ptr(cache["k_scale"]), _ptr(cache["v_codes"]), _ptr(cache["v_scale"]), _ptr(cache["modality"]),
+            cache["t_cap"], _ptr(rings["k"]), _ptr(rings["v"]), dt, rings["cap"], softmax_scale, num_splits,
+            _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
         return out

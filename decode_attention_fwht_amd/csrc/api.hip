@@ -335,7 +335,8 @@ omnikv_status decode_partial(const omnikv_ctx* ctx, const float* q, const int32_
   if ((st = check_decode(ctx, batch, max_len, t_cap, num_splits, workspace_bytes, &plan)) != OMNIKV_OK) return st;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(ctx->sh.d));
   const hipError_t e = omnikv::launch_decode_partial(ctx->sh, ctx->tb, plan, q, seq_lens, batch, max_len, k_codes, k_min,
-                                                     k_scale, v_codes, v_scale, modality, t_cap, scale, workspace, stream);
+                                                     k_scale, v_codes, v_scale, modality, t_cap, scale, workspace,
+                                                     false, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
   return OMNIKV_OK;
 }
@@ -352,7 +353,8 @@ omnikv_status decode_combine(const omnikv_ctx* ctx, const int32_t* seq_lens, int
   if ((st = check_decode(ctx, batch, max_len, max_len > 0 ? ((max_len + 31) / 32) * 32 : 32, num_splits,
                          workspace_bytes, &plan)) != OMNIKV_OK)
     return st;
-  const hipError_t e = omnikv::launch_decode_combine(ctx->sh, ctx->tb, plan, seq_lens, batch, workspace, out, stream);
+  const hipError_t e =
+      omnikv::launch_decode_combine(ctx->sh, ctx->tb, plan, seq_lens, batch, workspace, out, nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_combine launch");
   return OMNIKV_OK;
 }
@@ -387,6 +389,116 @@ omnikv_status omnikv_decode_attention(const omnikv_ctx* ctx, const float* q, con
                                           modality, t_cap, softmax_scale, num_splits, workspace, workspace_bytes, stream);
   if (st != OMNIKV_OK) return st;
   return decode_combine(ctx, seq_lens, batch, max_len, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+omnikv_status omnikv_stream_packed_lengths(int64_t n, int64_t* key_packed, int64_t* value_packed) {
+  if (n < 0) return fail(OMNIKV_EINVAL, "stream length must be >= 0 (got %lld)", (long long)n);
+  if (!key_packed || !value_packed) return fail(OMNIKV_EINVAL, "stream_packed_lengths: NULL output");
+  *key_packed = omnikv::stream_key_packed(n);
+  *value_packed = omnikv::stream_value_packed(n);
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_stream_append(const omnikv_ctx* ctx, const void* k_new, const void* v_new, omnikv_dtype dt,
+                                   const uint8_t* tags_new, const int32_t* lens, const int64_t* lens_host,
+                                   int32_t batch, void* k_ring, void* v_ring, int32_t ring_cap, uint32_t* k_codes,
+                                   uint16_t* k_min, uint16_t* k_scale, uint32_t* v_codes, uint16_t* v_scale,
+                                   uint8_t* modality, int64_t t_cap, hipStream_t stream) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (dt != OMNIKV_F32 && dt != OMNIKV_BF16) return fail(OMNIKV_EINVAL, "stream_append: dtype must be F32 or BF16");
+  if (batch <= 0) return fail(OMNIKV_EINVAL, "batch must be positive (got %d)", batch);
+  if (!k_new || !v_new || !tags_new || !lens || !lens_host || !k_ring || !v_ring || !k_codes || !k_min || !k_scale ||
+      !v_codes || !v_scale || !modality)
+    return fail(OMNIKV_EINVAL, "stream_append: NULL pointer");
+  // (tags_new and lens are read one element per sequence and need no alignment)
+  const void* ptrs[] = {k_new, v_new, k_ring, v_ring, k_codes, k_min, k_scale, v_codes, v_scale, modality};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(OMNIKV_EINVAL, "stream_append: device pointers must be 16-byte aligned");
+  if (ring_cap < omnikv::kStreamRecent + omnikv::kWindow || ring_cap % omnikv::kStreamRecent || ring_cap > omnikv::kMaxRingCap)
+    return fail(OMNIKV_EINVAL, "ring_cap must be a multiple of 128 in [256, 512] (got %d)", ring_cap);
+  if (t_cap <= 0 || t_cap % omnikv::kWindow) return fail(OMNIKV_EINVAL, "t_cap must be a positive multiple of 32");
+  for (int32_t b = 0; b < batch; ++b)
+    if (lens_host[b] < 0 || lens_host[b] + 1 > t_cap)
+      return fail(OMNIKV_EINVAL, "stream_append: sequence %d has %lld tokens; the cache holds %lld", b,
+                  (long long)lens_host[b], (long long)t_cap);
+  const omnikv::Shape& sh = ctx->sh;
+  const bool f32 = dt == OMNIKV_F32;
+  hipError_t e = omnikv::launch_stream_append(sh, k_new, v_new, f32, tags_new, lens, batch, k_ring, v_ring, ring_cap,
+                                              modality, t_cap, stream);
+  if (e != hipSuccess) return hip_fail(e, "stream_append launch");
+  // tokens that this append pushes past the schedule's thresholds are quantized from
+  // the rings, one sequence at a time (their rows are contiguous: the blocks are 32- or
+  // 128-aligned and ring_cap is a multiple of 128)
+  const size_t esz = f32 ? 4 : 2;
+  const size_t nwin = static_cast<size_t>(t_cap / omnikv::kWindow);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n0 = lens_host[b], n1 = n0 + 1;
+    const int64_t k0 = omnikv::stream_key_packed(n0), k1 = omnikv::stream_key_packed(n1);
+    const int64_t v0 = omnikv::stream_value_packed(n0), v1 = omnikv::stream_value_packed(n1);
+    const size_t head_win = static_cast<size_t>(b) * sh.hkv * nwin;  // first window block of sequence b
+    if (k1 > k0) {
+      const char* src = static_cast<const char*>(k_ring) + (static_cast<size_t>(b) * ring_cap + k0 % ring_cap) * sh.hkv * sh.d * esz;
+      e = omnikv::launch_quantize_keys(sh, ctx->tb, src, !f32, 1, k0, k1 - k0, t_cap,
+                                       k_codes + head_win * sh.d * sh.kbits, k_min + head_win * sh.d,
+                                       k_scale + head_win * sh.d, stream);
+      if (e != hipSuccess) return hip_fail(e, "stream_append key flush");
+    }
+    if (v1 > v0) {
+      const char* src = static_cast<const char*>(v_ring) + (static_cast<size_t>(b) * ring_cap + v0 % ring_cap) * sh.hkv * sh.d * esz;
+      e = omnikv::launch_quantize_values(sh, ctx->tb, src, !f32, modality + static_cast<size_t>(b) * t_cap, 1, v0,
+                                         v1 - v0, t_cap, v_codes + head_win * sh.d * sh.vbits,
+                                         v_scale + static_cast<size_t>(b) * sh.hkv * t_cap, stream);
+      if (e != hipSuccess) return hip_fail(e, "stream_append value flush");
+    }
+  }
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_decode_attention_streaming(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens,
+                                                int32_t batch, int64_t max_len, const uint32_t* k_codes,
+                                                const uint16_t* k_min, const uint16_t* k_scale,
+                                                const uint32_t* v_codes, const uint16_t* v_scale,
+                                                const uint8_t* modality, int64_t t_cap, const void* k_ring,
+                                                const void* v_ring, omnikv_dtype ring_dtype, int32_t ring_cap,
+                                                float softmax_scale, int32_t num_splits, void* workspace,
+                                                size_t workspace_bytes, float* out, hipStream_t stream) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!q || !seq_lens || !k_codes || !k_min || !k_scale || !v_codes || !v_scale || !modality || !k_ring || !v_ring ||
+      !workspace || !out)
+    return fail(OMNIKV_EINVAL, "decode_attention_streaming: NULL device pointer");
+  const void* ptrs[] = {q, seq_lens, k_codes, k_min, k_scale, v_codes, v_scale, modality, k_ring, v_ring, workspace, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(OMNIKV_EINVAL, "decode_attention_streaming: device pointers must be 16-byte aligned");
+  if (ring_dtype != OMNIKV_F32 && ring_dtype != OMNIKV_BF16)
+    return fail(OMNIKV_EINVAL, "decode_attention_streaming: ring dtype must be F32 or BF16");
+  if (ring_cap < omnikv::kStreamRecent + omnikv::kWindow || ring_cap % omnikv::kStreamRecent || ring_cap > omnikv::kMaxRingCap)
+    return fail(OMNIKV_EINVAL, "ring_cap must be a multiple of 128 in [256, 512] (got %d)", ring_cap);
+  if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale)) return fail(OMNIKV_EINVAL, "softmax_scale must be finite and >= 0");
+  omnikv::DecodePlan plan;
+  if ((st = check_decode(ctx, batch, max_len, t_cap, num_splits, workspace_bytes, &plan)) != OMNIKV_OK) return st;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(ctx->sh.d));
+  hipError_t e = omnikv::launch_decode_partial(ctx->sh, ctx->tb, plan, q, seq_lens, batch, max_len, k_codes, k_min,
+                                               k_scale, v_codes, v_scale, modality, t_cap, scale, workspace, true,
+                                               stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
+  omnikv::StreamTail tail;
+  tail.q = q;
+  tail.seq_lens = seq_lens;
+  tail.max_len = max_len;
+  tail.k_codes = k_codes;
+  tail.k_min = k_min;
+  tail.k_scale = k_scale;
+  tail.t_cap = t_cap;
+  tail.k_ring = k_ring;
+  tail.v_ring = v_ring;
+  tail.ring_f32 = ring_dtype == OMNIKV_F32;
+  tail.ring_cap = ring_cap;
+  tail.scale_log2 = scale * 1.4426950408889634f;
+  e = omnikv::launch_decode_combine(ctx->sh, ctx->tb, plan, seq_lens, batch, workspace, out, &tail, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_combine launch");
+  return OMNIKV_OK;
 }
 
 const char* omnikv_last_error(void) { return g_error.c_str(); }

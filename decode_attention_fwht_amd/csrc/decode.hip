@@ -171,6 +171,7 @@ struct PartialArgs {
   uint32_t* ws_mask; // [unit][split] modalities present
   float* ws_acc;     // [unit][split][M][8][D]
   float* ws_stash;   // [unit][split][wave][2][8][D]
+  int stream;        // 1: attend over the value-packed prefix of each stream (the rest is recent)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -293,8 +294,9 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int unit = blockIdx.y;                     // b * hkv + kvh
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  const int len = __builtin_amdgcn_readfirstlane(
+  int len = __builtin_amdgcn_readfirstlane(
       static_cast<int>(min<int64_t>(max<int64_t>(a.seq_lens[b], 0), a.max_len)));
+  if (a.stream) len = stream_value_packed(len);
   const int nwin = (len + kWindow - 1) / kWindow;
   const int wbeg = (blockIdx.x * kWaves + wave) * a.wpw;  // this wave's run of windows
   const int wend = min(nwin, wbeg + a.wpw);
@@ -822,7 +824,37 @@ struct CombineArgs {
   const uint32_t* ws_mask;
   const float* ws_acc;
   float* out;
+  // streamed sequences only: the recent tokens
+  const float* signs;        // [d] the key rotation's D
+  int kbits;
+  StreamTail tail;
 };
+
+// Key code of window token t, rotated channel c, in a key window block (the layout of
+// the quantizer's pack, described with the public cache layout).
+template <int D>
+__device__ inline uint32_t key_code_at(const uint32_t* blk, int kbits, int t, int c) {
+  const int tau = t >> 4, rho = t & 15;
+  const int g = c / (D / 4), r = c % (D / 4);
+  const int s = r >> 3, j = r & 7, i = j >> 1, e = j & 1;
+  const int per_lane = D * kbits / 64;
+  int lw, slot;
+  if (D == 128) {
+    if (kbits == 2) { lw = i; slot = 4 * tau + s; }
+    else { lw = 4 * tau + i; slot = s; }
+  } else {
+    if (kbits == 2) { lw = i & 1; slot = 4 * (i >> 1) + 2 * tau + s; }
+    else { lw = i; slot = 2 * tau + s; }
+  }
+  const uint32_t word = blk[(16 * g + rho) * per_lane + lw];
+  return (word >> (16 * e + kbits * slot)) & ((1u << kbits) - 1u);
+}
+
+__device__ inline float ring_elem(const void* ring, size_t idx, bool f32) {
+  if (f32) return static_cast<const float*>(ring)[idx];
+  return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(ring)[idx]) << 16);
+}
+__device__ inline float f16_to_float(uint16_t bits) { return static_cast<float>(__builtin_bit_cast(_Float16, bits)); }
 
 // One block per (query head, sequence x KV head).  Every global load that depends on
 // nothing is issued first - all of this thread's rotation rows, the first batch of split
@@ -835,7 +867,9 @@ constexpr int kCombineThreads = 1024;
 constexpr int kCombineXB = 32;    // splits per batch of accumulator loads
 constexpr int kMaxSplits = 1024;  // splits per (sequence, KV head)
 
-template <int D>
+constexpr int kMaxRing = kMaxRingCap;
+
+template <int D, bool STREAM>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a) {
   constexpr int J = kMaxModalities * D;       // stacked rotation rows (m, k)
   constexpr int KQ = kCombineThreads / D;     // row groups
@@ -844,7 +878,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   constexpr int PSTRIDE = kMaxModalities * kMaxGroup * D;  // floats per split
   __shared__ __attribute__((aligned(16))) float A[J];
   __shared__ float red[KQ][D];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = blockIdx.x, unit = blockIdx.y;
   if (h >= a.group) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
@@ -873,6 +907,82 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
     mk0 = a.ws_mask[base + lane];
   }
 
+  // ---- streamed sequences: scores of the recent tokens [T0, len) in log2 units.  A
+  // token below the key-packed length uses its packed key with the rotated query (the
+  // codec's butterflies), a later one its stored key with the query itself.
+  __shared__ float tsc[STREAM ? kMaxRing : 1];
+  __shared__ float qo[STREAM ? D : 1], qr[STREAM ? D : 1];
+  __shared__ float tred[kCombineThreads / 64];
+  __shared__ float tstat;
+  int T0 = 0, nt = 0;
+  float tmx = -INFINITY;
+  if constexpr (STREAM) {
+    const StreamTail& st = a.tail;
+    const int len = static_cast<int>(min<int64_t>(max<int64_t>(st.seq_lens[b], 0), st.max_len));
+    const int Pk = static_cast<int>(stream_key_packed(len));
+    T0 = max(static_cast<int>(stream_value_packed(len)), len - st.ring_cap);
+    nt = len - T0;
+    if (tid < D) {
+      const float qv = st.q[(static_cast<size_t>(b) * a.hq + kvh * a.group + h) * D + tid];
+      qo[tid] = qv;
+      qr[tid] = qv * a.signs[tid];
+    }
+    __syncthreads();
+    if (T0 < Pk) {
+      for (int hh = 1; hh < D; hh <<= 1) {
+        if (tid < D / 2) {
+          const int i = (tid / hh) * 2 * hh + (tid % hh);
+          const float x0 = qr[i], x1 = qr[i + hh];
+          qr[i] = x0 + x1;
+          qr[i + hh] = x0 - x1;
+        }
+        __syncthreads();
+      }
+    }
+    constexpr int CPT = D / 8;  // eight threads per token
+    const int sub = tid & 7;
+    for (int j0 = 0; j0 < nt; j0 += kCombineThreads / 8) {
+      const int j = j0 + (tid >> 3);
+      float acc = 0.0f;
+      if (j < nt) {
+        const int t = T0 + j;
+        if (t < Pk) {
+          const size_t wb = static_cast<size_t>(unit) * (st.t_cap / kWindow) + t / kWindow;
+          const uint32_t* blk = st.k_codes + wb * (D * a.kbits);
+          const uint16_t* mrow = st.k_min + wb * D;
+          const uint16_t* srow = st.k_scale + wb * D;
+          for (int cc = 0; cc < CPT; ++cc) {
+            const int c2 = sub * CPT + cc;
+            const float code = static_cast<float>(key_code_at<D>(blk, a.kbits, t % kWindow, c2));
+            acc = fmaf(qr[c2], f16_to_float(mrow[c2]) + f16_to_float(srow[c2]) * code, acc);
+          }
+          acc *= RhtConst<D>::value;
+        } else {
+          const size_t row = ((static_cast<size_t>(b) * st.ring_cap + t % st.ring_cap) * a.hkv + kvh) * D + sub * CPT;
+          for (int cc = 0; cc < CPT; ++cc) acc = fmaf(qo[sub * CPT + cc], ring_elem(st.k_ring, row + cc, st.ring_f32), acc);
+        }
+      }
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
+      if (j < nt && sub == 0) tsc[j] = acc * st.scale_log2;
+    }
+    __syncthreads();
+    float lm = -INFINITY;
+    for (int j = tid; j < nt; j += kCombineThreads) lm = fmaxf(lm, tsc[j]);
+#pragma unroll
+    for (int sx = 32; sx >= 1; sx >>= 1) lm = fmaxf(lm, __shfl_xor(lm, sx, 64));
+    if (lane == 0) tred[wv] = lm;
+    __syncthreads();
+    if (tid == 0) {
+      float m = -INFINITY;
+      for (int x = 0; x < kCombineThreads / 64; ++x) m = fmaxf(m, tred[x]);
+      tstat = m;
+    }
+    __syncthreads();
+    tmx = tstat;
+  }
+
   // ---- largest split max (every wave alike)
   float mx = ml0.y > 0.0f ? ml0.x : -INFINITY;
   for (int s = 64 + lane; s < S; s += 64) {
@@ -881,6 +991,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   }
 #pragma unroll
   for (int st = 32; st >= 1; st >>= 1) mx = fmaxf(mx, __shfl_xor(mx, st, 64));
+  mx = fmaxf(mx, tmx);
 
   // ---- (1) merge, 64 splits at a time: lane t holds split s0 + t's weight and mask.  A
   // split without modality m left that block unwritten: the mask selects, it never
@@ -927,8 +1038,33 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   }
 #pragma unroll
   for (int st = 32; st >= 1; st >>= 1) lsum += __shfl_xor(lsum, st, 64);
-  const float inv_l = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   if (tid < J) A[tid] = merger ? acc : 0.0f;
+  // ---- streamed sequences: probabilities of the recent tokens and their values, which
+  // are in the original space (added after the inverse rotation)
+  float ot = 0.0f;
+  if constexpr (STREAM) {
+    const StreamTail& st = a.tail;
+    float ls = 0.0f;
+    for (int j = tid; j < nt; j += kCombineThreads) {
+      const float p = exp2f(tsc[j] - mx);
+      tsc[j] = p;
+      ls += p;
+    }
+#pragma unroll
+    for (int sx = 32; sx >= 1; sx >>= 1) ls += __shfl_xor(ls, sx, 64);
+    __syncthreads();  // tred reads of the max are done; tsc holds probabilities
+    if (lane == 0) tred[wv] = ls;
+    for (int j = kq; j < nt; j += KQ) {
+      const int t = T0 + j;
+      const size_t idx = ((static_cast<size_t>(b) * st.ring_cap + t % st.ring_cap) * a.hkv + kvh) * D + c;
+      ot = fmaf(tsc[j], ring_elem(st.v_ring, idx, st.ring_f32), ot);
+    }
+    __syncthreads();
+    float tl = 0.0f;
+    for (int x = 0; x < kCombineThreads / 64; ++x) tl += tred[x];
+    lsum += tl;
+  }
+  const float inv_l = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   __syncthreads();
 
   // ---- (2) rotation over this thread's row group
@@ -941,7 +1077,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
     o = fmaf(u[i + 2], av.z, o);
     o = fmaf(u[i + 3], av.w, o);
   }
-  red[kq][c] = o;
+  red[kq][c] = o + ot;
   __syncthreads();
   if (tid < D) {
     float r = 0.0f;
@@ -1009,11 +1145,11 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
                                    const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
                                    const uint32_t* kc, const uint16_t* km, const uint16_t* ks,
                                    const uint32_t* vc, const uint16_t* vs, const uint8_t* mod,
-                                   int64_t t_cap, float scale, void* ws, hipStream_t st) {
+                                   int64_t t_cap, float scale, void* ws, bool stream, hipStream_t st) {
   const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits, sh.d);
   PartialArgs pa{q, seq_lens, kc, km, ks, vc, vs, mod, tb.signs, tb.pair_table, sh.hq, sh.hkv, sh.group,
                  sh.modalities, t_cap, max_len, scale * 1.4426950408889634f, plan.windows_per_wave, plan.splits,
-                 w.ml, w.mask, w.acc, w.stash};
+                 w.ml, w.mask, w.acc, w.stash, stream ? 1 : 0};
   const dim3 grid(static_cast<unsigned>(plan.splits), static_cast<unsigned>(batch * sh.hkv));
   constexpr size_t dyn_bytes = Lds<D, KB, VB>::DYN;
   static bool attr_set = false;  // dynamic LDS above the 64 KB default needs the attribute
@@ -1030,11 +1166,12 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
 hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan, const float* q,
                                  const int32_t* seq_lens, int batch, int64_t max_len, const uint32_t* kc,
                                  const uint16_t* km, const uint16_t* ks, const uint32_t* vc, const uint16_t* vs,
-                                 const uint8_t* mod, int64_t t_cap, float scale, void* ws, hipStream_t st) {
+                                 const uint8_t* mod, int64_t t_cap, float scale, void* ws, bool stream,
+                                 hipStream_t st) {
 #define OMNIKV_DEC(D_, KB_, VB_)                                                                           \
   if (sh.d == D_ && sh.kbits == KB_ && sh.vbits == VB_)                                                    \
     return launch_partial_t<D_, KB_, VB_>(sh, tb, plan, q, seq_lens, batch, max_len, kc, km, ks, vc, vs, mod, \
-                                          t_cap, scale, ws, st);
+                                          t_cap, scale, ws, stream, st);
   OMNIKV_DEC(128, 2, 2)
   OMNIKV_DEC(128, 4, 4)
   OMNIKV_DEC(128, 2, 4)
@@ -1048,14 +1185,56 @@ hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const 
 }
 
 hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
-                                 const int32_t* seq_lens, int batch, const void* ws, float* out, hipStream_t st) {
+                                 const int32_t* seq_lens, int batch, const void* ws, float* out,
+                                 const StreamTail* tail, hipStream_t st) {
   const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits, sh.d);
-  CombineArgs ca{tb.rotations_t, sh.hq, sh.hkv, sh.group, sh.modalities, plan.splits, w.ml, w.mask, w.acc, out};
+  CombineArgs ca{tb.rotations_t, sh.hq, sh.hkv, sh.group, sh.modalities, plan.splits, w.ml, w.mask, w.acc, out,
+                 tb.signs, sh.kbits, tail ? *tail : StreamTail{}};
+  (void)seq_lens;
   const dim3 grid(static_cast<unsigned>(sh.group), static_cast<unsigned>(batch * sh.hkv));
-  if (sh.d == 128)
-    decode_combine_kernel<128><<<grid, kCombineThreads, 0, st>>>(ca);
+  if (sh.d == 128) {
+    if (tail) decode_combine_kernel<128, true><<<grid, kCombineThreads, 0, st>>>(ca);
+    else decode_combine_kernel<128, false><<<grid, kCombineThreads, 0, st>>>(ca);
+  } else {
+    if (tail) decode_combine_kernel<64, true><<<grid, kCombineThreads, 0, st>>>(ca);
+    else decode_combine_kernel<64, false><<<grid, kCombineThreads, 0, st>>>(ca);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+
+// One block per (KV head, sequence), one thread per channel: the new token's key and
+// value go to ring row lens[b] % ring_cap, its tag to modality[b][lens[b]].
+template <typename T>
+__global__ void stream_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                     const uint8_t* __restrict__ tags_new, const int32_t* __restrict__ lens,
+                                     int hkv, int d, T* __restrict__ k_ring, T* __restrict__ v_ring, int ring_cap,
+                                     uint8_t* __restrict__ modality, int64_t t_cap) {
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int64_t len = lens[b];
+  if (len < 0 || len >= t_cap || c >= d) return;  // outside the cache: nothing to write
+  const size_t src = (static_cast<size_t>(b) * hkv + h) * d + c;
+  const size_t dst = ((static_cast<size_t>(b) * ring_cap + len % ring_cap) * hkv + h) * d + c;
+  k_ring[dst] = k_new[src];
+  v_ring[dst] = v_new[src];
+  if (h == 0 && c == 0) modality[static_cast<size_t>(b) * t_cap + len] = tags_new[b];
+}
+
+}  // namespace
+
+hipError_t launch_stream_append(const Shape& sh, const void* k_new, const void* v_new, bool f32,
+                                const uint8_t* tags_new, const int32_t* lens, int batch, void* k_ring,
+                                void* v_ring, int ring_cap, uint8_t* modality, int64_t t_cap, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(sh.hkv), static_cast<unsigned>(batch));
+  if (f32)
+    stream_append_kernel<float><<<grid, sh.d, 0, st>>>(static_cast<const float*>(k_new), static_cast<const float*>(v_new),
+                                                       tags_new, lens, sh.hkv, sh.d, static_cast<float*>(k_ring),
+                                                       static_cast<float*>(v_ring), ring_cap, modality, t_cap);
   else
-    decode_combine_kernel<64><<<grid, kCombineThreads, 0, st>>>(ca);
+    stream_append_kernel<uint16_t><<<grid, sh.d, 0, st>>>(
+        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), tags_new, lens, sh.hkv, sh.d,
+        static_cast<uint16_t*>(k_ring), static_cast<uint16_t*>(v_ring), ring_cap, modality, t_cap);
   return hipGetLastError();
 }
 

@@ -30,6 +30,17 @@ struct DeviceTables {
   float rot_col_norm = 1.0f;
 };
 
+// Streaming schedule ([paper] §3.1 Implementation details, captioning): after n
+// streamed tokens, keys are quantized for the first 128 floor(n / 128) tokens (every
+// 128 tokens, in 32-token groups); values stay in a sliding window of the 128 most
+// recent tokens and are quantized per 32-token window once all of it has left.
+__host__ __device__ inline int64_t stream_key_packed(int64_t n) { return (n / 128) * 128; }
+__host__ __device__ inline int64_t stream_value_packed(int64_t n) {
+  return (n > 128 ? (n - 128) / kWindow : 0) * kWindow;
+}
+constexpr int kStreamRecent = 128;  // tokens of the sliding value window
+constexpr int kMaxRingCap = 512;    // largest ring of recent tokens
+
 struct Shape {
   int d, hq, hkv, group, kbits, vbits, modalities;
 };
@@ -54,14 +65,42 @@ struct DecodePlan {
 
 DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested_splits);
 
+// stream = true: each sequence's seq_lens value is a streamed length n, and only its
+// value-packed prefix (tokens below stream_value_packed(n)) is attended here.
 hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
                                  const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
                                  const uint32_t* k_codes, const uint16_t* k_min, const uint16_t* k_scale,
                                  const uint32_t* v_codes, const uint16_t* v_scale, const uint8_t* modality,
-                                 int64_t t_cap, float softmax_scale, void* workspace, hipStream_t stream);
+                                 int64_t t_cap, float softmax_scale, void* workspace, bool stream,
+                                 hipStream_t stream_handle);
+
+// The recent (unquantized) tokens of streamed sequences, attended inside the combine:
+// keys of tokens [stream_key_packed(n), n) and values of [stream_value_packed(n), n) come
+// from the rings (token t at row t % ring_cap); older keys of the recent span come from
+// the packed cache.
+struct StreamTail {
+  const float* q = nullptr;          // [B][Hq][d]
+  const int32_t* seq_lens = nullptr; // [B] streamed lengths
+  int64_t max_len = 0;
+  const uint32_t* k_codes = nullptr;
+  const uint16_t* k_min = nullptr;
+  const uint16_t* k_scale = nullptr;
+  int64_t t_cap = 0;
+  const void* k_ring = nullptr;      // [B][ring_cap][Hkv][d], bf16 or fp32
+  const void* v_ring = nullptr;
+  bool ring_f32 = false;
+  int ring_cap = 0;
+  float scale_log2 = 0.0f;           // softmax scale * log2(e)
+};
 
 hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
                                  const int32_t* seq_lens, int batch, const void* workspace, float* out,
-                                 hipStream_t stream);
+                                 const StreamTail* tail, hipStream_t stream);
+
+// Appends one token per sequence to the rings (row lens[b] % ring_cap) and writes its
+// modality tag at modality[b][lens[b]]; lens (device) are the lengths before the append.
+hipError_t launch_stream_append(const Shape& sh, const void* k_new, const void* v_new, bool f32,
+                                const uint8_t* tags_new, const int32_t* lens, int batch, void* k_ring,
+                                void* v_ring, int ring_cap, uint8_t* modality, int64_t t_cap, hipStream_t stream);
 
 }  // namespace omnikv

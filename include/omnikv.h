@@ -216,6 +216,59 @@ omnikv_status omnikv_decode_combine(const omnikv_ctx* ctx, const int32_t* seq_le
                                     int64_t max_len, int32_t num_splits, const void* workspace,
                                     size_t workspace_bytes, float* out, hipStream_t stream);
 
+/* ---- Streaming generation ([paper] §3.1 Implementation details, captioning:
+ * keys are quantized every 128 tokens in groups of 32; values keep a 128-token
+ * sliding FP16 window before quantization).
+ *
+ * A streamed sequence of n tokens is held as the packed cache above plus two
+ * rings of recent tokens, k_ring and v_ring [B][ring_cap][Hkv][d] (device, caller-
+ * allocated, dtype F32 or BF16, token t at row t % ring_cap, stored as given):
+ *   keys   of tokens [0, kp) are packed, kp = 128 * floor(n / 128);
+ *   values of tokens [0, vp) are packed, vp = 32 * floor(max(0, n - 128) / 32)
+ *   (a value window is quantized once all of its 32 tokens have left the
+ *   128-token window; reading: the pages do not say how the sliding window meets
+ *   the 32-token packing).  Always vp <= kp <= n and n - vp < 160.
+ * ring_cap must be a multiple of 128 in [256, 512]. */
+
+/* kp and vp for a stream of n >= 0 tokens (host arithmetic, no device work). */
+omnikv_status omnikv_stream_packed_lengths(int64_t n, int64_t* key_packed, int64_t* value_packed);
+
+/* Appends one token to every sequence of the batch: k_new, v_new (device,
+ * [B][Hkv][d] of dtype dt) go to ring row lens[b] % ring_cap, tags_new[b]
+ * (device, uint8 [B]) to modality[b][lens[b]].  lens (device int32 [B]) and
+ * lens_host (host int64 [B]) both give each sequence's length before the append
+ * and must agree; lens_host[b] + 1 <= t_cap.  tags_new and lens need no
+ * alignment (the other device pointers do, as everywhere).  Every key group and value window
+ * that the new length moves past the schedule's thresholds is then quantized
+ * from the rings into the packed cache (omnikv_quantize_keys / _values on that
+ * sequence's rows), all on `stream`.  The caller advances its lengths by one
+ * afterwards.  Errors as for omnikv_quantize_keys; nothing is launched on an
+ * argument error. */
+omnikv_status omnikv_stream_append(const omnikv_ctx* ctx, const void* k_new, const void* v_new, omnikv_dtype dt,
+                                   const uint8_t* tags_new, const int32_t* lens, const int64_t* lens_host,
+                                   int32_t batch, void* k_ring, void* v_ring, int32_t ring_cap, uint32_t* k_codes,
+                                   uint16_t* k_min, uint16_t* k_scale, uint32_t* v_codes, uint16_t* v_scale,
+                                   uint8_t* modality, int64_t t_cap, hipStream_t stream);
+
+/* Decode attention of streamed sequences: as omnikv_decode_attention over all n =
+ * seq_lens[b] tokens, where token t attends with its packed key when t < kp and
+ * with its ring key otherwise, and with its packed value when t < vp and its ring
+ * value otherwise (ring tokens are not quantized; their values enter in the
+ * original space).  The packed prefix [0, vp) runs through the split-KV pass;
+ * the recent tokens [vp, n) are attended in the combine.  Arguments as for
+ * omnikv_decode_attention, plus the rings (ring_dtype F32 or BF16, ring_cap as
+ * above, each sequence's recent tokens present in its ring); the workspace size
+ * is the one omnikv_decode_workspace_size gives for (batch, max_len,
+ * num_splits). */
+omnikv_status omnikv_decode_attention_streaming(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens,
+                                                int32_t batch, int64_t max_len, const uint32_t* k_codes,
+                                                const uint16_t* k_min, const uint16_t* k_scale,
+                                                const uint32_t* v_codes, const uint16_t* v_scale,
+                                                const uint8_t* modality, int64_t t_cap, const void* k_ring,
+                                                const void* v_ring, omnikv_dtype ring_dtype, int32_t ring_cap,
+                                                float softmax_scale, int32_t num_splits, void* workspace,
+                                                size_t workspace_bytes, float* out, hipStream_t stream);
+
 /* Thread-local text describing the last non-OK status of this thread. */
 const char* omnikv_last_error(void);
 

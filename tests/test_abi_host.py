@@ -95,3 +95,23 @@ def test_null_context_and_null_out():
     assert L.omnikv_decode_workspace_size(None, 1, 32, 0, ctypes.byref(sz)) == binding.EINVAL
     assert L.omnikv_create(None, None, None, None, None) == binding.EINVAL
     assert L.omnikv_destroy(None) == binding.OK
+
+
+def test_stream_schedule_host_function_matches_the_oracle():
+    """omnikv_stream_packed_lengths (host arithmetic) against the oracle's schedule."""
+    from oracle import omnikv_oracle as O
+    for n in range(0, 2000, 7):
+        assert binding.Context.stream_packed_lengths(n) == O.stream_packed_lengths(n), n
+    L = binding.load()
+    kp, vp = ctypes.c_int64(), ctypes.c_int64()
+    assert L.omnikv_stream_packed_lengths(-1, ctypes.byref(kp), ctypes.byref(vp)) == binding.EINVAL
+
+
+def test_streaming_calls_reject_a_null_context():
+    L = binding.load()
+    z = None
+    st = L.omnikv_stream_append(z, z, z, binding.BF16, z, z, z, 1, z, z, 256, z, z, z, z, z, z, 32, z)
+    assert st == binding.EINVAL
+    st = L.omnikv_decode_attention_streaming(z, z, z, 1, 32, z, z, z, z, z, z, 32, z, z, binding.BF16, 256,
+                                             0.0, 0, z, 0, z, z)
+    assert st == binding.EINVAL
