@@ -24,6 +24,11 @@ Source pages (cited by title and section):
 * Decode: attention over the dequantized cache.  The pages' fused kernel
   reorders this computation ([paper] §1, Fig. 1(d)); the oracle computes the
   plain definition, softmax(scale * q . k_hat) . v_hat, in float64.
+* Value-rotation calibration ([paper] §2.3: a basis U_m calibrated for each
+  modality; [digest] 方法概览: an attention-contribution-weighted covariance,
+  eigendecomposed).  Reading: the weighted second moment, its eigenvectors in
+  descending order composed with the normalized Hadamard ("modality-aware
+  correction of the Hadamard rotation", [paper] §2.3).
 * Streaming generation ([paper] §3.1 Implementation details, captioning):
   keys are quantized every 128 tokens in groups of 32; values stay in a
   128-token sliding FP16 window before quantization.  Recent tokens enter the
@@ -459,3 +464,37 @@ def decode_attention_streaming(q, seq_lens, cache: dict, k_recent, v_recent, sig
         for h in heads:
             out[b, h] = attention_f64(q[b, h], keys, vals, scale)
     return out
+
+
+# ----------------------------------------------------------------------------- calibration
+def calibrate_value_rotation(values: np.ndarray, weights: Optional[np.ndarray] = None) -> np.ndarray:
+    """U_m for one modality from its calibration values, float64 [d][d].
+
+    C = sum_t w_t v_t v_t^T / sum_t w_t (w_t = 1 when no weights are given; the pages
+    weight by attention contribution); E = eigenvectors of C as columns, eigenvalues
+    descending, each column's largest-magnitude entry (the first such) made positive;
+    U = E H_d / sqrt(d).  Then v' = U^T v decorrelates v and spreads the result over
+    the channels like the Hadamard rotation.
+    """
+    v = np.asarray(values, np.float64)
+    n, d = v.shape
+    w = np.ones(n) if weights is None else np.asarray(weights, np.float64)
+    C = (v * w[:, None]).T @ v / w.sum()
+    lam, E = np.linalg.eigh(C)
+    E = E[:, np.argsort(-lam, kind="stable")]
+    lead = np.argmax(np.abs(E), axis=0)
+    E = E * np.sign(E[lead, np.arange(d)])[None, :]
+    return E @ sylvester(d) / math.sqrt(d)
+
+
+def value_codec_mse(v: np.ndarray, U: np.ndarray, bits: int = 2) -> float:
+    """Mean squared error of the value codec (rotation U, per-token scale, fixed
+    codebook) on values v [n][d], relative to the mean squared value."""
+    v = np.asarray(v, F32)
+    n, d = v.shape
+    Us = np.asarray(U, F32)[None]
+    tags = np.zeros((1, n), np.uint8)
+    lv = value_codebook_f16(bits)
+    vc, vs = quantize_values(v[None, :, None, :], tags, Us, lv, bits)
+    vh = dequantize_values(vc, vs, tags, Us, lv, bits)[0, 0]
+    return float(np.mean((vh - v) ** 2) / np.mean(np.asarray(v, np.float64) ** 2))

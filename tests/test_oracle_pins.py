@@ -466,3 +466,44 @@ def test_streaming_attention_special_cases():
         assert np.allclose(out[0, h], O.attention_f64(q[0, h], keys, vals, 1.0 / math.sqrt(d)), rtol=1e-12, atol=1e-14)
     full = O.decode_attention(q, [n], cache, signs, U, lv)
     assert not np.allclose(out, full)  # the unquantized tokens matter
+
+
+# ----------------------------------------------------------------------------- value-rotation calibration
+def test_calibration_closed_form_diagonal_moment():
+    """A diagonal second moment with distinct entries: its eigenvectors are the unit
+    vectors in descending order, so U = P H / sqrt(d) with P that permutation."""
+    d = 64
+    c = np.random.default_rng(2).permutation(np.arange(1, d + 1, dtype=np.float64))
+    v = np.diag(np.sqrt(c * d))                      # one token per channel
+    U = O.calibrate_value_rotation(v)
+    P = np.zeros((d, d))
+    P[np.argsort(-c), np.arange(d)] = 1.0
+    assert np.allclose(U, P @ O.sylvester(d) / 8.0, atol=1e-12)
+    assert np.allclose(U.T @ U, np.eye(d), atol=1e-12)
+
+
+def test_calibration_weights_count_like_repeated_tokens():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((400, 64)) * np.linspace(3, 0.1, 64)   # full rank, distinct eigenvalues
+    w = rng.integers(1, 4, 400)
+    assert np.allclose(O.calibrate_value_rotation(v, w.astype(float)),
+                       O.calibrate_value_rotation(np.repeat(v, w, axis=0)), atol=1e-10)
+
+
+@pytest.mark.parametrize("d,heavy", [(64, False), (64, True), (128, False), (128, True)])
+def test_matched_rotation_beats_shared_and_transferred(d, heavy):
+    """On per-modality clusters, each modality's calibrated rotation quantizes its
+    held-out values with lower error than one randomized Hadamard shared by all
+    modalities and than the other modalities' rotations ([paper] §1 and §2.3:
+    heterogeneous value geometry)."""
+    cal, held = synth.modality_clusters(d, 0, n=2048, heavy_tail=heavy)
+    held = [h[:1024] for h in held]
+    Us = [O.calibrate_value_rotation(c) for c in cal]
+    signs = synth.rademacher_signs(d, 0).astype(np.float64)
+    shared = (O.sylvester(d) * signs[None, :]).T / math.sqrt(d)   # U with U^T v = H D v / sqrt(d)
+    for m in range(3):
+        matched = O.value_codec_mse(held[m], Us[m])
+        assert matched < O.value_codec_mse(held[m], shared), (d, heavy, m)
+        for o in range(3):
+            if o != m:
+                assert matched < O.value_codec_mse(held[m], Us[o]), (d, heavy, m, o)
