@@ -23,8 +23,24 @@ EXPORTED = (
     "omnikv_create", "omnikv_destroy", "omnikv_value_codebook", "omnikv_quantize_keys",
     "omnikv_quantize_values", "omnikv_decode_workspace_size", "omnikv_decode_attention",
     "omnikv_decode_partial", "omnikv_decode_combine", "omnikv_stream_packed_lengths", "omnikv_stream_append",
-    "omnikv_decode_attention_streaming", "omnikv_last_error",
+    "omnikv_decode_attention_streaming", "omnikv_calibrate_value_rotation", "omnikv_last_error",
 )
+
+
+def calibrate_value_rotation(values, weights=None, stream=None) -> np.ndarray:
+    """U_m (fp32 numpy [d][d]) from one modality's calibration values: a contiguous device
+    tensor [n][d] (fp32 or bf16) and optional fp32 weights [n]."""
+    import torch
+    if values.dtype not in (torch.float32, torch.bfloat16) or not values.is_contiguous() or values.dim() != 2:
+        raise ValueError("values must be a contiguous fp32 or bf16 tensor [n][d]")
+    if weights is not None and (weights.dtype != torch.float32 or not weights.is_contiguous()):
+        raise ValueError("weights must be a contiguous fp32 tensor [n]")
+    n, d = int(values.shape[0]), int(values.shape[1])
+    out = np.zeros((d, d), np.float32)
+    dt = BF16 if values.dtype == torch.bfloat16 else F32
+    _check(load().omnikv_calibrate_value_rotation(_ptr(values), dt, _ptr(weights), n, d, out.ctypes.data,
+                                                  _stream(stream)))
+    return out
 
 
 class OmniKVError(RuntimeError):
@@ -64,6 +80,7 @@ def load() -> ctypes.CDLL:
     L.omnikv_stream_packed_lengths.argtypes = [i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.omnikv_stream_append.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i32, vp, vp, i32,
                                        vp, vp, vp, vp, vp, vp, i64, vp]
+    L.omnikv_calibrate_value_rotation.argtypes = [vp, ctypes.c_int, vp, i64, i32, vp, vp]
     L.omnikv_decode_attention_streaming.argtypes = [vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, i64,
                                                     vp, vp, ctypes.c_int, i32, ctypes.c_float, i32, vp, sz,
                                                     vp, vp]

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libomnikv.so")
 
-SOURCES = ["api.hip", "quantize_keys.hip", "quantize_values.hip", "decode.hip"]
+SOURCES = ["api.hip", "quantize_keys.hip", "quantize_values.hip", "decode.hip", "calibrate.hip"]
 
 # The decode kernel keeps its matrix-core accumulators in ordinary VGPRs: with the
 # accumulation-register form the compiler shuttles all of them between register files

@@ -501,6 +501,18 @@ omnikv_status omnikv_decode_attention_streaming(const omnikv_ctx* ctx, const flo
   return OMNIKV_OK;
 }
 
+omnikv_status omnikv_calibrate_value_rotation(const void* values, omnikv_dtype dt, const float* weights, int64_t n,
+                                              int32_t head_dim, float* u_out, hipStream_t stream) {
+  if (head_dim != 64 && head_dim != 128) return fail(OMNIKV_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (dt != OMNIKV_F32 && dt != OMNIKV_BF16) return fail(OMNIKV_EINVAL, "calibrate: dtype must be F32 or BF16");
+  if (n <= 0) return fail(OMNIKV_EINVAL, "calibrate: n must be positive (got %lld)", (long long)n);
+  if (!values || !u_out) return fail(OMNIKV_EINVAL, "calibrate: NULL pointer");
+  if (!aligned16(values)) return fail(OMNIKV_EINVAL, "calibrate: values must be 16-byte aligned");
+  const std::string err = omnikv::calibrate_value_rotation(values, dt == OMNIKV_BF16, weights, n, head_dim, u_out, stream);
+  if (!err.empty()) return fail(OMNIKV_EHIP, "calibrate: %s", err.c_str());
+  return OMNIKV_OK;
+}
+
 const char* omnikv_last_error(void) { return g_error.c_str(); }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 #include "omnikv.h"
 
 namespace omnikv {
@@ -102,5 +104,11 @@ hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const 
 hipError_t launch_stream_append(const Shape& sh, const void* k_new, const void* v_new, bool f32,
                                 const uint8_t* tags_new, const int32_t* lens, int batch, void* k_ring,
                                 void* v_ring, int ring_cap, uint8_t* modality, int64_t t_cap, hipStream_t stream);
+
+// U_m from calibration values [n][d] (fp32 or bf16, device) and optional weights [n]
+// (device); writes u_out (host, [d][d] row-major) and returns "" or an error text.
+// Offline: allocates scratch and synchronizes `stream`.
+std::string calibrate_value_rotation(const void* values, bool bf16, const float* weights, int64_t n, int d,
+                                     float* u_out, hipStream_t stream);
 
 }  // namespace omnikv

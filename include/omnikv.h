@@ -269,6 +269,22 @@ omnikv_status omnikv_decode_attention_streaming(const omnikv_ctx* ctx, const flo
                                                 float softmax_scale, int32_t num_splits, void* workspace,
                                                 size_t workspace_bytes, float* out, hipStream_t stream);
 
+/* ---- Calibration of a modality's value basis U_m ([paper] §2.3 "Modality-aware
+ * value rotation"; [digest] 方法概览: an attention-contribution-weighted covariance,
+ * eigendecomposed).  From one modality's calibration values v_t (device, [n][d] of
+ * dtype dt, 16-byte aligned) and optional weights w_t (device fp32 [n], e.g. each
+ * token's mean attention probability; NULL = 1):
+ *   C = sum_t w_t v_t v_t^T / sum_t w_t, accumulated in float64 on the GPU;
+ *   E = its eigenvectors (cyclic Jacobi, float64, host), columns in descending
+ *       eigenvalue order, each column's first largest-magnitude entry positive;
+ *   U_m = E H_d / sqrt(d), H_d the Sylvester Hadamard matrix (reading of the pages'
+ *       "modality-aware correction of the Hadamard rotation"),
+ * written to u_out (host, fp32 [d][d] row-major) in the layout omnikv_create takes.
+ * Offline: it allocates scratch device memory and synchronizes `stream` before it
+ * returns.  OMNIKV_EHIP if the weights sum to zero or a HIP call fails. */
+omnikv_status omnikv_calibrate_value_rotation(const void* values, omnikv_dtype dt, const float* weights, int64_t n,
+                                              int32_t head_dim, float* u_out, hipStream_t stream);
+
 /* Thread-local text describing the last non-OK status of this thread. */
 const char* omnikv_last_error(void);
 

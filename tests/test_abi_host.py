@@ -115,3 +115,12 @@ def test_streaming_calls_reject_a_null_context():
     st = L.omnikv_decode_attention_streaming(z, z, z, 1, 32, z, z, z, z, z, z, 32, z, z, binding.BF16, 256,
                                              0.0, 0, z, 0, z, z)
     assert st == binding.EINVAL
+
+
+def test_calibration_rejects_bad_arguments():
+    L = binding.load()
+    out = np.zeros((128, 128), np.float32)
+    assert L.omnikv_calibrate_value_rotation(None, binding.F32, None, 16, 96, out.ctypes.data, None) == binding.EUNSUPPORTED
+    assert L.omnikv_calibrate_value_rotation(None, binding.F32, None, 0, 128, out.ctypes.data, None) == binding.EINVAL
+    assert L.omnikv_calibrate_value_rotation(None, binding.F32, None, 16, 128, out.ctypes.data, None) == binding.EINVAL
+    assert L.omnikv_calibrate_value_rotation(None, 7, None, 16, 128, out.ctypes.data, None) == binding.EINVAL
