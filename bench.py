@@ -237,11 +237,21 @@ def main():
                      args.steps)
     g_comb = capture(lambda i: ctx.decode_combine(lens, cfg.batch, T, ws, out, num_splits=args.splits),
                      args.steps)
+    # the same step for streamed sequences: the last stream_value_packed tokens (the
+    # 128-token sliding value window) come from rings of recent tokens
+    rings = ctx.alloc_rings(cfg.batch, 256)
+    rings["k"].normal_()
+    rings["v"].normal_()
+    g_stream = capture(lambda i: ctx.decode_streaming(q, lens, T, caches[i % nbuf], rings, out=out, workspace=ws,
+                                                      num_splits=args.splits), args.steps)
     g_step.replay()  # untimed first replay
+    g_stream.replay()
     torch.cuda.synchronize()
     step_ms, wall = timed_replay(g_step)
     part_ms, _ = timed_replay(g_part)
     comb_ms, _ = timed_replay(g_comb)
+    stream_ms, _ = timed_replay(g_stream)
+    kp, vp = binding.Context.stream_packed_lengths(T)
     ms_per_step = step_ms / args.steps
     us_step_med = ms_per_step * 1e3
     part_avg_s = part_ms / args.steps / 1e3
@@ -276,6 +286,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(f"{cfg.name} K{args.kbits}V{args.vbits} splits {args.splits}")},
         "write_path": write_path,
+        "streaming": {"us_per_step": round(stream_ms / args.steps * 1e3, 2),
+                      "recent_tokens_per_sequence": T - vp, "packed_key_tokens": kp},
     }
     if args.copy_reference_mib:
         n = args.copy_reference_mib * (1 << 20) // 4

@@ -830,26 +830,6 @@ struct CombineArgs {
   StreamTail tail;
 };
 
-// Key code of window token t, rotated channel c, in a key window block (the layout of
-// the quantizer's pack, described with the public cache layout).
-template <int D>
-__device__ inline uint32_t key_code_at(const uint32_t* blk, int kbits, int t, int c) {
-  const int tau = t >> 4, rho = t & 15;
-  const int g = c / (D / 4), r = c % (D / 4);
-  const int s = r >> 3, j = r & 7, i = j >> 1, e = j & 1;
-  const int per_lane = D * kbits / 64;
-  int lw, slot;
-  if (D == 128) {
-    if (kbits == 2) { lw = i; slot = 4 * tau + s; }
-    else { lw = 4 * tau + i; slot = s; }
-  } else {
-    if (kbits == 2) { lw = i & 1; slot = 4 * (i >> 1) + 2 * tau + s; }
-    else { lw = i; slot = 2 * tau + s; }
-  }
-  const uint32_t word = blk[(16 * g + rho) * per_lane + lw];
-  return (word >> (16 * e + kbits * slot)) & ((1u << kbits) - 1u);
-}
-
 __device__ inline float ring_elem(const void* ring, size_t idx, bool f32) {
   if (f32) return static_cast<const float*>(ring)[idx];
   return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(ring)[idx]) << 16);
@@ -869,7 +849,7 @@ constexpr int kMaxSplits = 1024;  // splits per (sequence, KV head)
 
 constexpr int kMaxRing = kMaxRingCap;
 
-template <int D, bool STREAM>
+template <int D, int KB, bool STREAM>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a) {
   constexpr int J = kMaxModalities * D;       // stacked rotation rows (m, k)
   constexpr int KQ = kCombineThreads / D;     // row groups
@@ -887,25 +867,29 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   const int c = tid % D, kq = tid / D;
   const int jrows = a.modalities * D;
 
-  // ---- loads that depend on nothing
+  // ---- loads that depend on nothing (for streamed sequences they follow the recent
+  // tokens' scores, whose registers they would otherwise crowd)
   const int j0 = kq * JPG;
   const float* up = a.rotations_t + static_cast<size_t>(j0) * D + c;
-  float u[JPG];
-#pragma unroll
-  for (int i = 0; i < JPG; ++i) u[i] = (j0 + i < jrows) ? up[static_cast<size_t>(i) * D] : 0.0f;
   const bool merger = tid < jrows;  // item (m, k) = (tid / D, tid % D)
   const int im = tid / D;
   const float* src = a.ws_acc + base * PSTRIDE + (im * kMaxGroup + h) * D + c;
+  float u[JPG];
   float x[kCombineXB];
-#pragma unroll
-  for (int t = 0; t < kCombineXB; ++t) x[t] = (merger && t < S) ? src[static_cast<size_t>(t) * PSTRIDE] : 0.0f;
   // lane t: split t's (max, sum) and modality mask (splits 64.. are read in the loop)
   float2 ml0 = make_float2(-INFINITY, 0.0f);
   uint32_t mk0 = 0u;
-  if (lane < S) {
-    ml0 = a.ws_ml[(base + lane) * kMaxGroup + h];
-    mk0 = a.ws_mask[base + lane];
-  }
+  auto issue_loads = [&]() {
+#pragma unroll
+    for (int i = 0; i < JPG; ++i) u[i] = (j0 + i < jrows) ? up[static_cast<size_t>(i) * D] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < kCombineXB; ++t) x[t] = (merger && t < S) ? src[static_cast<size_t>(t) * PSTRIDE] : 0.0f;
+    if (lane < S) {
+      ml0 = a.ws_ml[(base + lane) * kMaxGroup + h];
+      mk0 = a.ws_mask[base + lane];
+    }
+  };
+  if constexpr (!STREAM) issue_loads();
 
   // ---- streamed sequences: scores of the recent tokens [T0, len) in log2 units.  A
   // token below the key-packed length uses its packed key with the rotated query (the
@@ -939,8 +923,14 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
         __syncthreads();
       }
     }
-    constexpr int CPT = D / 8;  // eight threads per token
-    const int sub = tid & 7;
+    // Eight threads per token, CPT consecutive channels each; all of a thread's channels
+    // lie in one channel group g of the key window block, whose lane words (16 g + rho)
+    // hold their codes (the block layout of the cache description).
+    constexpr int CPT = D / 8;
+    constexpr int PER_LANE = D * KB / 64;                  // words per block lane
+    constexpr int NW = (D == 128 && KB == 4) ? 4 : PER_LANE;  // words of one token half
+    const int sub = tid & 7, c0 = sub * CPT;
+    const int g = c0 / (D / 4), sh2 = (c0 % (D / 4)) / 8;  // group, first 8-channel step
     for (int j0 = 0; j0 < nt; j0 += kCombineThreads / 8) {
       const int j = j0 + (tid >> 3);
       float acc = 0.0f;
@@ -948,18 +938,56 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
         const int t = T0 + j;
         if (t < Pk) {
           const size_t wb = static_cast<size_t>(unit) * (st.t_cap / kWindow) + t / kWindow;
-          const uint32_t* blk = st.k_codes + wb * (D * a.kbits);
-          const uint16_t* mrow = st.k_min + wb * D;
-          const uint16_t* srow = st.k_scale + wb * D;
+          const int tt = t % kWindow, tau = tt >> 4, rho = tt & 15;
+          const uint32_t* wp = st.k_codes + wb * (D * KB) + (16 * g + rho) * PER_LANE + ((D == 128 && KB == 4) ? 4 * tau : 0);
+          uint32_t w[NW];
+#pragma unroll
+          for (int x = 0; x < NW; ++x) w[x] = wp[x];
+          uint16_t mv[CPT], sv[CPT];
+#pragma unroll
+          for (int x = 0; x < CPT; x += 8) {
+            const uint4 m8 = *reinterpret_cast<const uint4*>(st.k_min + wb * D + c0 + x);
+            const uint4 s8 = *reinterpret_cast<const uint4*>(st.k_scale + wb * D + c0 + x);
+            const uint32_t mw[4] = {m8.x, m8.y, m8.z, m8.w}, sw[4] = {s8.x, s8.y, s8.z, s8.w};
+#pragma unroll
+            for (int y = 0; y < 8; ++y) {
+              mv[x + y] = static_cast<uint16_t>(mw[y >> 1] >> (16 * (y & 1)));
+              sv[x + y] = static_cast<uint16_t>(sw[y >> 1] >> (16 * (y & 1)));
+            }
+          }
+#pragma unroll
           for (int cc = 0; cc < CPT; ++cc) {
-            const int c2 = sub * CPT + cc;
-            const float code = static_cast<float>(key_code_at<D>(blk, a.kbits, t % kWindow, c2));
-            acc = fmaf(qr[c2], f16_to_float(mrow[c2]) + f16_to_float(srow[c2]) * code, acc);
+            const int jj = cc & 7, i = jj >> 1, e = jj & 1, s8 = sh2 + (cc >> 3);
+            uint32_t word, bit;
+            if (D == 128 && KB == 2) { word = w[i]; bit = 16 * e + 2 * (4 * tau + s8); }
+            else if (D == 128) { word = w[i]; bit = 16 * e + 4 * s8; }
+            else if (KB == 2) { word = w[i & 1]; bit = 16 * e + 2 * (4 * (i >> 1) + 2 * tau + s8); }
+            else { word = w[i]; bit = 16 * e + 4 * (2 * tau + s8); }
+            const float code = static_cast<float>((word >> bit) & ((1u << KB) - 1u));
+            acc = fmaf(qr[c0 + cc], f16_to_float(mv[cc]) + f16_to_float(sv[cc]) * code, acc);
           }
           acc *= RhtConst<D>::value;
         } else {
-          const size_t row = ((static_cast<size_t>(b) * st.ring_cap + t % st.ring_cap) * a.hkv + kvh) * D + sub * CPT;
-          for (int cc = 0; cc < CPT; ++cc) acc = fmaf(qo[sub * CPT + cc], ring_elem(st.k_ring, row + cc, st.ring_f32), acc);
+          const size_t row = ((static_cast<size_t>(b) * st.ring_cap + t % st.ring_cap) * a.hkv + kvh) * D + c0;
+          if (st.ring_f32) {
+#pragma unroll
+            for (int x = 0; x < CPT; x += 4) {
+              const float4 k4 = *reinterpret_cast<const float4*>(static_cast<const float*>(st.k_ring) + row + x);
+              acc = fmaf(qo[c0 + x], k4.x, acc);
+              acc = fmaf(qo[c0 + x + 1], k4.y, acc);
+              acc = fmaf(qo[c0 + x + 2], k4.z, acc);
+              acc = fmaf(qo[c0 + x + 3], k4.w, acc);
+            }
+          } else {
+#pragma unroll
+            for (int x = 0; x < CPT; x += 8) {
+              const uint4 k8 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(st.k_ring) + row + x);
+              const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
+#pragma unroll
+              for (int y = 0; y < 8; ++y)
+                acc = fmaf(qo[c0 + x + y], __uint_as_float((y & 1) ? (kw[y >> 1] & 0xFFFF0000u) : (kw[y >> 1] << 16)), acc);
+            }
+          }
         }
       }
       acc += __shfl_xor(acc, 1, 64);
@@ -981,6 +1009,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
     }
     __syncthreads();
     tmx = tstat;
+    issue_loads();
   }
 
   // ---- largest split max (every wave alike)
@@ -1192,12 +1221,15 @@ hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const 
                  tb.signs, sh.kbits, tail ? *tail : StreamTail{}};
   (void)seq_lens;
   const dim3 grid(static_cast<unsigned>(sh.group), static_cast<unsigned>(batch * sh.hkv));
+  const bool k4 = sh.kbits == 4;
   if (sh.d == 128) {
-    if (tail) decode_combine_kernel<128, true><<<grid, kCombineThreads, 0, st>>>(ca);
-    else decode_combine_kernel<128, false><<<grid, kCombineThreads, 0, st>>>(ca);
+    if (!tail) decode_combine_kernel<128, 2, false><<<grid, kCombineThreads, 0, st>>>(ca);
+    else if (k4) decode_combine_kernel<128, 4, true><<<grid, kCombineThreads, 0, st>>>(ca);
+    else decode_combine_kernel<128, 2, true><<<grid, kCombineThreads, 0, st>>>(ca);
   } else {
-    if (tail) decode_combine_kernel<64, true><<<grid, kCombineThreads, 0, st>>>(ca);
-    else decode_combine_kernel<64, false><<<grid, kCombineThreads, 0, st>>>(ca);
+    if (!tail) decode_combine_kernel<64, 2, false><<<grid, kCombineThreads, 0, st>>>(ca);
+    else if (k4) decode_combine_kernel<64, 4, true><<<grid, kCombineThreads, 0, st>>>(ca);
+    else decode_combine_kernel<64, 2, true><<<grid, kCombineThreads, 0, st>>>(ca);
   }
   return hipGetLastError();
 }
