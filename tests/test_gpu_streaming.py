@@ -48,26 +48,28 @@ def _rings(ctx, cfg, k, v, lens, cap):
     return rings
 
 
-@pytest.mark.parametrize("cid,lens,cap", [
-    (1, [0, 1, 127, 128], 256),
-    (2, [300, 97, 515, 160], 256),
-    (2, [640, 383, 129], 512),
+@pytest.mark.parametrize("cid,lens,cap,kbits,vbits", [
+    (1, [0, 1, 127, 128], 256, 2, 2),
+    (1, [200, 257, 129], 256, 4, 4),
+    (2, [300, 97, 515, 160], 256, 2, 2),
+    (2, [640, 383, 129], 512, 2, 2),
+    (2, [400, 260], 256, 4, 2),
 ])
-def test_streaming_decode_parity(cid, lens, cap):
+def test_streaming_decode_parity(cid, lens, cap, kbits, vbits):
     """Packed prefix + recent tokens, cache quantized by the oracle (the same packed
     cache on both sides), recent tokens in rings that have wrapped."""
     import torch
     cfg = synth.CONFIGS[cid]
     B = len(lens)
     T = max(32, ((max(lens) + 31) // 32) * 32)
-    say(f"[stream-decode] cfg{cid} lens {lens} ring {cap}")
-    ctx, signs, U, lv = make_context(cfg)
+    say(f"[stream-decode] cfg{cid} K{kbits}V{vbits} lens {lens} ring {cap}")
+    ctx, signs, U, lv = make_context(cfg, kbits, vbits)
     tags, k, v = _tokens(cfg, T, 3)
     tags, k, v = tags[:1].repeat(B, 0), np.repeat(k[:1], B, 0), np.repeat(v[:1], B, 0)
-    kc, km, ks = O.quantize_keys(k, signs, cfg.key_bits)
-    vc, vs = O.quantize_values(v, tags, U, lv, cfg.value_bits)
+    kc, km, ks = O.quantize_keys(k, signs, kbits)
+    vc, vs = O.quantize_values(v, tags, U, lv, vbits)
     host = dict(k_codes=kc, k_min=km, k_scale=ks, v_codes=vc, v_scale=vs, modality=tags,
-                key_bits=cfg.key_bits, value_bits=cfg.value_bits)
+                key_bits=kbits, value_bits=vbits)
     cache = cache_to_device(host)
     rings = _rings(ctx, cfg, k, v, lens, cap)
     q_np = synth.queries(cfg, 4, B)
