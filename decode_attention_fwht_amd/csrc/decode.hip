@@ -170,7 +170,6 @@ struct PartialArgs {
   float2* ws_ml;     // [unit][split][8] (max, sum) in log2 units
   uint32_t* ws_mask; // [unit][split] modalities present
   float* ws_acc;     // [unit][split][M][8][D]
-  float* ws_stash;   // [unit][split][wave][2][8][D]
   int stream;        // 1: attend over the value-packed prefix of each stream (the rest is recent)
 };
 
@@ -359,55 +358,15 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     }
   }
 
-  // ---- visit order.  The wave's windows go in chunks of up to 64; within a chunk, one
-  // pass per modality present (the resident one first) over the windows holding it, in
-  // window order, two at a time.  The ring is filled along the same sequence of visits,
-  // across passes: visit i goes to slot i % RING once visit i - RING has been computed.
-  // The first chunk's first copies go out before the query set-up, which hides their
+  // ---- visit order: the wave's windows in order, each visited once whatever modalities
+  // it holds.  Visit i (window wbeg + i) goes to slot i % RING once visit i - RING has
+  // been computed; the first copies go out before the query set-up, which hides their
   // latency.
-  int cur = -1;  // resident modality (wave-uniform); -1 before the first visit
-  uint64_t ps0 = 0u, ps1 = 0u, ps2 = 0u;  // windows of passes 0, 1, 2 (bit = window of the chunk)
-  int pmod0 = 0;                          // modality of pass 0; passes k take (pmod0 + k) % 3
-  int total = 0, issued = 0, fk = 0, ck = 0, chunk0 = 0;
-  uint64_t fmask = 0u, cmask = 0u;
-  auto pass_mask = [&](int k) -> uint64_t { return k == 0 ? ps0 : (k == 1 ? ps1 : ps2); };
-  auto begin_chunk = [&](int c0) {
-    const int cn = min(64, nw - c0);
-    uint32_t bits = 0u;
-    if (lane < cn) {
-      const int tok0 = (wbeg + c0 + lane) * kWindow;
-      const uint4_t* tp = reinterpret_cast<const uint4_t*>(a.modality + static_cast<size_t>(b) * a.t_cap + tok0);
-      const uint4_t t01 = tp[0], t23 = tp[1];
-      const uint32_t tw[8] = {t01[0], t01[1], t01[2], t01[3], t23[0], t23[1], t23[2], t23[3]};
-#pragma unroll
-      for (int j = 0; j < kWindow; ++j) {
-        const uint32_t tg = (tw[j / 4] >> (8 * (j % 4))) & 0xFFu;
-        if (tok0 + j < len && tg < static_cast<uint32_t>(kMaxModalities)) bits |= 1u << tg;
-      }
-    }
-    const uint64_t pm0 = __ballot(bits & 1u), pm1 = __ballot((bits >> 1) & 1u), pm2 = __ballot((bits >> 2) & 1u);
-    total = __builtin_popcountll(pm0) + __builtin_popcountll(pm1) + __builtin_popcountll(pm2);
-    // pass order: the resident modality first, then the others
-    pmod0 = cur < 0 ? 0 : cur;
-    ps0 = pmod0 == 0 ? pm0 : (pmod0 == 1 ? pm1 : pm2);
-    ps1 = pmod0 == 0 ? pm1 : (pmod0 == 1 ? pm2 : pm0);
-    ps2 = pmod0 == 0 ? pm2 : (pmod0 == 1 ? pm0 : pm1);
-    chunk0 = c0;
-    issued = fk = ck = 0;
-    fmask = cmask = ps0;
-  };
+  int issued = 0;
   auto issue_upto = [&](int lim) {
-    for (; issued < lim; ++issued) {
-      while (fmask == 0u) fmask = pass_mask(++fk);
-      const int w = __builtin_ctzll(fmask);
-      fmask &= fmask - 1u;
-      issue(wbeg + chunk0 + w, issued % RING);
-    }
+    for (; issued < lim; ++issued) issue(wbeg + issued, issued % RING);
   };
-  if (nw > 0) {
-    begin_chunk(0);
-    issue_upto(min(total, RING - 1));
-  }
+  issue_upto(min(nw, RING - 1));
 
   for (int i = tid; i < (1 << (2 * VB)); i += kWaves * 64) vtab[i] = a.pair_table[i];
 
@@ -496,52 +455,20 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   __syncthreads();
 
   // ---- running state.  Scores, l_part and the accumulators are relative to m_ref (per
-  // column, log2 units).  One modality's accumulator is resident in registers; the
-  // others wait in this wave's two stash slots (workspace memory, touched only when the
-  // wave changes modality pass), each with the m_ref it was stored at.
+  // column, log2 units).  The value contraction's 16 columns are the 8 heads of two
+  // modalities: accumulator A holds audio (columns 0-7) and video (8-15), accumulator B
+  // text (0-7); the fp16 hi and lo parts of the probability operand enter as two
+  // contractions into the same columns.  A window is therefore visited once, whatever
+  // modalities it holds, and no accumulator ever leaves the registers.
   float m_ref = -INFINITY;
   float l_part = 0.0f;
-  float4_t acc[NU];
+  float4_t accA[NU], accB[NU];
 #pragma unroll
-  for (int u = 0; u < NU; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-  int occ0 = -1, occ1 = -1;       // modality held by stash slot 0 / 1 (wave-uniform)
-  float mst0 = 0.0f, mst1 = 0.0f; // m_ref at which slot 0 / 1 was stored (per column)
-  float* const my_stash =
-      a.ws_stash + ((static_cast<size_t>(unit) * a.splits + blockIdx.x) * kWaves + wave) * (2 * kMaxGroup * D);
-  const uint32_t lo_mask = part ? 0xFFFFFFFFu : 0u;
-
-  // Lane (n, g) of tile u holds channels 16u + 4g .. +3 of column n; a stash slot keeps
-  // the hi + lo sum, and a restored tile goes back into the hi columns.
-  auto make_resident = [&](int t) {
-    if (cur < 0) {
-      cur = t;
-      return;
-    }
-    const int x = (occ0 == t) ? 0 : (occ1 == t) ? 1 : (occ0 < 0 ? 0 : 1);
-    const bool restore = (x == 0 ? occ0 : occ1) == t;
-    const float f = restore ? exp2f((x == 0 ? mst0 : mst1) - m_ref) : 0.0f;  // <= 1
-    float* sp = my_stash + (x * kMaxGroup + h) * D + 4 * g;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      float4_t v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[u][i] + row_ror8(acc[u][i]);
-      float4_t* tp = reinterpret_cast<float4_t*>(sp + 16 * u);
-      float4_t old = float4_t{0.f, 0.f, 0.f, 0.f};
-      if (restore) old = *tp;
-      if (part == 0) *tp = v;
-      const float fp = part == 0 ? f : 0.0f;
-      acc[u] = float4_t{old[0] * fp, old[1] * fp, old[2] * fp, old[3] * fp};
-    }
-    if (x == 0) {
-      occ0 = cur;
-      mst0 = m_ref;
-    } else {
-      occ1 = cur;
-      mst1 = m_ref;
-    }
-    cur = t;
-  };
+  for (int u = 0; u < NU; ++u) accA[u] = accB[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t seen = 0u;  // modalities met (wave-uniform)
+  // this lane's column modality in A and in B (kMaxModalities: none)
+  const uint32_t modA = part ? 2u : 1u;
+  const uint32_t modB = part ? static_cast<uint32_t>(kMaxModalities) : 0u;
 
   // ---- score contractions of the window in `slot` (modality-independent): the k_min
   // term cm (every A row is m_w, so each lane's results all equal q^ . m_w) and
@@ -589,21 +516,21 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     }
   };
 
-  // ---- the rest of one visit of a window for modality m, given its score contractions.
-  // Only tokens of modality m (and inside the sequence) count: a window holding several
-  // modalities is visited once per modality.  `overlap` runs inside the last basic block
-  // (after the rare branches), a place for independent work to interleave with it.
-  auto visit = [&](const uint8_t* slot, int tokb, int m, const float4_t (&cs)[2], const float4_t& cm,
-                   auto&& overlap) {
+  // ---- the rest of one visit of a window, given its score contractions.  Tokens count
+  // when they lie inside the sequence and carry a modality tag below 3.
+  auto visit = [&](const uint8_t* slot, int tokb, const float4_t (&cs)[2], const float4_t& cm) {
     const uint32_t tg0 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 4 * g);
     const uint32_t tg1 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 16 + 4 * g);
     // value scales of this lane's tokens, fp16 pairs (tokens 4g.., then 16 + 4g..)
     const uint2 sig0 = *reinterpret_cast<const uint2*>(slot + SG::OFF_SIG + 2 * (4 * g));
     const uint2 sig1 = *reinterpret_cast<const uint2*>(slot + SG::OFF_SIG + 2 * (16 + 4 * g));
     uint32_t sgw[4] = {sig0.x, sig0.y, sig1.x, sig1.y};
-    // ---- which tokens count: all of them unless the window is partial or mixed
-    const uint32_t rep = static_cast<uint32_t>(m) * 0x01010101u;
-    const bool all_count = (tokb + kWindow <= len) && __all((tg0 == rep) && (tg1 == rep));
+    // ---- the common case: one modality over a whole window inside the sequence.  Lane 0
+    // holds tokens 0 .. 3 in tg0, so its low byte is token 0's tag.
+    const uint32_t t00 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tg0))) & 0xFFu;
+    const uint32_t rep = t00 * 0x01010101u;
+    const bool uniform = t00 < static_cast<uint32_t>(kMaxModalities) && (tokb + kWindow <= len) &&
+                         __all((tg0 == rep) && (tg1 == rep));
     // ---- scores relative to m_ref (the first visit of a wave takes absolute scores)
     const bool fresh = m_ref == -INFINITY;
     const float aw = (cm[0] + row_ror8(cm[0])) * zh;
@@ -613,16 +540,18 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[tau][i] = fmaf(cs[tau][i] + row_ror8(cs[tau][i]), zfac, base);
-    if (!all_count) {
+    if (!uniform) {
       // a real branch: the masking is rare, keep it off the common path
       asm volatile("" ::: "memory");
+      bool any_counted = false;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         const uint32_t tw = tau ? tg1 : tg0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = (tokb + 16 * tau + 4 * g + i < len) && ((tw >> (8 * i)) & 0xFFu) == static_cast<uint32_t>(m);
+          const bool ok = (tokb + 16 * tau + 4 * g + i < len) && ((tw >> (8 * i)) & 0xFFu) < static_cast<uint32_t>(kMaxModalities);
           if (!ok) sc[tau][i] = -INFINITY;
+          any_counted = any_counted || ok;
         }
         // tokens that do not count get p = 0 and, as their scale bits may be anything, a
         // zero scale
@@ -632,6 +561,9 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
                               (sc[tau][2 * e + 1] == -INFINITY ? 0u : 0xFFFF0000u);
         }
       }
+      // with tags in range every window inside the sequence has a counted token; a window
+      // without one (tags out of range) is skipped, which keeps the column max finite
+      if (!__any(any_counted)) return;
     }
     float lmax = -INFINITY;
 #pragma unroll
@@ -650,15 +582,17 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       if (grow) m_ref = (fresh ? 0.0f : m_ref) + delta;
       l_part *= alf;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) acc[u] *= alf;
+      for (int u = 0; u < NU; ++u) {
+        accA[u] *= alf;
+        accB[u] *= alf;
+      }
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[tau][i] -= delta;
     }
-    overlap();
-    // ---- probabilities times the value scale, as fp16 hi (part 0) or lo (part 1)
-    uint32_t bvw[4];
+    // ---- probabilities times the value scale, as fp16 hi and lo = fp16(p sigma - hi)
+    uint32_t bhi[4], blo[4];
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
       const int tau = qd >> 1;
@@ -666,9 +600,8 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       const float p1 = exp2_raw(sc[tau][2 * (qd & 1) + 1]);
       l_part += p0;
       l_part += p1;
-      // hi = fp16(p sigma); part 1 lanes then take lo = fp16(p sigma - hi)
-      const uint32_t hi = mix_pair(p0, p1, sgw[qd], 0u);
-      bvw[qd] = mix_pair(p0, p1, sgw[qd], hi & lo_mask);
+      bhi[qd] = mix_pair(p0, p1, sgw[qd], 0u);
+      blo[qd] = mix_pair(p0, p1, sgw[qd], bhi[qd]);
     }
     // ---- value contraction into the resident accumulator, one channel tile at a time.
     // Byte offsets of the pair-table entries: 2-bit values take four offsets per dword at
@@ -702,85 +635,106 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
         return vtab[(vw[pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
       }
     };
-    const uint4_t bv = uint4_t{bvw[0], bvw[1], bvw[2], bvw[3]};
+    // the operand of one accumulator keeps, in each lane, the tokens of its column's
+    // modality (dword qd holds tokens 2 (qd & 1), + 1 of byte group qd >> 1)
+    auto keep = [&](uint32_t mod, uint32_t (&k4)[4]) {
+      if (uniform) {
+        const uint32_t all = t00 == mod ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      uint4_t av;
+        for (int qd = 0; qd < 4; ++qd) k4[qd] = all;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = entry(4 * u + i);
-      acc[u] = mfma16(av, bv, acc[u]);
+        for (int qd = 0; qd < 4; ++qd) {
+          const uint32_t tw = (qd >> 1) ? tg1 : tg0;
+          const uint32_t ta = (tw >> (16 * (qd & 1))) & 0xFFu, tb = (tw >> (16 * (qd & 1) + 8)) & 0xFFu;
+          k4[qd] = (ta == mod ? 0x0000FFFFu : 0u) | (tb == mod ? 0xFFFF0000u : 0u);
+        }
+      }
+    };
+    auto accumulate = [&](float4_t (&A)[NU], const uint32_t (&k4)[4]) {
+      const uint4_t bh = uint4_t{bhi[0] & k4[0], bhi[1] & k4[1], bhi[2] & k4[2], bhi[3] & k4[3]};
+      const uint4_t bl = uint4_t{blo[0] & k4[0], blo[1] & k4[1], blo[2] & k4[2], blo[3] & k4[3]};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        uint4_t av;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = entry(4 * u + i);
+        A[u] = mfma16(av, bh, A[u]);
+        A[u] = mfma16(av, bl, A[u]);
+      }
+    };
+    // which accumulators the window needs (wave-uniform)
+    bool needA, needB;
+    if (uniform) {
+      needA = t00 != 0u;
+      needB = t00 == 0u;
+      seen |= 1u << t00;
+    } else {
+      bool a12 = false, a0 = false, a1 = false, a2 = false;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t tgi = ((tau ? tg1 : tg0) >> (8 * i)) & 0xFFu;
+          const bool ok = sc[tau][i] != -INFINITY;
+          a0 = a0 || (ok && tgi == 0u);
+          a1 = a1 || (ok && tgi == 1u);
+          a2 = a2 || (ok && tgi == 2u);
+        }
+      a12 = __any(a1 || a2);
+      needA = a12;
+      needB = __any(a0);
+      seen |= (needB ? 1u : 0u) | (__any(a1) ? 2u : 0u) | (__any(a2) ? 4u : 0u);
+    }
+    if (needA) {
+      uint32_t kA[4];
+      keep(modA, kA);
+      accumulate(accA, kA);
+    }
+    if (needB) {
+      uint32_t kB[4];
+      keep(modB, kB);
+      accumulate(accB, kB);
     }
   };
 
-  // ---- the visits, chunk by chunk (interleaving the next visit's score contractions
-  // with this one measured slower: the SIMD is issue-bound, not latency-bound)
-  for (int c0 = 0; c0 < nw; c0 += 64) {
-    if (c0 > 0) begin_chunk(c0);
-    for (int i = 0; i < total; ++i) {
-      while (cmask == 0u) cmask = pass_mask(++ck);
-      const int m = (pmod0 + ck) % kMaxModalities;
-      const int w0 = __builtin_ctzll(cmask);
-      cmask &= cmask - 1u;
-      issue_upto(min(total, i + RING));
-      // wait for this visit's copies: later visits' copies may stay in flight
-      wait_groups<L, RING - 1>(issued - (i + 1));
-      if (m != cur) make_resident(m);
-      const uint8_t* slot = ring_slot(wave, i % RING);
-      float4_t cs[2], cm;
-      score_mma(slot, cs, cm);
-      visit(slot, (wbeg + c0 + w0) * kWindow, m, cs, cm, []() {});
-    }
+  // ---- the visits
+  for (int i = 0; i < nw; ++i) {
+    issue_upto(min(nw, i + RING));
+    // wait for this visit's copies: later visits' copies may stay in flight
+    wait_groups<L, RING - 1>(issued - (i + 1));
+    const uint8_t* slot = ring_slot(wave, i % RING);
+    float4_t cs[2], cm;
+    score_mma(slot, cs, cm);
+    visit(slot, (wbeg + i) * kWindow, cs, cm);
   }
 
   // ---- epilogue: merge the block's waves into one partial.  Every copy of this wave
-  // has been waited for, so its own ring region is free: the resident accumulator goes
-  // there, next to the two stash slots.
+  // has been waited for, so its own ring region is free: each modality's accumulator
+  // columns pass through it in turn.
   __shared__ float2 ml_lds[kWaves][kMaxGroup];
-  __shared__ float ref_lds[kWaves][3][kMaxGroup];  // reference max of: resident, slot 0, slot 1
-  __shared__ int mod_lds[kWaves][3];                // their modalities (-1: none)
-  const float l = group_sum(l_part);
-  if (lane < kMaxGroup) {  // lane < 8: column = head, part 0
-    ml_lds[wave][lane] = make_float2(m_ref, l);
-    ref_lds[wave][0][lane] = m_ref;
-    ref_lds[wave][1][lane] = mst0;
-    ref_lds[wave][2][lane] = mst1;
-  }
-  if (lane == 0) {
-    mod_lds[wave][0] = cur;
-    mod_lds[wave][1] = occ0;
-    mod_lds[wave][2] = occ1;
-  }
-  float* const res_mem = reinterpret_cast<float*>(ring_slot(wave, 0));  // [8][D]
-  if (cur >= 0) {
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      float4_t v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[u][i] + row_ror8(acc[u][i]);
-      if (part == 0) *reinterpret_cast<float4_t*>(res_mem + h * D + 16 * u + 4 * g) = v;
-    }
-  }
-  __syncthreads();
-  // per (wave, source, head): the factor that brings the source to the block's max
-  __shared__ float fac_lds[kWaves][3][kMaxGroup];
+  __shared__ uint32_t seen_lds[kWaves];
+  __shared__ float fac_lds[kWaves][kMaxGroup];
   __shared__ float mb_lds[kMaxGroup];
-  if (tid < kWaves * 3 * kMaxGroup) {
-    const int v = tid / (3 * kMaxGroup), j = (tid / kMaxGroup) % 3, hh = tid % kMaxGroup;
+  const float l = group_sum(l_part);
+  if (lane < kMaxGroup) ml_lds[wave][lane] = make_float2(m_ref, l);  // lane < 8: column = head
+  if (lane == 0) seen_lds[wave] = seen;
+  __syncthreads();
+  // per (wave, head): the factor that brings the wave's sums to the block's max
+  if (tid < kWaves * kMaxGroup) {
+    const int v = tid / kMaxGroup, hh = tid % kMaxGroup;
     float mb = -INFINITY;
 #pragma unroll
     for (int x = 0; x < kWaves; ++x)
       if (ml_lds[x][hh].y > 0.0f) mb = fmaxf(mb, ml_lds[x][hh].x);
-    fac_lds[v][j][hh] = (mod_lds[v][j] >= 0 && ml_lds[v][hh].y > 0.0f) ? exp2f(ref_lds[v][j][hh] - mb) : 0.0f;
-    if (v == 0 && j == 0) mb_lds[hh] = mb;
+    fac_lds[v][hh] = ml_lds[v][hh].y > 0.0f ? exp2f(ml_lds[v][hh].x - mb) : 0.0f;
+    if (v == 0) mb_lds[hh] = mb;
   }
   __syncthreads();
   const size_t pidx = static_cast<size_t>(unit) * a.splits + blockIdx.x;
   uint32_t present = 0u;
 #pragma unroll
-  for (int v = 0; v < kWaves; ++v)
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (mod_lds[v][j] >= 0) present |= 1u << mod_lds[v][j];
+  for (int v = 0; v < kWaves; ++v) present |= seen_lds[v];
   if (tid < kMaxGroup) {
     const float mb = mb_lds[tid];
     float lsum = 0.0f;
@@ -790,31 +744,32 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     if (tid < a.group) a.ws_ml[pidx * kMaxGroup + tid] = make_float2(mb, lsum);
   }
   if (tid == 0) a.ws_mask[pidx] = present;
-  // four consecutive elements of [8][D] per thread
-  const int e4 = 4 * tid;
-  if (e4 < a.group * D) {
-    const int hh = e4 / D;
+  float* const res_mem = reinterpret_cast<float*>(ring_slot(wave, 0));  // [8][D] of this wave
+  const int e4 = 4 * tid;  // four consecutive elements of [8][D] per thread
+  // modality m lives in accumulator A (audio: half 0, video: half 1) or B (text: half 0);
+  // lane (n, g) of tile u holds channels 16u + 4g .. +3 of column n
+  auto merge = [&](int m, const float4_t (&X)[NU], int half) {
+    if (((seen >> m) & 1u) && part == half) {
 #pragma unroll
-    for (int m = 0; m < kMaxModalities; ++m) {
-      if (!(present & (1u << m))) continue;
+      for (int u = 0; u < NU; ++u) *reinterpret_cast<float4_t*>(res_mem + h * D + 16 * u + 4 * g) = X[u];
+    }
+    __syncthreads();
+    if (e4 < a.group * D) {
+      const int hh = e4 / D;
       float4_t sum = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          if (mod_lds[v][j] != m) continue;
-          // stash slots: written by wave v before the barrier (block-scope visibility)
-          const float* src = j == 0 ? reinterpret_cast<const float*>(ring_slot(v, 0))
-                                    : a.ws_stash + ((static_cast<size_t>(unit) * a.splits + blockIdx.x) * kWaves + v) *
-                                                       (2 * kMaxGroup * D) + (j - 1) * kMaxGroup * D;
-          const float f = fac_lds[v][j][hh];
-          const float4_t x = *reinterpret_cast<const float4_t*>(src + e4);
-          sum += x * f;
-        }
+        if (!((seen_lds[v] >> m) & 1u)) continue;
+        const float4_t x = *reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(ring_slot(v, 0)) + e4);
+        sum += x * fac_lds[v][hh];
       }
       *reinterpret_cast<float4_t*>(a.ws_acc + (pidx * kMaxModalities + m) * kMaxGroup * D + e4) = sum;
     }
-  }
+    __syncthreads();  // the ring regions are rewritten by the next modality
+  };
+  if (present & 1u) merge(0, accB, 0);
+  if (present & 2u) merge(1, accA, 0);
+  if (present & 4u) merge(2, accA, 1);
 }
 
 struct CombineArgs {
@@ -1122,7 +1077,6 @@ struct WorkspaceView {
   float2* ml;
   uint32_t* mask;
   float* acc;
-  float* stash;
 };
 
 WorkspaceView carve(const void* ws, size_t parts, int d) {
@@ -1133,8 +1087,6 @@ WorkspaceView carve(const void* ws, size_t parts, int d) {
   v.mask = reinterpret_cast<uint32_t*>(w);
   w += align256(parts * sizeof(uint32_t));
   v.acc = reinterpret_cast<float*>(w);
-  w += align256(parts * kMaxModalities * kMaxGroup * d * sizeof(float));
-  v.stash = reinterpret_cast<float*>(w);
   return v;
 }
 
@@ -1164,8 +1116,7 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
   p.windows_per_wave = static_cast<int>(wpw);
   const size_t parts = static_cast<size_t>(units) * splits;
   p.workspace_bytes = align256(parts * kMaxGroup * sizeof(float2)) + align256(parts * sizeof(uint32_t)) +
-                      align256(parts * kMaxModalities * kMaxGroup * sh.d * sizeof(float)) +
-                      align256(parts * kWaves * 2 * kMaxGroup * sh.d * sizeof(float));
+                      align256(parts * kMaxModalities * kMaxGroup * sh.d * sizeof(float));
   return p;
 }
 
@@ -1178,7 +1129,7 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
   const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits, sh.d);
   PartialArgs pa{q, seq_lens, kc, km, ks, vc, vs, mod, tb.signs, tb.pair_table, sh.hq, sh.hkv, sh.group,
                  sh.modalities, t_cap, max_len, scale * 1.4426950408889634f, plan.windows_per_wave, plan.splits,
-                 w.ml, w.mask, w.acc, w.stash, stream ? 1 : 0};
+                 w.ml, w.mask, w.acc, stream ? 1 : 0};
   const dim3 grid(static_cast<unsigned>(plan.splits), static_cast<unsigned>(batch * sh.hkv));
   constexpr size_t dyn_bytes = Lds<D, KB, VB>::DYN;
   static bool attr_set = false;  // dynamic LDS above the 64 KB default needs the attribute
