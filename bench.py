@@ -100,11 +100,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_16x32k_k2v2_hbm_tr
 DECODE_SOURCE = os.path.join(ROOT, "decode_attention_fwht_amd", "csrc", "decode.hip")
 
 
+def decode_code_sha256(path: str = None) -> str:
+    """sha256 of the decode source with comments and blank lines removed: a change to
+    the kernel's code changes it, a change to its comments does not."""
+    import hashlib
+    import re
+    text = open(path or DECODE_SOURCE).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
+
+
 def measured_traffic(workload: str):
     """HBM bytes per decode_partial launch from the committed FETCH_SIZE / WRITE_SIZE
     summary, scaled by the copy reference; None unless the summary was taken on this
-    workload with the current kernel source."""
-    import hashlib
+    workload with the current kernel code."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as f:
@@ -112,9 +123,7 @@ def measured_traffic(workload: str):
                 if "=" in line and not line.lstrip().startswith("#"):
                     k, v = line.split("=", 1)
                     kv[k.strip()] = v.strip()
-        with open(DECODE_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if kv.get("decode_source_sha256") != sha or kv.get("workload") != workload:
+        if kv.get("decode_code_sha256") != decode_code_sha256() or kv.get("workload") != workload:
             return None
         return int(float(kv["hbm_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):

@@ -13,21 +13,23 @@
 // (decode_combine) merges the splits with the log-sum-exp rule and applies
 // sum_m U_m A_m once per head.
 //
-// Per 32-token window the wave issues two matrix-core contractions
+// Per 32-token window the wave issues two kinds of matrix-core contraction
 // (v_mfma_f32_16x16x32_f16):
 //   scores^T [32 tok x 16 col] = codes [32 x d] . Qt [d x 16]
-//   acc_m^T  [d x 16 col]     += levels^T [d x 32 tok] . Pt [32 x 16]
-// The 16 columns are the G <= 8 query heads of the KV head, twice: columns
-// 0..7 carry the fp16 "hi" part and 8..15 the "lo" remainder of the fp32
-// operand, so each product keeps ~22 significant bits and the two halves add
-// up after the contraction (one DPP row rotate).
+//   acc^T    [d x 16 col]     += levels^T [d x 32 tok] . Pt [32 x 16]
+// For the scores the 16 columns are the G <= 8 query heads of the KV head, twice:
+// columns 0..7 carry the fp16 "hi" part and 8..15 the "lo" remainder of the fp32
+// operand, so each product keeps ~22 significant bits and the two halves add up
+// after the contraction (one DPP row rotate).  For the values the 16 columns are
+// the heads of two modalities (accumulator A: audio, video; B: text) and the hi
+// and lo parts of p * sigma enter as two contractions into the same columns.
 //   Key codes enter as fp16 subnormals: masking a stored word leaves
 //   code * 2^(bits*p - 24) in each half, exact in fp16 and exact in the f32
 //   accumulation; the per-K-step power of two is folded into Qt.
 //   Score algebra: score_log2 = Z_h * (q^.m_w + 2^24 * C) with
 //   q^ = log2(e) * scale * R q / Z_h (|q^| <= 1, Z_h a power of two),
-//   C = sum_c code_c * 2^-24 * (q^_c s_c); the q^.m_w term comes from one extra
-//   contraction per 16 windows with k_min as the operand.
+//   C = sum_c code_c * 2^-24 * (q^_c s_c); the q^.m_w term comes from four extra
+//   contractions per window with k_min as the operand.
 //   Value levels come from a per-context table of fp16 level pairs indexed by
 //   two packed codes (LDS, conflict-free for 2-bit).
 #include <math.h>
@@ -603,7 +605,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       bhi[qd] = mix_pair(p0, p1, sgw[qd], 0u);
       blo[qd] = mix_pair(p0, p1, sgw[qd], bhi[qd]);
     }
-    // ---- value contraction into the resident accumulator, one channel tile at a time.
+    // ---- value contractions, one channel tile at a time.
     // Byte offsets of the pair-table entries: 2-bit values take four offsets per dword at
     // once (low nibbles of the bytes, then high nibbles).
     uint32_t vw[VW];
