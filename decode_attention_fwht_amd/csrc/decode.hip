@@ -235,6 +235,21 @@ __device__ __forceinline__ void copy16_to_lds_sbase(const void* sbase, uint32_t 
       : "memory");
 }
 
+// One 4-byte global->LDS copy per active lane (lane l writes lds_addr + 4 l); the same
+// M0 handling as above.
+__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -258,14 +273,29 @@ __device__ __forceinline__ void wait_groups(int ahead) {
 // and leave each wave registers for the k_min operand.
 constexpr int kBlocksPerCU = 2;
 constexpr bool kBqaInRegs = kBlocksPerCU <= 2;
+// Dynamic LDS: the ring, filled by the asynchronous copies.  Before the visits a wave's
+// last ring slot (not filled before the first visit) stages its two query heads, the
+// signs of D, the sequence's length and (wave 0) the level-pair table; after them the
+// whole region holds every wave's per-modality accumulators for the block merge.
 template <int D, int KB, int VB>
 struct Lds {
-  static constexpr int fits(int ring) {
-    return kWaves * ring * Slot<D, KB, VB>::BYTES + kMaxGroup * D * 4 + 2048 <= 160 * 1024 / kBlocksPerCU;
+  static constexpr int QRAW = 2 * D * 4;         // staging: two heads' queries, fp32
+  static constexpr int SGN = D * 4;              // then the signs of D, fp32
+  static constexpr int LEN = QRAW + SGN;         // then the length (4 bytes, 16 reserved)
+  static constexpr int TAB_OFF = LEN + 16;       // then the level-pair table
+  static constexpr int TAB = 4 << (2 * VB);
+  static constexpr int MERGE = kWaves * kMaxModalities * kMaxGroup * D * 4;
+  static constexpr int STATIC = kMaxGroup * D * 4 + TAB + 1024;  // q_lds, the table, small arrays
+  static constexpr int dyn(int ring) {
+    const int r = kWaves * ring * Slot<D, KB, VB>::BYTES;
+    return r > MERGE ? r : MERGE;
   }
+  static constexpr bool fits(int ring) { return dyn(ring) + STATIC <= 160 * 1024 / kBlocksPerCU; }
   static constexpr int RING = fits(4) ? 4 : (fits(3) ? 3 : 2);
   static constexpr int RING_BYTES = kWaves * RING * Slot<D, KB, VB>::BYTES;
-  static constexpr int DYN = RING_BYTES;
+  static constexpr int DYN = dyn(RING);
+  static_assert(fits(RING), "LDS budget");
+  static_assert(TAB_OFF + TAB <= Slot<D, KB, VB>::BYTES, "staging must fit in one slot");
 };
 
 template <int D, int KB, int VB>
@@ -281,10 +311,11 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   constexpr int PPW = 16 / VB;      // value code pairs per word
   constexpr uint32_t PMASK = (1u << (2 * VB)) - 1u;
   constexpr int L = SG::COPIES;
+  using LY = Lds<D, KB, VB>;
 
-  // Dynamic LDS: the ring, kWaves x RING slots.  Only the asm copies write it, and a
-  // static LDS array that no visible code stores to would let the optimizer treat its
-  // contents as undefined and fold the slot reads.
+  // Dynamic LDS (layout in Lds).  Only the asm copies write the ring and the staging
+  // areas, and a static LDS array that no visible code stores to would let the optimizer
+  // treat its contents as undefined and fold the reads.
   extern __shared__ __attribute__((aligned(16))) uint8_t ring_mem[];
   auto ring_slot = [&](int wv, int slot) -> uint8_t* { return ring_mem + (wv * RING + slot) * SG::BYTES; };
   __shared__ __attribute__((aligned(16))) float q_lds[kMaxGroup][D];
@@ -295,13 +326,29 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int unit = blockIdx.y;                     // b * hkv + kvh
   const int b = unit / a.hkv, kvh = unit % a.hkv;
-  int len = __builtin_amdgcn_readfirstlane(
-      static_cast<int>(min<int64_t>(max<int64_t>(a.seq_lens[b], 0), a.max_len)));
-  if (a.stream) len = stream_value_packed(len);
-  const int nwin = (len + kWindow - 1) / kWindow;
+  const int h0 = 2 * wave;                         // this wave's two query heads
   const int wbeg = (blockIdx.x * kWaves + wave) * a.wpw;  // this wave's run of windows
-  const int wend = min(nwin, wbeg + a.wpw);
-  const int nw = max(0, wend - wbeg);
+
+  // ---- first copies, before anything waits for memory: this wave's two heads of the
+  // query, the signs of D, the level-pair table (wave 0), then the first windows.  The
+  // windows are bounded by the host's max_len, as the sequence's own length is not known
+  // yet; copies past it are drained before the ring is reused.
+  const auto lds_addr = [&](int off) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_mem + off)));
+  };
+  const int stage_off = (wave * RING + RING - 1) * SG::BYTES;  // this wave's last slot
+  {
+    constexpr int qlanes = LY::QRAW / 16, slanes = LY::SGN / 16, tlanes = LY::TAB / 16;
+    if (lane < qlanes) {
+      const int j = (16 * lane) / (4 * D);  // head h0 + j; heads past the group copy head 0 (zeroed later)
+      const int hh = (h0 + j < a.group) ? h0 + j : 0;
+      const float* src = a.q + (static_cast<size_t>(b) * a.hq + kvh * a.group + hh) * D + (4 * lane) % D;
+      copy16_to_lds(src, lds_addr(stage_off));
+    }
+    if (lane < slanes) copy16_to_lds(a.signs + 4 * lane, lds_addr(stage_off + LY::QRAW));
+    if (lane == 0) copy4_to_lds(a.seq_lens + b, lds_addr(stage_off + LY::LEN));
+    if (wave == 0 && lane < tlanes) copy16_to_lds(a.pair_table + 4 * lane, lds_addr(stage_off + LY::TAB_OFF));
+  }
   const int n = lane & 15, g = lane >> 4, h = n & 7, part = n >> 3;
   const int64_t nwin_cap = a.t_cap / kWindow;
   const size_t unit_win = static_cast<size_t>(unit) * nwin_cap;
@@ -343,23 +390,6 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     if (lane < SG::MISC_LANES) copy16_to_lds(mbase + static_cast<size_t>(w) * mstride, dst + SG::OFF_S);
   };
 
-  // ---- the queries of this wave's two heads
-  const int h0 = 2 * wave;
-  float qv[2][NC];
-  {
-    float sg[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) sg[c] = a.signs[lane + 64 * c];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int hh = h0 + j;
-      const bool ok = hh < a.group;
-      const float* qp = a.q + (static_cast<size_t>(b) * a.hq + kvh * a.group + (ok ? hh : 0)) * D;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) qv[j][c] = qp[lane + 64 * c] * (ok ? sg[c] : 0.0f);
-    }
-  }
-
   // ---- visit order: the wave's windows in order, each visited once whatever modalities
   // it holds.  Visit i (window wbeg + i) goes to slot i % RING once visit i - RING has
   // been computed; the first copies go out before the query set-up, which hides their
@@ -368,9 +398,36 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   auto issue_upto = [&](int lim) {
     for (; issued < lim; ++issued) issue(wbeg + issued, issued % RING);
   };
-  issue_upto(min(nw, RING - 1));
+  {
+    const int64_t bound = a.stream ? stream_value_packed(a.max_len) : a.max_len;
+    const int nwin_bound = static_cast<int>((bound + kWindow - 1) / kWindow);
+    issue_upto(min(max(0, min(nwin_bound, wbeg + a.wpw) - wbeg), RING - 1));
+  }
 
-  for (int i = tid; i < (1 << (2 * VB)); i += kWaves * 64) vtab[i] = a.pair_table[i];
+  // ---- the staging copies (issued before any window's) have landed: the sequence's
+  // length (clamped to the host bound), this wave's visits, the queries of its two heads
+  wait_groups<L, RING - 1>(issued);
+  int len = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(ring_mem + stage_off + LY::LEN));
+  if (wave == 0) {  // the table goes to its own array (read by every wave after the barrier below)
+    const uint32_t* t = reinterpret_cast<const uint32_t*>(ring_mem + stage_off + LY::TAB_OFF);
+    for (int i = lane; i < (1 << (2 * VB)); i += 64) vtab[i] = t[i];
+  }
+  len = static_cast<int>(min<int64_t>(max(len, 0), a.max_len));
+  if (a.stream) len = stream_value_packed(len);
+  const int nwin = (len + kWindow - 1) / kWindow;
+  const int wend = min(nwin, wbeg + a.wpw);
+  const int nw = max(0, wend - wbeg);
+  float qv[2][NC];
+  {
+    const float* qraw = reinterpret_cast<const float*>(ring_mem + stage_off);
+    const float* sgn = reinterpret_cast<const float*>(ring_mem + stage_off + LY::QRAW);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = h0 + j < a.group;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qv[j][c] = qraw[j * D + lane + 64 * c] * (ok ? sgn[lane + 64 * c] : 0.0f);
+    }
+  }
 
   // ---- query rotation q' = c_d H D q (two heads per wave), scaled to log2 units
 #pragma unroll
@@ -700,8 +757,17 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     }
   };
 
-  // ---- the visits
+  // ---- the visits.  Waves of two workgroups share each SIMD, and the arbiter favours the
+  // older one, which would leave the younger to finish its last windows alone at a lower
+  // issue rate.  Each wave therefore lowers its priority as it progresses (3 for its first
+  // quarter of visits .. 0 for its last), so a wave that falls behind a quarter gets the
+  // issue slots until it catches up.
+  const int q1 = nw / 4, q2 = nw / 2, q3 = (3 * nw) / 4;
+  __builtin_amdgcn_s_setprio(3);
   for (int i = 0; i < nw; ++i) {
+    if (i == q1) __builtin_amdgcn_s_setprio(2);
+    if (i == q2) __builtin_amdgcn_s_setprio(1);
+    if (i == q3) __builtin_amdgcn_s_setprio(0);
     issue_upto(min(nw, i + RING));
     // wait for this visit's copies: later visits' copies may stay in flight
     wait_groups<L, RING - 1>(issued - (i + 1));
@@ -711,67 +777,74 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     visit(slot, (wbeg + i) * kWindow, cs, cm);
   }
 
-  // ---- epilogue: merge the block's waves into one partial.  Every copy of this wave
-  // has been waited for, so its own ring region is free: each modality's accumulator
-  // columns pass through it in turn.
+  __builtin_amdgcn_s_setprio(0);
+
+  // ---- epilogue: merge the block's waves into one partial.  Copies past this wave's
+  // visits (issued before its length was known) are drained first; once every wave is past
+  // its visits the dynamic LDS is free, and every wave stages the accumulators of the
+  // modalities it met in its own [modality][head][D] region, all read after one more
+  // barrier.
+  wait_vmcnt<0>();
   __shared__ float2 ml_lds[kWaves][kMaxGroup];
   __shared__ uint32_t seen_lds[kWaves];
-  __shared__ float fac_lds[kWaves][kMaxGroup];
-  __shared__ float mb_lds[kMaxGroup];
   const float l = group_sum(l_part);
   if (lane < kMaxGroup) ml_lds[wave][lane] = make_float2(m_ref, l);  // lane < 8: column = head
   if (lane == 0) seen_lds[wave] = seen;
   __syncthreads();
-  // per (wave, head): the factor that brings the wave's sums to the block's max
-  if (tid < kWaves * kMaxGroup) {
-    const int v = tid / kMaxGroup, hh = tid % kMaxGroup;
-    float mb = -INFINITY;
+  constexpr int RES = kMaxModalities * kMaxGroup * D;  // floats per wave
+  {
+    float* const res = reinterpret_cast<float*>(ring_mem) + wave * RES;
+    // modality m lives in accumulator A (audio: half 0, video: half 1) or B (text: half 0);
+    // lane (n, g) of tile u holds channels 16u + 4g .. +3 of column n
+    auto stage = [&](int m, const float4_t (&X)[NU], int half) {
+      if (((seen >> m) & 1u) && part == half) {
 #pragma unroll
-    for (int x = 0; x < kWaves; ++x)
-      if (ml_lds[x][hh].y > 0.0f) mb = fmaxf(mb, ml_lds[x][hh].x);
-    fac_lds[v][hh] = ml_lds[v][hh].y > 0.0f ? exp2f(ml_lds[v][hh].x - mb) : 0.0f;
-    if (v == 0) mb_lds[hh] = mb;
+        for (int u = 0; u < NU; ++u)
+          *reinterpret_cast<float4_t*>(res + (m * kMaxGroup + h) * D + 16 * u + 4 * g) = X[u];
+      }
+    };
+    stage(0, accB, 0);
+    stage(1, accA, 0);
+    stage(2, accA, 1);
   }
   __syncthreads();
   const size_t pidx = static_cast<size_t>(unit) * a.splits + blockIdx.x;
   uint32_t present = 0u;
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) present |= seen_lds[v];
-  if (tid < kMaxGroup) {
-    const float mb = mb_lds[tid];
-    float lsum = 0.0f;
+  if (tid == 0) a.ws_mask[pidx] = present;
+  const int e4 = 4 * tid;  // four consecutive elements of [head][D] per thread
+  if (e4 < a.group * D) {
+    const int hh = e4 / D;
+    // the factors that bring each wave's sums to the block's max
+    float mb = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v)
-      if (ml_lds[v][tid].y > 0.0f) lsum += exp2f(ml_lds[v][tid].x - mb) * ml_lds[v][tid].y;
-    if (tid < a.group) a.ws_ml[pidx * kMaxGroup + tid] = make_float2(mb, lsum);
-  }
-  if (tid == 0) a.ws_mask[pidx] = present;
-  float* const res_mem = reinterpret_cast<float*>(ring_slot(wave, 0));  // [8][D] of this wave
-  const int e4 = 4 * tid;  // four consecutive elements of [8][D] per thread
-  // modality m lives in accumulator A (audio: half 0, video: half 1) or B (text: half 0);
-  // lane (n, g) of tile u holds channels 16u + 4g .. +3 of column n
-  auto merge = [&](int m, const float4_t (&X)[NU], int half) {
-    if (((seen >> m) & 1u) && part == half) {
+      if (ml_lds[v][hh].y > 0.0f) mb = fmaxf(mb, ml_lds[v][hh].x);
+    float fac[kWaves];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) *reinterpret_cast<float4_t*>(res_mem + h * D + 16 * u + 4 * g) = X[u];
+    for (int v = 0; v < kWaves; ++v) fac[v] = ml_lds[v][hh].y > 0.0f ? exp2f(ml_lds[v][hh].x - mb) : 0.0f;
+    if (e4 % D == 0) {
+      float lsum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v)
+        if (ml_lds[v][hh].y > 0.0f) lsum += fac[v] * ml_lds[v][hh].y;
+      a.ws_ml[pidx * kMaxGroup + hh] = make_float2(mb, lsum);
     }
-    __syncthreads();
-    if (e4 < a.group * D) {
-      const int hh = e4 / D;
+#pragma unroll
+    for (int m = 0; m < kMaxModalities; ++m) {
+      if (!((present >> m) & 1u)) continue;
       float4_t sum = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
         if (!((seen_lds[v] >> m) & 1u)) continue;
-        const float4_t x = *reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(ring_slot(v, 0)) + e4);
-        sum += x * fac_lds[v][hh];
+        const float4_t x = *reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(ring_mem) + v * RES +
+                                                             m * kMaxGroup * D + e4);
+        sum += x * fac[v];
       }
       *reinterpret_cast<float4_t*>(a.ws_acc + (pidx * kMaxModalities + m) * kMaxGroup * D + e4) = sum;
     }
-    __syncthreads();  // the ring regions are rewritten by the next modality
-  };
-  if (present & 1u) merge(0, accB, 0);
-  if (present & 2u) merge(1, accA, 0);
-  if (present & 4u) merge(2, accA, 1);
+  }
 }
 
 struct CombineArgs {
