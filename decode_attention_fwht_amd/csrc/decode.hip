@@ -108,11 +108,11 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 // just written by a transcendental instruction (the hazard recognizer does not look
 // inside asm).
 __device__ __forceinline__ uint32_t mix_pair(float p0, float p1, uint32_t s, uint32_t c) {
-  uint32_t d = 0u;
+  uint32_t d;  // both halves are written here, so its earlier contents do not matter
   asm("s_nop 0\n\t"
       "v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
       "v_fma_mixhi_f16 %0, %4, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
-      : "+&v"(d)
+      : "=&v"(d)
       : "v"(p0), "v"(s), "v"(c), "v"(p1));
   return d;
 }
@@ -553,17 +553,21 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
         cm = mfma16(mv4, bqa[s], cm);
       else
         cm = mfma16(mv4, bqa_lds[s * 64 + lane], cm);
+      // three passes over the four dwords (independent neighbours between dependent steps)
+      half2_t sv[4], t[4];
       uint32_t bq[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // copy the element out first: bit_cast of an ext-vector element subscript is
         // lowered as element 0 by this compiler
         const uint32_t svw = sv4[i];
-        const half2_t sv = __builtin_bit_cast(half2_t, svw);
-        const half2_t t1 = beta[s][i] * sv;
-        const half2_t t2 = __builtin_elementwise_fma(alpha[s][i], sv, -t1);
-        bq[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(gamma[s][i], sv, t2));
+        sv[i] = __builtin_bit_cast(half2_t, svw);
+        t[i] = beta[s][i] * sv[i];
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = __builtin_elementwise_fma(alpha[s][i], sv[i], -t[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bq[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(gamma[s][i], sv[i], t[i]));
       const uint4_t bqv = uint4_t{bq[0], bq[1], bq[2], bq[3]};
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
