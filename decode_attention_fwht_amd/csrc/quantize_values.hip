@@ -7,6 +7,8 @@
 // plain dot product accumulated in index order with every product and sum
 // rounded to fp32, so the codes are bit-identical to any implementation of the
 // same definition.
+#include <type_traits>
+
 #include "omnikv_internal.h"
 
 namespace omnikv {
@@ -275,8 +277,13 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
     }
     if (lane == 0) nflag_lds[wave] = 0;
 
-    // ---- per-token scale: stride-halving tree of squares (lane l holds channels l, l + 64)
-    uint16_t my_s16 = 0;
+    // ---- per-token scale: stride-halving tree of squares (lane l holds channels l, l + 64).
+    // The 32 trees run as one reduce-scatter: the stage across lane bit b (b = 5 .. 1) adds
+    // the partner's partial sums for half of the lane's tokens and leaves the other half to
+    // the partner, so after five stages lane l holds token l >> 1 alone, and the last stage
+    // (bit 0) completes it in both lanes of the pair.  Every sum is the tree's own (each
+    // stage adds the same two partial sums as the stride-halving definition), so the result
+    // is the definition's exactly; no stage waits on another token's shuffles.
     {
       float x[kWindow][NC];
 #pragma unroll
@@ -284,26 +291,46 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           x[t][c] = __uint_as_float(static_cast<uint32_t>(v[row0 + t * rstride + lane + 64 * c]) << 16);
+      float part[kWindow];
+      uint32_t nzbits = 0u;  // tokens with a nonzero magnitude bit in this lane (subnormals count)
 #pragma unroll
       for (int t = 0; t < kWindow; ++t) {
-        float s = (NC == 2) ? (x[t][0] * x[t][0] + x[t][1] * x[t][1]) : x[t][0] * x[t][0];
-#pragma unroll
-        for (int hh = 32; hh >= 1; hh >>= 1) s = s + __shfl_xor(s, hh, 64);
-        const float sigma = sqrtf(s * (1.0f / static_cast<float>(D)));
-        const uint16_t s16 = f16_bits(sigma);
-        // any nonzero magnitude bit among the token's values (an integer test: subnormals count)
+        part[t] = (NC == 2) ? (x[t][0] * x[t][0] + x[t][1] * x[t][1]) : x[t][0] * x[t][0];
         uint32_t mag = 0u;
 #pragma unroll
         for (int c = 0; c < NC; ++c) mag |= __float_as_uint(x[t][c]) & 0x7FFFFFFFu;
-        const bool nonzero = __ballot(mag != 0u) != 0ull;
-        if (lane == t) my_s16 = s16;
-        if (lane == 0) {
-          sig_lds[wave][t] = f16_value(s16);
-          eps_lds[wave][t] = nonzero ? eps_c * sqrtf(s) + 1e-20f : -1.0f;
+        nzbits |= (mag != 0u ? 1u : 0u) << t;
+      }
+#pragma unroll
+      for (int hh = 32; hh >= 1; hh >>= 1) nzbits |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(nzbits), hh, 64));
+      // reduce-scatter over lane bits 5 .. 1; part[k] is then the partial sum of token base + k
+      int base = 0;
+      auto stage = [&](auto st_c) {
+        constexpr int st = decltype(st_c)::value, cnt = 1 << (st - 1);
+        const bool up = (lane >> st) & 1;
+#pragma unroll
+        for (int k = 0; k < cnt; ++k) {
+          const float give = up ? part[k] : part[cnt + k];
+          const float keep = up ? part[cnt + k] : part[k];
+          part[k] = keep + __shfl_xor(give, 1 << st, 64);
         }
+        base += up ? cnt : 0;
+      };
+      stage(std::integral_constant<int, 5>{});
+      stage(std::integral_constant<int, 4>{});
+      stage(std::integral_constant<int, 3>{});
+      stage(std::integral_constant<int, 2>{});
+      stage(std::integral_constant<int, 1>{});
+      const float S = part[0] + __shfl_xor(part[0], 1, 64);  // token base = lane >> 1
+      const float sigma = sqrtf(S * (1.0f / static_cast<float>(D)));
+      const uint16_t s16 = f16_bits(sigma);
+      if ((lane & 1) == 0) {
+        const int t = base;
+        sig_lds[wave][t] = f16_value(s16);
+        eps_lds[wave][t] = ((nzbits >> t) & 1u) ? eps_c * sqrtf(S) + 1e-20f : -1.0f;
+        v_scale[(static_cast<size_t>(b) * hkv + h) * t_cap + tok0 + t] = s16;
       }
     }
-    if (lane < kWindow) v_scale[(static_cast<size_t>(b) * hkv + h) * t_cap + tok0 + lane] = my_s16;
 
     // ---- the window as matrix-core A operands: token 16 tt + n, channels 32 ks + 8 g ..
     const int nn = lane & 15, g = lane >> 4;
