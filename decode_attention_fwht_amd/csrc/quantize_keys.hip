@@ -5,11 +5,14 @@
 //   (TurboQuant's rotation; temporal key drift), §3.1 Implementation details
 //   (32-token groups), §3.3 Error comparison (m_gc, s_gc in FP16).
 //
-// One 64-lane wave owns one window of one (sequence, KV head).  Lane l holds
-// channels l and l + 64 of every token, so the per-channel min/max over the
-// window never leaves the lane; the Hadamard stages h < 64 cross lanes.  The
-// fp32 operations follow the documented order exactly, so codes and metadata
-// are bit-identical to any implementation of the same definition.
+// One 64-lane wave owns one window of one (sequence, KV head).  A token spans D/8 lanes
+// of one 16-lane row, eight consecutive channels per lane, so a wave holds 64/(D/8)
+// tokens at a time: the Hadamard stages h = 1, 2, 4 stay inside the lane and the larger
+// ones pair lanes of the same row (data-parallel-primitive moves, no LDS).  Every stage
+// adds or subtracts the same two values as the documented butterfly order, so codes and
+// metadata are bit-identical to any implementation of the same definition.
+#include <type_traits>
+
 #include "omnikv_internal.h"
 
 namespace omnikv {
@@ -67,16 +70,37 @@ __device__ __forceinline__ void key_slot(int tau, int s, int j, int& lw, int& bi
 
 constexpr int kWavesPerBlock = 4;
 
+// value of lane l ^ (1 << k) within each 16-lane row (k = 0 .. 3)
+template <int K>
+__device__ __forceinline__ float row_xor(float x) {
+  const int v = __builtin_bit_cast(int, x);
+  if constexpr (K == 0) {  // quad_perm [1, 0, 3, 2]
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (K == 1) {  // quad_perm [2, 3, 0, 1]
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (K == 2) {
+    // lanes 0-3 and 8-11 of a row read lane + 4 (row_shl:4), lanes 4-7 and 12-15 lane - 4
+    // (row_shr:4); the bank mask picks which lanes each move writes
+    const int lo = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(lo, v, 0x114, 0xF, 0xA, false));
+  } else {  // row_ror:8
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+  }
+}
+
 template <int D, int KB, bool BF16>
 __global__ __launch_bounds__(256) void quantize_keys_kernel(
     const void* __restrict__ k, int hkv, int64_t n, int64_t w0, int64_t nwin_cap,
     int64_t tasks, const float* __restrict__ signs, uint32_t* __restrict__ k_codes,
     uint16_t* __restrict__ k_min, uint16_t* __restrict__ k_scale) {
-  constexpr int NC = D / 64;                 // channels per lane
   constexpr int L = (1 << KB) - 1;           // largest code
   constexpr int KW = D * KB / 64;            // output words per lane
   constexpr int NS = D / 32;                 // K-steps of the decode operand
   constexpr int ROW = D + 8;                 // padded LDS row (bytes)
+  constexpr int LPT = D / 8;                 // lanes per token
+  constexpr int TPI = 64 / LPT;              // tokens per pass
+  constexpr int NP = kWindow / TPI;          // passes per window
+  constexpr int XS = D == 128 ? 4 : 3;       // cross-lane stages (lane bits 0 .. XS-1)
   __shared__ uint8_t codes_lds[kWavesPerBlock][kWindow][ROW];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -88,65 +112,128 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
   const int64_t w = active ? (task / hkv) % nw : 0;
   const int h = active ? static_cast<int>(task % hkv) : 0;
   const size_t blk = (static_cast<size_t>(b) * hkv + h) * nwin_cap + w0 + w;
+  const int q = lane % LPT, r = lane / LPT;  // channels 8q .. 8q + 7 of token TPI * pass + r
 
   if (active) {
-    float sg[NC];
+    float sg[8];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sg[c] = signs[lane + 64 * c];
-    float y[kWindow][NC];
-    float mn[NC], mx[NC];
+    for (int e = 0; e < 8; ++e) sg[e] = signs[8 * q + e];
+    float y[NP][8];
+    float mn[8], mx[8];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      mn[c] = INFINITY;
-      mx[c] = -INFINITY;
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = INFINITY;
+      mx[e] = -INFINITY;
     }
 #pragma unroll
-    for (int t = 0; t < kWindow; ++t) {
-      const size_t row = ((static_cast<size_t>(b) * n + w * kWindow + t) * hkv + h) * D;
-      float z[NC];
+    for (int pp = 0; pp < NP; ++pp) {
+      const int t = TPI * pp + r;
+      const size_t row = ((static_cast<size_t>(b) * n + w * kWindow + t) * hkv + h) * D + 8 * q;
+      float z[8];
+      if constexpr (BF16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + row);
+        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) z[c] = load_elem<BF16>(k, row + lane + 64 * c) * sg[c];
-      // butterfly stages h = 1 .. 32 across lanes: lower index keeps a + b, upper gets a - b
+        for (int e = 0; e < 8; ++e) z[e] = __uint_as_float((e & 1) ? (wds[e >> 1] & 0xFFFF0000u) : (wds[e >> 1] << 16));
+      } else {
+        const float4 f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(k) + row);
+        const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(k) + row + 4);
+        z[0] = f0.x; z[1] = f0.y; z[2] = f0.z; z[3] = f0.w;
+        z[4] = f1.x; z[5] = f1.y; z[6] = f1.z; z[7] = f1.w;
+      }
 #pragma unroll
-      for (int hh = 1; hh < 64; hh <<= 1) {
+      for (int e = 0; e < 8; ++e) z[e] = z[e] * sg[e];
+      // stages h = 1, 2, 4 inside the lane: lower index keeps a + b, upper gets a - b
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const float p = __shfl_xor(z[c], hh, 64);
-          z[c] = (lane & hh) ? (p - z[c]) : (z[c] + p);
+      for (int hh = 1; hh < 8; hh <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (e & hh) continue;
+          const float a0 = z[e], b0 = z[e + hh];
+          z[e] = a0 + b0;
+          z[e + hh] = a0 - b0;
         }
       }
-      if constexpr (NC == 2) {  // stage h = 64 inside the lane
-        const float a0 = z[0] + z[1];
-        const float a1 = z[0] - z[1];
-        z[0] = a0;
-        z[1] = a1;
-      }
+      // stages h = 8 << kk across lanes q ^ (1 << kk): the lower lane keeps own + partner,
+      // the upper gets partner - own, both one rounding of the exact sum (fma by +-1)
+      auto cross = [&](auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
+        const float sgn = ((q >> kk) & 1) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float yy = z[c] * RhtConst<D>::value;
-        y[t][c] = yy;
-        mn[c] = fminf(mn[c], yy);
-        mx[c] = fmaxf(mx[c], yy);
+        for (int e = 0; e < 8; ++e) z[e] = __builtin_fmaf(z[e], sgn, row_xor<kk>(z[e]));
+      };
+      cross(std::integral_constant<int, 0>{});
+      cross(std::integral_constant<int, 1>{});
+      cross(std::integral_constant<int, 2>{});
+      if constexpr (XS == 4) cross(std::integral_constant<int, 3>{});
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float yy = z[e] * RhtConst<D>::value;
+        y[pp][e] = yy;
+        mn[e] = fminf(mn[e], yy);
+        mx[e] = fmaxf(mx[e], yy);
       }
     }
+    // the window's extremes: combine the TPI token rows holding the same channels
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float lo = mn[c] + 0.0f;  // a zero extreme is +0
-      const float hi = mx[c] + 0.0f;
+    for (int sh = LPT; sh < 64; sh <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mn[e] = fminf(mn[e], __shfl_xor(mn[e], sh, 64));
+        mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], sh, 64));
+      }
+    }
+    float mf[8], sf[8];
+    uint16_t m16[8], s16[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float lo = mn[e] + 0.0f;  // a zero extreme is +0
+      const float hi = mx[e] + 0.0f;
       const float step = (hi - lo) / static_cast<float>(L);
-      const uint16_t m16 = f16_bits(lo), s16 = f16_bits(step);
-      k_min[blk * D + lane + 64 * c] = m16;
-      k_scale[blk * D + lane + 64 * c] = s16;
-      const float mf = f16_value(m16), sf = f16_value(s16);
-      float th[L];
+      m16[e] = f16_bits(lo);
+      s16[e] = f16_bits(step);
+      mf[e] = f16_value(m16[e]);
+      sf[e] = f16_value(s16[e]);
+    }
+    if (r == 0) {
+      uint32_t pm[4], ps[4];
 #pragma unroll
-      for (int j = 0; j < L; ++j) th[j] = mf + sf * (static_cast<float>(j) + 0.5f);
+      for (int x = 0; x < 4; ++x) {
+        pm[x] = static_cast<uint32_t>(m16[2 * x]) | (static_cast<uint32_t>(m16[2 * x + 1]) << 16);
+        ps[x] = static_cast<uint32_t>(s16[2 * x]) | (static_cast<uint32_t>(s16[2 * x + 1]) << 16);
+      }
+      *reinterpret_cast<uint4*>(k_min + blk * D + 8 * q) = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+      *reinterpret_cast<uint4*>(k_scale + blk * D + 8 * q) = make_uint4(ps[0], ps[1], ps[2], ps[3]);
+    }
+    // code = #{j : y >= m + s (j + 1/2)}; the thresholds rise with j, so for 4-bit codes a
+    // binary search over j finds the same count
 #pragma unroll
-      for (int t = 0; t < kWindow; ++t) {
-        int code = 0;
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (KB == 2) {
+        float th[L];
 #pragma unroll
-        for (int j = 0; j < L; ++j) code += (y[t][c] >= th[j]) ? 1 : 0;
-        codes_lds[wave][t][lane + 64 * c] = static_cast<uint8_t>(code);
+        for (int j = 0; j < L; ++j) th[j] = mf[e] + sf[e] * (static_cast<float>(j) + 0.5f);
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          int code = 0;
+#pragma unroll
+          for (int j = 0; j < L; ++j) code += (y[pp][e] >= th[j]) ? 1 : 0;
+          codes_lds[wave][TPI * pp + r][8 * q + e] = static_cast<uint8_t>(code);
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          int code = 0;  // invariant: y >= theta_j for every j < code
+#pragma unroll
+          for (int stp = 8; stp >= 1; stp >>= 1) {
+            const int j = code + stp - 1;  // candidate: is y >= theta_j ?
+            if (j < L) {
+              const float th = mf[e] + sf[e] * (static_cast<float>(j) + 0.5f);
+              code = (y[pp][e] >= th) ? code + stp : code;
+            }
+          }
+          codes_lds[wave][TPI * pp + r][8 * q + e] = static_cast<uint8_t>(code);
+        }
       }
     }
   }
