@@ -221,6 +221,20 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
     }
   if (!std::isfinite(col_norm)) split_exact = false;
   ctx->tb.rot_col_norm = static_cast<float>(col_norm * (1.0 + 1e-6));
+  double lo_norm = 0.0;  // largest column norm of the third part
+  for (int m = 0; m < omnikv::kMaxModalities; ++m)
+    for (int ct = 0; ct < nct; ++ct)
+      for (int n = 0; n < 16; ++n) {
+        double s2 = 0.0;
+        for (int ks = 0; ks < nks; ++ks)
+          for (int g = 0; g < 4; ++g)
+            for (int i = 0; i < 8; ++i) {
+              const double u = host_bf16_value(rb16[(((((static_cast<size_t>(m) * 3 + 2) * nct + ct) * nks + ks) * 64 + 16 * g + n) * 8) + i]);
+              s2 += u * u;
+            }
+        lo_norm = std::max(lo_norm, std::sqrt(s2));
+      }
+  ctx->tb.rot_lo_col_norm = static_cast<float>(lo_norm * (1.0 + 1e-6));
 
   omnikv_status st;
   if ((st = upload(&ctx->tb.signs, sg.data(), sg.size())) != OMNIKV_OK ||

@@ -30,6 +30,9 @@ struct DeviceTables {
   // host value: the largest column norm max_{m,c} ||U_m e_c||_2, which bounds the sum of
   // |U_m[k][c] v_k| over k by that times ||v||_2
   float rot_col_norm = 1.0f;
+  // host value: the same for the third bf16 part alone (the part the value quantizer's
+  // matrix-core pass leaves out), rounded up
+  float rot_lo_col_norm = 0.0f;
 };
 
 // Streaming schedule ([paper] §3.1 Implementation details, captioning): after n

@@ -211,10 +211,11 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(
 // ---------------------------------------------------------------------------------------
 // bf16 inputs on the matrix cores.  v' = U_m^T v for the 32 tokens of a window is one
 // [32 x d] x [d x d] product: v_mfma_f32_16x16x32_bf16 with the bf16 values as they come
-// and U_m in three bf16 parts whose sum is U_m exactly.  That result and the defined
-// sequential fp32 sum both lie within a bounded number of fp32 roundings of the exact dot
-// product, each rounding at most 2^-23 of the sum of |terms|, and that sum is at most
-// (largest column norm of U_m) x ||v_t||_2; so the two differ by at most
+// and the two leading parts of U_m's split into three bf16 parts whose sum is U_m exactly.
+// That result and the defined sequential fp32 sum both lie within a bounded number of fp32
+// roundings of the exact dot product, each rounding at most 2^-23 of the sum of |terms|,
+// and that sum is at most (largest column norm of U_m) x ||v_t||_2; the omitted third part
+// adds at most its own largest column norm x ||v_t||_2; so the two differ by at most
 // eps_t = eps_c ||v_t||_2 (+ a tiny absolute term for underflow).  A code is taken from
 // the matrix-core value when that value is farther than eps_t from every threshold - the
 // sequential sum then falls on the same side of each - and otherwise from the sequential
@@ -357,14 +358,14 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
       const uint4_t* B = rot_b16 + static_cast<size_t>(m) * 3 * NCT * NKS * 64 + lane;
 #pragma unroll 2
       for (int ct = 0; ct < NCT; ++ct) {
-        uint4_t bv[3][NKS];
+        uint4_t bv[2][NKS];
 #pragma unroll
-        for (int part = 0; part < 3; ++part)
+        for (int part = 0; part < 2; ++part)
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) bv[part][ks] = B[((part * NCT + ct) * NKS + ks) * 64];
         float4_t acc[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int part = 0; part < 3; ++part)
+        for (int part = 0; part < 2; ++part)
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -453,15 +454,19 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
   for (int x = 0; x < VW; x += 2) *reinterpret_cast<uint2*>(dst + x) = make_uint2(words[x], words[x + 1]);
 }
 
-// eps_c / (largest column norm of U_m), in units of the sum of |terms| of one dot product.
-// Matrix cores: 3 d/32 instructions per output, each adding 32 exact bf16 products to the
-// accumulator with an error of at most 34 x 2^-23 of (|acc| + those products), in case the
-// unit aligns the addends by truncation.  Sequential: d products and d sums, each rounded
-// to nearest.  The three bf16 parts of U_m sum in magnitude to at most 1.01 |U_m|, and a 2%
-// margin covers the rounding of ||v||_2 = sqrt(S) and of |v' - theta|.
+// The tolerance eps_t = eps ||v_t||_2 between the matrix-core value and the sequential
+// definition, eps = value_eps_unit * (largest column norm of U_m) + 1.02 * (largest column
+// norm of the third bf16 part of U_m, which the matrix cores leave out: its dot product
+// with v is at most that times ||v||_2).  value_eps_unit counts, in units of the sum of
+// |terms| of one dot product: matrix cores, 2 d/32 instructions per output, each adding 32
+// exact bf16 products to the accumulator with an error of at most 34 x 2^-23 of (|acc| +
+// those products), in case the unit aligns the addends by truncation; sequential, d
+// products and d sums, each rounded to nearest.  The two bf16 parts of U_m sum in
+// magnitude to at most 1.01 |U_m|, and a 2% margin covers the rounding of ||v||_2 =
+// sqrt(S) and of |v' - theta|.
 template <int D>
 constexpr double value_eps_unit() {
-  return 1.02 * 1.01 * (68.0 * (3 * (D / 32) + 1) + (2 * D + 2)) / 16777216.0;
+  return 1.02 * 1.01 * (68.0 * (2 * (D / 32) + 1) + (2 * D + 2)) / 16777216.0;
 }
 
 template <int D, int VB>
@@ -473,7 +478,8 @@ hipError_t launch_vb(const DeviceTables& tb, const void* v, bool bf16, const uin
   if (bf16 && tb.rot_bf16 != nullptr)
     quantize_values_mfma_kernel<D, VB><<<grid, 256, 0, stream>>>(
         static_cast<const uint16_t*>(v), mod, hkv, n, t0, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
-        tb.rotations_t, tb.boundaries, static_cast<float>(value_eps_unit<D>() * tb.rot_col_norm), vc, vs);
+        tb.rotations_t, tb.boundaries,
+        static_cast<float>(value_eps_unit<D>() * tb.rot_col_norm + 1.02 * tb.rot_lo_col_norm), vc, vs);
   else if (bf16)
     quantize_values_kernel<D, VB, true><<<grid, 256, 0, stream>>>(v, mod, hkv, n, t0, t_cap, tasks, tb.rotations,
                                                                   tb.boundaries, vc, vs);
