@@ -350,6 +350,15 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) my_tag[tt][i] = tag_lds[wave][16 * tt + 4 * g + i];
+    // and their scales and tolerances, read once for all channel tiles
+    float my_sg[2][4], my_ep[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        my_sg[tt][i] = sig_lds[wave][16 * tt + 4 * g + i];
+        my_ep[tt][i] = eps_lds[wave][16 * tt + 4 * g + i];
+      }
 
     // ---- one pass per modality present
 #pragma unroll
@@ -380,7 +389,7 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
             if (my_tag[tt][i] != static_cast<uint32_t>(m)) continue;
             const int t = 16 * tt + 4 * g + i;
             const float x = acc[tt][i];
-            const float sg = sig_lds[wave][t], e = eps_lds[wave][t];
+            const float sg = my_sg[tt][i], e = my_ep[tt][i];
             int code = 0;
             bool near = false;
 #pragma unroll
