@@ -70,29 +70,34 @@ def build_caches(ctx, cfg, nbuf, kbits, vbits, chunk=4096, seed=0):
 
 
 def time_write_path(ctx, cfg, tags_np, reps=20, seed=3):
-    """Time omnikv_quantize_keys / _values on one prefill chunk per sequence."""
+    """Time omnikv_quantize_keys / _values on one prefill chunk per sequence.  Several
+    input chunks (together over 2.5x the Infinity Cache) are cycled, so the inputs are read
+    from HBM as a prefill's freshly computed keys and values would be."""
     import torch
     n = cfg.prefill if cfg.prefill else 4096
     c = ctx.alloc_cache(cfg.batch, n)
     c["modality"].copy_(torch.from_numpy(tags_np[:, :n]))
-    kk = synth.drifting_tensor_device(cfg, tags_np, seed, 0, 0, n)
-    vv = synth.drifting_tensor_device(cfg, tags_np, seed, 1, 0, n)
-    for _ in range(3):
-        ctx.quantize_keys(kk, 0, c)
-        ctx.quantize_values(vv, 0, c)
+    chunk_bytes = cfg.batch * n * cfg.kv_heads * cfg.head_dim * (4 if cfg.fp32_inputs else 2)
+    nbuf = max(2, math.ceil(2.5 * MALL_BYTES / chunk_bytes))
+    ks = [synth.drifting_tensor_device(cfg, tags_np, seed + 31 * i, 0, 0, n) for i in range(nbuf)]
+    vs = [synth.drifting_tensor_device(cfg, tags_np, seed + 31 * i, 1, 0, n) for i in range(nbuf)]
+    for i in range(3):
+        ctx.quantize_keys(ks[i % nbuf], 0, c)
+        ctx.quantize_values(vs[i % nbuf], 0, c)
     torch.cuda.synchronize()
     res = {}
-    for name, fn, x in (("keys", ctx.quantize_keys, kk), ("values", ctx.quantize_values, vv)):
+    for name, fn, xs in (("keys", ctx.quantize_keys, ks), ("values", ctx.quantize_values, vs)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            fn(x, 0, c)
+        for r in range(reps):
+            fn(xs[r % nbuf], 0, c)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        in_bytes = x.numel() * x.element_size()
-        res[name] = {"us_per_call": round(us, 2), "input_GBps": round(in_bytes / us / 1e3, 1)}
-    res["chunk"] = {"tokens_per_sequence": n, "batch": cfg.batch, "dtype": "fp32" if cfg.fp32_inputs else "bf16"}
+        res[name] = {"us_per_call": round(us, 2), "input_GBps": round(chunk_bytes / us / 1e3, 1)}
+    res["chunk"] = {"tokens_per_sequence": n, "batch": cfg.batch, "dtype": "fp32" if cfg.fp32_inputs else "bf16",
+                    "input_buffers": nbuf}
+    del ks, vs
     return res
 
 
