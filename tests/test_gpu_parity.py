@@ -131,6 +131,46 @@ def test_quantize_values_degenerate_tokens():
     ctx.close()
 
 
+@pytest.mark.parametrize("cid,kbits", [(2, 2), (2, 4), (1, 2), (1, 4)])
+def test_quantize_keys_degenerate_windows(cid, kbits):
+    """Key codes and metadata at the edges of the row-parallel Hadamard transform: an
+    all-zero window (m = +0, s = 0), a window of 32 identical tokens (zero range in every
+    channel), negative zeros, tokens near the bottom and the top of the fp32 range, and a
+    window with a single nonzero channel."""
+    import torch
+    cfg = synth.CONFIGS[cid]
+    n = 256
+    say(f"[codec-degenerate-keys] cfg{cid} K{kbits} n=256")
+    ctx, signs, U, lv = make_context(cfg, kbits, 2)
+    tags, k, v = _inputs(cfg, n)
+    k = k.copy()
+    k[:, 0:32] = 0.0                         # window 0: all zero
+    k[:, 32:64] = k[:, 32:33]                # window 1: identical tokens
+    k[:, 64:96] = np.where(k[:, 64:96] < 0, -0.0, k[:, 64:96])   # window 2: negative zeros
+    k[:, 64:70] = -0.0
+    k[:, 96:99] *= 1e-30                     # window 3: tiny tokens among ordinary ones
+    k[:, 128:130] *= 1e30                    # window 4: huge tokens
+    k[:, 160:192] = 0.0                      # window 5: one nonzero channel
+    k[:, 160:192, :, 7] = np.linspace(-3.0, 2.0, 32, dtype=np.float32)[None, :, None]
+    if not cfg.fp32_inputs:                  # what the bf16 path sees
+        k = torch.from_numpy(k).to(torch.bfloat16).float().numpy()
+    cache = ctx.alloc_cache(cfg.batch, n)
+    kd = torch.from_numpy(k).cuda() if cfg.fp32_inputs else bf16_tensor(k)
+    ctx.quantize_keys(kd, 0, cache)
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        kc, km, ks = O.quantize_keys(k, signs, kbits)
+    assert np.array_equal(from_dev(cache["k_min"], np.uint16), km)
+    assert np.array_equal(from_dev(cache["k_scale"], np.uint16), ks)
+    gk = from_dev(cache["k_codes"], np.uint32)
+    if not np.array_equal(gk, kc):
+        g = O.unpack_windows(gk, "key", cfg.head_dim, kbits)
+        o = O.unpack_windows(kc, "key", cfg.head_dim, kbits)
+        bad = np.argwhere(g != o)
+        raise AssertionError(f"{len(bad)} key codes differ, first at {bad[:4].tolist()}")
+    ctx.close()
+
+
 # ----------------------------------------------------------------------------- codec at full size, sampled
 @pytest.mark.parametrize("cid", [3, 5])
 def test_quantize_parity_prefill_sampled(cid):
