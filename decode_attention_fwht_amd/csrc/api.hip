@@ -314,7 +314,7 @@ omnikv_status omnikv_decode_workspace_size(const omnikv_ctx* ctx, int32_t batch,
 namespace {
 
 omnikv_status check_decode(const omnikv_ctx* ctx, int32_t batch, int64_t max_len, int64_t t_cap, int32_t num_splits,
-                           size_t workspace_bytes, omnikv::DecodePlan* plan) {
+                           size_t workspace_bytes, omnikv::DecodePlan* plan, bool stream = false) {
   if (batch <= 0) return fail(OMNIKV_EINVAL, "batch must be positive (got %d)", batch);
   if (t_cap <= 0 || t_cap % omnikv::kWindow) return fail(OMNIKV_EINVAL, "t_cap must be a positive multiple of 32");
   if (max_len < 0 || max_len > t_cap) return fail(OMNIKV_EINVAL, "max_len must be in [0, t_cap] (got %lld)", (long long)max_len);
@@ -326,7 +326,7 @@ omnikv_status check_decode(const omnikv_ctx* ctx, int32_t batch, int64_t max_len
       return fail(OMNIKV_EUNSUPPORTED, "t_cap %lld too large: one KV head's code blocks must stay below 2 GiB",
                   (long long)t_cap);
   }
-  *plan = omnikv::plan_decode(ctx->sh, batch, max_len, num_splits);
+  *plan = omnikv::plan_decode(ctx->sh, batch, max_len, num_splits, stream);
   if (workspace_bytes < plan->workspace_bytes)
     return fail(OMNIKV_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, plan->workspace_bytes);
   return OMNIKV_OK;
@@ -350,7 +350,7 @@ omnikv_status decode_partial(const omnikv_ctx* ctx, const float* q, const int32_
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(ctx->sh.d));
   const hipError_t e = omnikv::launch_decode_partial(ctx->sh, ctx->tb, plan, q, seq_lens, batch, max_len, k_codes, k_min,
                                                      k_scale, v_codes, v_scale, modality, t_cap, scale, workspace,
-                                                     false, stream);
+                                                     nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
   return OMNIKV_OK;
 }
@@ -491,25 +491,17 @@ omnikv_status omnikv_decode_attention_streaming(const omnikv_ctx* ctx, const flo
     return fail(OMNIKV_EINVAL, "ring_cap must be a multiple of 128 in [256, 512] (got %d)", ring_cap);
   if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale)) return fail(OMNIKV_EINVAL, "softmax_scale must be finite and >= 0");
   omnikv::DecodePlan plan;
-  if ((st = check_decode(ctx, batch, max_len, t_cap, num_splits, workspace_bytes, &plan)) != OMNIKV_OK) return st;
+  if ((st = check_decode(ctx, batch, max_len, t_cap, num_splits, workspace_bytes, &plan, true)) != OMNIKV_OK) return st;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(ctx->sh.d));
-  hipError_t e = omnikv::launch_decode_partial(ctx->sh, ctx->tb, plan, q, seq_lens, batch, max_len, k_codes, k_min,
-                                               k_scale, v_codes, v_scale, modality, t_cap, scale, workspace, true,
-                                               stream);
-  if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
   omnikv::StreamTail tail;
-  tail.q = q;
-  tail.seq_lens = seq_lens;
-  tail.max_len = max_len;
-  tail.k_codes = k_codes;
-  tail.k_min = k_min;
-  tail.k_scale = k_scale;
-  tail.t_cap = t_cap;
   tail.k_ring = k_ring;
   tail.v_ring = v_ring;
   tail.ring_f32 = ring_dtype == OMNIKV_F32;
   tail.ring_cap = ring_cap;
-  tail.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = omnikv::launch_decode_partial(ctx->sh, ctx->tb, plan, q, seq_lens, batch, max_len, k_codes, k_min,
+                                               k_scale, v_codes, v_scale, modality, t_cap, scale, workspace, &tail,
+                                               stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_partial launch");
   e = omnikv::launch_decode_combine(ctx->sh, ctx->tb, plan, seq_lens, batch, workspace, out, &tail, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_combine launch");
   return OMNIKV_OK;

@@ -34,6 +34,7 @@
 //   two packed codes (LDS, conflict-free for 2-bit).
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "omnikv_internal.h"
@@ -173,6 +174,12 @@ struct PartialArgs {
   uint32_t* ws_mask; // [unit][split] modalities present
   float* ws_acc;     // [unit][split][M][8][D]
   int stream;        // 1: attend over the value-packed prefix of each stream (the rest is recent)
+  // streamed sequences: workgroup `splits` of each unit scores the recent tokens instead
+  const void* k_ring;  // [B][ring_cap][Hkv][d], bf16 or fp32
+  const void* v_ring;
+  int ring_f32, ring_cap;
+  float2* tail_ml;   // [unit][8] (max, sum) of the recent tokens, log2 units
+  float* tail_o;     // [unit][8][D] their value sum in the original space, relative to the max
 };
 
 // ---------------------------------------------------------------------------------------
@@ -298,6 +305,170 @@ struct Lds {
   static_assert(TAB_OFF + TAB <= Slot<D, KB, VB>::BYTES, "staging must fit in one slot");
 };
 
+// The recent tokens [T0, n) of a streamed sequence (T0 = max(value-packed length, n -
+// ring_cap)), for the 8 query heads of one KV head at once, by one workgroup:
+//   scores in log2 units: a token below the key-packed length from its packed key with the
+//   rotated query (q_rot, already scaled by c_d and the softmax scale), a later one from its
+//   stored key with the query itself;
+//   then per head the max, the sum of 2^(s - max) and the value sum in the original space.
+// scratch: [8][D] original queries, then [8][kMaxRingCap] scores (dynamic LDS).
+template <int D, int KB>
+__device__ void stream_tail(const PartialArgs& a, const float (*q_rot)[D], float* scratch, int unit, int b,
+                            int kvh, int n) {
+  constexpr int T = kWaves * 64;
+  constexpr int PER_LANE = D * KB / 64;                     // words per block lane
+  constexpr int NW = (D == 128 && KB == 4) ? 4 : PER_LANE;  // words of one token half
+  constexpr int CPT = D / 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kp = static_cast<int>(stream_key_packed(n));
+  const int T0 = max(static_cast<int>(stream_value_packed(n)), n - a.ring_cap);
+  const int nt = max(0, n - T0);
+  float* qo = scratch;                 // [8][D]
+  float* sc = scratch + kMaxGroup * D; // [8][kMaxRingCap]
+  for (int i = tid; i < kMaxGroup * D; i += T) {
+    const int hh = i / D;
+    qo[i] = hh < a.group ? a.q[(static_cast<size_t>(b) * a.hq + kvh * a.group + hh) * D + i % D] : 0.0f;
+  }
+  __syncthreads();
+  // scores: eight threads per token, CPT consecutive channels each (one channel group g of
+  // the key window block, whose lane words 16 g + rho hold their codes), summed over the
+  // eight by row moves
+  const int64_t nwin_cap = a.t_cap / kWindow;
+  const int sub = tid & 7, c0 = sub * CPT;
+  const int g = c0 / (D / 4), sh2 = (c0 % (D / 4)) / 8;  // group, first 8-channel step
+  for (int j0 = 0; j0 < nt; j0 += T / 8) {
+    const int j = j0 + (tid >> 3);
+    float acc[kMaxGroup];
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] = 0.0f;
+    if (j < nt) {
+      const int t = T0 + j;
+      if (t < kp) {
+        const size_t wb = static_cast<size_t>(unit) * nwin_cap + t / kWindow;
+        const int tt = t % kWindow, tau = tt >> 4, rho = tt & 15;
+        const uint32_t* wp = a.k_codes + wb * (D * KB) + (16 * g + rho) * PER_LANE + ((D == 128 && KB == 4) ? 4 * tau : 0);
+        uint32_t w[NW];
+#pragma unroll
+        for (int x = 0; x < NW; ++x) w[x] = wp[x];
+        uint32_t mw[CPT / 2], sw[CPT / 2];
+#pragma unroll
+        for (int x = 0; x < CPT; x += 8) {
+          const uint4 m8 = *reinterpret_cast<const uint4*>(a.k_min + wb * D + c0 + x);
+          const uint4 s8 = *reinterpret_cast<const uint4*>(a.k_scale + wb * D + c0 + x);
+          mw[x / 2] = m8.x; mw[x / 2 + 1] = m8.y; mw[x / 2 + 2] = m8.z; mw[x / 2 + 3] = m8.w;
+          sw[x / 2] = s8.x; sw[x / 2 + 1] = s8.y; sw[x / 2 + 2] = s8.z; sw[x / 2 + 3] = s8.w;
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+          const int jj = cc & 7, i = jj >> 1, e = jj & 1, s8i = sh2 + (cc >> 3);
+          uint32_t word, bit;
+          if (D == 128 && KB == 2) { word = w[i]; bit = 16 * e + 2 * (4 * tau + s8i); }
+          else if (D == 128) { word = w[i]; bit = 16 * e + 4 * s8i; }
+          else if (KB == 2) { word = w[i & 1]; bit = 16 * e + 2 * (4 * (i >> 1) + 2 * tau + s8i); }
+          else { word = w[i]; bit = 16 * e + 4 * (2 * tau + s8i); }
+          const float code = static_cast<float>((word >> bit) & ((1u << KB) - 1u));
+          const float mv = f16_value(static_cast<uint16_t>(mw[cc >> 1] >> (16 * (cc & 1))));
+          const float sv = f16_value(static_cast<uint16_t>(sw[cc >> 1] >> (16 * (cc & 1))));
+          const float kval = mv + sv * code;
+#pragma unroll
+          for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] = fmaf(q_rot[hh][c0 + cc], kval, acc[hh]);
+        }
+      } else {
+        const size_t row = ((static_cast<size_t>(b) * a.ring_cap + t % a.ring_cap) * a.hkv + kvh) * D + c0;
+        float kv[CPT];
+        if (a.ring_f32) {
+#pragma unroll
+          for (int x = 0; x < CPT; x += 4) {
+            const float4 k4 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k_ring) + row + x);
+            kv[x] = k4.x; kv[x + 1] = k4.y; kv[x + 2] = k4.z; kv[x + 3] = k4.w;
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < CPT; x += 8) {
+            const uint4 k8 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_ring) + row + x);
+            const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
+#pragma unroll
+            for (int y = 0; y < 8; ++y) kv[x + y] = __uint_as_float((y & 1) ? (kw[y >> 1] & 0xFFFF0000u) : (kw[y >> 1] << 16));
+          }
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc)
+#pragma unroll
+          for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] = fmaf(qo[hh * D + c0 + cc], kv[cc], acc[hh]);
+#pragma unroll
+        for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] *= a.scale_log2;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+      acc[hh] += __shfl_xor(acc[hh], 1, 64);
+      acc[hh] += __shfl_xor(acc[hh], 2, 64);
+      acc[hh] += __shfl_xor(acc[hh], 4, 64);
+    }
+    if (j < nt && sub == 0) {
+#pragma unroll
+      for (int hh = 0; hh < kMaxGroup; ++hh) sc[hh * kMaxRingCap + j] = acc[hh];
+    }
+  }
+  __syncthreads();
+  // per head (wave w: heads 2w, 2w + 1): max, probabilities in place, their sum
+  __shared__ float2 tml[kMaxGroup];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int hh = 2 * wave + x;
+    float m = -INFINITY;
+    for (int j = lane; j < nt; j += 64) m = fmaxf(m, sc[hh * kMaxRingCap + j]);
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1) m = fmaxf(m, __shfl_xor(m, st, 64));
+    float l = 0.0f;
+    for (int j = lane; j < nt; j += 64) {
+      const float p = exp2f(sc[hh * kMaxRingCap + j] - m);
+      sc[hh * kMaxRingCap + j] = p;
+      l += p;
+    }
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1) l += __shfl_xor(l, st, 64);
+    if (lane == 0) tml[hh] = make_float2(m, nt > 0 ? l : 0.0f);
+  }
+  __syncthreads();
+  // value sums in the original space: thread (c, head quarter), 8 / (T / D) heads each
+  constexpr int HPT = kMaxGroup * D / T;
+  const int c = tid % D, hq0 = (tid / D) * HPT;
+  float o[HPT];
+#pragma unroll
+  for (int x = 0; x < HPT; ++x) o[x] = 0.0f;
+  // 32 tokens' values are loaded together (past the last token: the last token again, with
+  // weight zero), without branches, so the loads are in flight at once
+  constexpr int VBT = 32;
+  const size_t vrow0 = (static_cast<size_t>(b) * a.ring_cap * a.hkv + kvh) * D + c;
+  const size_t vstride = static_cast<size_t>(a.hkv) * D;  // elements per ring row
+  for (int j0 = 0; j0 < nt; j0 += VBT) {
+    float vv[VBT];
+    if (a.ring_f32) {
+#pragma unroll
+      for (int y = 0; y < VBT; ++y) {
+        const int t = T0 + min(j0 + y, nt - 1);
+        vv[y] = static_cast<const float*>(a.v_ring)[vrow0 + static_cast<size_t>(t % a.ring_cap) * vstride];
+      }
+    } else {
+#pragma unroll
+      for (int y = 0; y < VBT; ++y) {
+        const int t = T0 + min(j0 + y, nt - 1);
+        vv[y] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.v_ring)[vrow0 + static_cast<size_t>(t % a.ring_cap) * vstride]) << 16);
+      }
+    }
+#pragma unroll
+    for (int y = 0; y < VBT; ++y) {
+      const bool ok = j0 + y < nt;
+#pragma unroll
+      for (int x = 0; x < HPT; ++x) o[x] = fmaf(ok ? sc[(hq0 + x) * kMaxRingCap + j0 + y] : 0.0f, vv[y], o[x]);
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < HPT; ++x) a.tail_o[(static_cast<size_t>(unit) * kMaxGroup + hq0 + x) * D + c] = o[x];
+  if (tid < kMaxGroup) a.tail_ml[static_cast<size_t>(unit) * kMaxGroup + tid] = tml[tid];
+}
+
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kernel(PartialArgs a) {
   using SG = Slot<D, KB, VB>;
@@ -413,6 +584,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     for (int i = lane; i < (1 << (2 * VB)); i += 64) vtab[i] = t[i];
   }
   len = static_cast<int>(min<int64_t>(max(len, 0), a.max_len));
+  const int len_streamed = len;
   if (a.stream) len = stream_value_packed(len);
   const int nwin = (len + kWindow - 1) / kWindow;
   const int wend = min(nwin, wbeg + a.wpw);
@@ -512,6 +684,16 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     for (int s = 0; s < NS; ++s) bqa_lds[s * 64 + lane] = bqa[s];
   }
   __syncthreads();
+
+  // ---- streamed sequences: the extra workgroup of the unit takes the recent tokens
+  if (a.stream && static_cast<int>(blockIdx.x) == a.splits) {
+    static_assert(kBqaInRegs, "the recent tokens read the rotated queries from q_lds");
+    // the split workgroups sharing this CU raise their priority while they start: this short
+    // one takes the highest too, or it would only get their leftover issue slots
+    __builtin_amdgcn_s_setprio(3);
+    stream_tail<D, KB>(a, q_lds, reinterpret_cast<float*>(ring_mem), unit, b, kvh, len_streamed);
+    return;
+  }
 
   // ---- running state.  Scores, l_part and the accumulators are relative to m_ref (per
   // column, log2 units).  The value contraction's 16 columns are the 8 heads of two
@@ -858,17 +1040,10 @@ struct CombineArgs {
   const uint32_t* ws_mask;
   const float* ws_acc;
   float* out;
-  // streamed sequences only: the recent tokens
-  const float* signs;        // [d] the key rotation's D
-  int kbits;
-  StreamTail tail;
+  // streamed sequences only: the recent tokens' partial, original space
+  const float2* tail_ml;     // [unit][8]
+  const float* tail_o;       // [unit][8][D]
 };
-
-__device__ inline float ring_elem(const void* ring, size_t idx, bool f32) {
-  if (f32) return static_cast<const float*>(ring)[idx];
-  return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(ring)[idx]) << 16);
-}
-__device__ inline float f16_to_float(uint16_t bits) { return static_cast<float>(__builtin_bit_cast(_Float16, bits)); }
 
 // One block per (query head, sequence x KV head).  Every global load that depends on
 // nothing is issued first - all of this thread's rotation rows, the first batch of split
@@ -876,14 +1051,15 @@ __device__ inline float f16_to_float(uint16_t bits) { return static_cast<float>(
 // memory about once.  Every wave derives the split weights itself (no barrier for them).
 // (1) log-sum-exp merge of the splits' rotated-space accumulators, one (m, k) item per
 // thread, into LDS; (2) out = sum_m U_m A_m, each thread a column c over one group of
-// stacked (m, k) rows, the groups summed through LDS, then normalised.
+// stacked (m, k) rows, the groups summed through LDS, then normalised.  For streamed
+// sequences the recent tokens' partial (max, sum, value sums in the original space) joins
+// the merge and is added after the rotation.
 constexpr int kCombineThreads = 1024;
 constexpr int kCombineXB = 32;    // splits per batch of accumulator loads
 constexpr int kMaxSplits = 1024;  // splits per (sequence, KV head)
 
-constexpr int kMaxRing = kMaxRingCap;
 
-template <int D, int KB, bool STREAM>
+template <int D, bool STREAM>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a) {
   constexpr int J = kMaxModalities * D;       // stacked rotation rows (m, k)
   constexpr int KQ = kCombineThreads / D;     // row groups
@@ -892,7 +1068,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   constexpr int PSTRIDE = kMaxModalities * kMaxGroup * D;  // floats per split
   __shared__ __attribute__((aligned(16))) float A[J];
   __shared__ float red[KQ][D];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int h = blockIdx.x, unit = blockIdx.y;
   if (h >= a.group) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
@@ -901,8 +1077,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   const int c = tid % D, kq = tid / D;
   const int jrows = a.modalities * D;
 
-  // ---- loads that depend on nothing (for streamed sequences they follow the recent
-  // tokens' scores, whose registers they would otherwise crowd)
+  // ---- loads that depend on nothing
   const int j0 = kq * JPG;
   const float* up = a.rotations_t + static_cast<size_t>(j0) * D + c;
   const bool merger = tid < jrows;  // item (m, k) = (tid / D, tid % D)
@@ -913,138 +1088,22 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   // lane t: split t's (max, sum) and modality mask (splits 64.. are read in the loop)
   float2 ml0 = make_float2(-INFINITY, 0.0f);
   uint32_t mk0 = 0u;
-  auto issue_loads = [&]() {
 #pragma unroll
-    for (int i = 0; i < JPG; ++i) u[i] = (j0 + i < jrows) ? up[static_cast<size_t>(i) * D] : 0.0f;
+  for (int i = 0; i < JPG; ++i) u[i] = (j0 + i < jrows) ? up[static_cast<size_t>(i) * D] : 0.0f;
 #pragma unroll
-    for (int t = 0; t < kCombineXB; ++t) x[t] = (merger && t < S) ? src[static_cast<size_t>(t) * PSTRIDE] : 0.0f;
-    if (lane < S) {
-      ml0 = a.ws_ml[(base + lane) * kMaxGroup + h];
-      mk0 = a.ws_mask[base + lane];
-    }
-  };
-  if constexpr (!STREAM) issue_loads();
-
-  // ---- streamed sequences: scores of the recent tokens [T0, len) in log2 units.  A
-  // token below the key-packed length uses its packed key with the rotated query (the
-  // codec's butterflies), a later one its stored key with the query itself.
-  __shared__ float tsc[STREAM ? kMaxRing : 1];
-  __shared__ float qo[STREAM ? D : 1], qr[STREAM ? D : 1];
-  __shared__ float tred[kCombineThreads / 64];
-  __shared__ float tstat;
-  int T0 = 0, nt = 0;
-  float tmx = -INFINITY;
-  if constexpr (STREAM) {
-    const StreamTail& st = a.tail;
-    const int len = static_cast<int>(min<int64_t>(max<int64_t>(st.seq_lens[b], 0), st.max_len));
-    const int Pk = static_cast<int>(stream_key_packed(len));
-    T0 = max(static_cast<int>(stream_value_packed(len)), len - st.ring_cap);
-    nt = len - T0;
-    if (tid < D) {
-      const float qv = st.q[(static_cast<size_t>(b) * a.hq + kvh * a.group + h) * D + tid];
-      qo[tid] = qv;
-      qr[tid] = qv * a.signs[tid];
-    }
-    __syncthreads();
-    if (T0 < Pk) {
-      for (int hh = 1; hh < D; hh <<= 1) {
-        if (tid < D / 2) {
-          const int i = (tid / hh) * 2 * hh + (tid % hh);
-          const float x0 = qr[i], x1 = qr[i + hh];
-          qr[i] = x0 + x1;
-          qr[i + hh] = x0 - x1;
-        }
-        __syncthreads();
-      }
-    }
-    // Eight threads per token, CPT consecutive channels each; all of a thread's channels
-    // lie in one channel group g of the key window block, whose lane words (16 g + rho)
-    // hold their codes (the block layout of the cache description).
-    constexpr int CPT = D / 8;
-    constexpr int PER_LANE = D * KB / 64;                  // words per block lane
-    constexpr int NW = (D == 128 && KB == 4) ? 4 : PER_LANE;  // words of one token half
-    const int sub = tid & 7, c0 = sub * CPT;
-    const int g = c0 / (D / 4), sh2 = (c0 % (D / 4)) / 8;  // group, first 8-channel step
-    for (int j0 = 0; j0 < nt; j0 += kCombineThreads / 8) {
-      const int j = j0 + (tid >> 3);
-      float acc = 0.0f;
-      if (j < nt) {
-        const int t = T0 + j;
-        if (t < Pk) {
-          const size_t wb = static_cast<size_t>(unit) * (st.t_cap / kWindow) + t / kWindow;
-          const int tt = t % kWindow, tau = tt >> 4, rho = tt & 15;
-          const uint32_t* wp = st.k_codes + wb * (D * KB) + (16 * g + rho) * PER_LANE + ((D == 128 && KB == 4) ? 4 * tau : 0);
-          uint32_t w[NW];
-#pragma unroll
-          for (int x = 0; x < NW; ++x) w[x] = wp[x];
-          uint16_t mv[CPT], sv[CPT];
-#pragma unroll
-          for (int x = 0; x < CPT; x += 8) {
-            const uint4 m8 = *reinterpret_cast<const uint4*>(st.k_min + wb * D + c0 + x);
-            const uint4 s8 = *reinterpret_cast<const uint4*>(st.k_scale + wb * D + c0 + x);
-            const uint32_t mw[4] = {m8.x, m8.y, m8.z, m8.w}, sw[4] = {s8.x, s8.y, s8.z, s8.w};
-#pragma unroll
-            for (int y = 0; y < 8; ++y) {
-              mv[x + y] = static_cast<uint16_t>(mw[y >> 1] >> (16 * (y & 1)));
-              sv[x + y] = static_cast<uint16_t>(sw[y >> 1] >> (16 * (y & 1)));
-            }
-          }
-#pragma unroll
-          for (int cc = 0; cc < CPT; ++cc) {
-            const int jj = cc & 7, i = jj >> 1, e = jj & 1, s8 = sh2 + (cc >> 3);
-            uint32_t word, bit;
-            if (D == 128 && KB == 2) { word = w[i]; bit = 16 * e + 2 * (4 * tau + s8); }
-            else if (D == 128) { word = w[i]; bit = 16 * e + 4 * s8; }
-            else if (KB == 2) { word = w[i & 1]; bit = 16 * e + 2 * (4 * (i >> 1) + 2 * tau + s8); }
-            else { word = w[i]; bit = 16 * e + 4 * (2 * tau + s8); }
-            const float code = static_cast<float>((word >> bit) & ((1u << KB) - 1u));
-            acc = fmaf(qr[c0 + cc], f16_to_float(mv[cc]) + f16_to_float(sv[cc]) * code, acc);
-          }
-          acc *= RhtConst<D>::value;
-        } else {
-          const size_t row = ((static_cast<size_t>(b) * st.ring_cap + t % st.ring_cap) * a.hkv + kvh) * D + c0;
-          if (st.ring_f32) {
-#pragma unroll
-            for (int x = 0; x < CPT; x += 4) {
-              const float4 k4 = *reinterpret_cast<const float4*>(static_cast<const float*>(st.k_ring) + row + x);
-              acc = fmaf(qo[c0 + x], k4.x, acc);
-              acc = fmaf(qo[c0 + x + 1], k4.y, acc);
-              acc = fmaf(qo[c0 + x + 2], k4.z, acc);
-              acc = fmaf(qo[c0 + x + 3], k4.w, acc);
-            }
-          } else {
-#pragma unroll
-            for (int x = 0; x < CPT; x += 8) {
-              const uint4 k8 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(st.k_ring) + row + x);
-              const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
-#pragma unroll
-              for (int y = 0; y < 8; ++y)
-                acc = fmaf(qo[c0 + x + y], __uint_as_float((y & 1) ? (kw[y >> 1] & 0xFFFF0000u) : (kw[y >> 1] << 16)), acc);
-            }
-          }
-        }
-      }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
-      if (j < nt && sub == 0) tsc[j] = acc * st.scale_log2;
-    }
-    __syncthreads();
-    float lm = -INFINITY;
-    for (int j = tid; j < nt; j += kCombineThreads) lm = fmaxf(lm, tsc[j]);
-#pragma unroll
-    for (int sx = 32; sx >= 1; sx >>= 1) lm = fmaxf(lm, __shfl_xor(lm, sx, 64));
-    if (lane == 0) tred[wv] = lm;
-    __syncthreads();
-    if (tid == 0) {
-      float m = -INFINITY;
-      for (int x = 0; x < kCombineThreads / 64; ++x) m = fmaxf(m, tred[x]);
-      tstat = m;
-    }
-    __syncthreads();
-    tmx = tstat;
-    issue_loads();
+  for (int t = 0; t < kCombineXB; ++t) x[t] = (merger && t < S) ? src[static_cast<size_t>(t) * PSTRIDE] : 0.0f;
+  if (lane < S) {
+    ml0 = a.ws_ml[(base + lane) * kMaxGroup + h];
+    mk0 = a.ws_mask[base + lane];
   }
+  // streamed sequences: the recent tokens' (max, sum) and, for row group 0, value sums
+  float2 tml = make_float2(-INFINITY, 0.0f);
+  float to = 0.0f;
+  if constexpr (STREAM) {
+    tml = a.tail_ml[static_cast<size_t>(unit) * kMaxGroup + h];
+    if (kq == 0) to = a.tail_o[(static_cast<size_t>(unit) * kMaxGroup + h) * D + c];
+  }
+  const float tmx = tml.y > 0.0f ? tml.x : -INFINITY;
 
   // ---- largest split max (every wave alike)
   float mx = ml0.y > 0.0f ? ml0.x : -INFINITY;
@@ -1106,26 +1165,11 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   // are in the original space (added after the inverse rotation)
   float ot = 0.0f;
   if constexpr (STREAM) {
-    const StreamTail& st = a.tail;
-    float ls = 0.0f;
-    for (int j = tid; j < nt; j += kCombineThreads) {
-      const float p = exp2f(tsc[j] - mx);
-      tsc[j] = p;
-      ls += p;
+    if (tml.y > 0.0f) {
+      const float wt = exp2f(tml.x - mx);
+      lsum += wt * tml.y;
+      ot = wt * to;
     }
-#pragma unroll
-    for (int sx = 32; sx >= 1; sx >>= 1) ls += __shfl_xor(ls, sx, 64);
-    __syncthreads();  // tred reads of the max are done; tsc holds probabilities
-    if (lane == 0) tred[wv] = ls;
-    for (int j = kq; j < nt; j += KQ) {
-      const int t = T0 + j;
-      const size_t idx = ((static_cast<size_t>(b) * st.ring_cap + t % st.ring_cap) * a.hkv + kvh) * D + c;
-      ot = fmaf(tsc[j], ring_elem(st.v_ring, idx, st.ring_f32), ot);
-    }
-    __syncthreads();
-    float tl = 0.0f;
-    for (int x = 0; x < kCombineThreads / 64; ++x) tl += tred[x];
-    lsum += tl;
   }
   const float inv_l = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   __syncthreads();
@@ -1156,9 +1200,13 @@ struct WorkspaceView {
   float2* ml;
   uint32_t* mask;
   float* acc;
+  float2* tail_ml;  // streamed sequences: [unit][8]
+  float* tail_o;    // [unit][8][d]
 };
 
-WorkspaceView carve(const void* ws, size_t parts, int d) {
+// [ml | mask | acc | tail_ml | tail_o], each 256-byte aligned
+WorkspaceView carve(const void* ws, size_t units, size_t splits, int d) {
+  const size_t parts = units * splits;
   char* w = static_cast<char*>(const_cast<void*>(ws));
   WorkspaceView v;
   v.ml = reinterpret_cast<float2*>(w);
@@ -1166,16 +1214,21 @@ WorkspaceView carve(const void* ws, size_t parts, int d) {
   v.mask = reinterpret_cast<uint32_t*>(w);
   w += align256(parts * sizeof(uint32_t));
   v.acc = reinterpret_cast<float*>(w);
+  w += align256(parts * kMaxModalities * kMaxGroup * d * sizeof(float));
+  v.tail_ml = reinterpret_cast<float2*>(w);
+  w += align256(units * kMaxGroup * sizeof(float2));
+  v.tail_o = reinterpret_cast<float*>(w);
   return v;
 }
 
 }  // namespace
 
-DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested) {
+DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested, bool stream) {
   // A split is one workgroup of kWaves waves; each wave takes wpw consecutive windows
-  // and the block merges its waves' partials before writing one.  Default: one wave per
-  // SIMD slot the kernel's resources allow (256 CUs x 4 SIMDs x kBlocksPerCU), with at
-  // least 8 windows per wave.
+  // and the block merges its waves' partials before writing one.  Default: as many
+  // workgroups as the kernel's resources let run at once (256 CUs x kBlocksPerCU), so no
+  // workgroup waits for another to finish, with at least 8 windows per wave; streamed
+  // sequences keep one of those places per (sequence, KV head) for the recent tokens.
   DecodePlan p{};
   const int64_t nwin = (max_len + kWindow - 1) / kWindow;
   const int64_t units = static_cast<int64_t>(batch) * sh.hkv;
@@ -1183,8 +1236,8 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
   if (requested > 0) {
     want = requested;
   } else {
-    const int64_t target_waves = 256 * 4 * kBlocksPerCU;
-    want = (target_waves / kWaves + units - 1) / units;
+    const int64_t slots = 256 * kBlocksPerCU;
+    want = slots / units - (stream ? 1 : 0);
     want = std::min<int64_t>(want, std::max<int64_t>(1, (nwin + 8 * kWaves - 1) / (8 * kWaves)));
   }
   want = std::max<int64_t>(1, std::min<int64_t>({want, std::max<int64_t>(1, nwin), static_cast<int64_t>(kMaxSplits)}));
@@ -1195,7 +1248,9 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
   p.windows_per_wave = static_cast<int>(wpw);
   const size_t parts = static_cast<size_t>(units) * splits;
   p.workspace_bytes = align256(parts * kMaxGroup * sizeof(float2)) + align256(parts * sizeof(uint32_t)) +
-                      align256(parts * kMaxModalities * kMaxGroup * sh.d * sizeof(float));
+                      align256(parts * kMaxModalities * kMaxGroup * sh.d * sizeof(float)) +
+                      align256(static_cast<size_t>(units) * kMaxGroup * sizeof(float2)) +
+                      align256(static_cast<size_t>(units) * kMaxGroup * sh.d * sizeof(float));
   return p;
 }
 
@@ -1204,19 +1259,28 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
                                    const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
                                    const uint32_t* kc, const uint16_t* km, const uint16_t* ks,
                                    const uint32_t* vc, const uint16_t* vs, const uint8_t* mod,
-                                   int64_t t_cap, float scale, void* ws, bool stream, hipStream_t st) {
-  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits, sh.d);
+                                   int64_t t_cap, float scale, void* ws, const StreamTail* tail, hipStream_t st) {
+  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv, plan.splits, sh.d);
   PartialArgs pa{q, seq_lens, kc, km, ks, vc, vs, mod, tb.signs, tb.pair_table, sh.hq, sh.hkv, sh.group,
                  sh.modalities, t_cap, max_len, scale * 1.4426950408889634f, plan.windows_per_wave, plan.splits,
-                 w.ml, w.mask, w.acc, stream ? 1 : 0};
-  const dim3 grid(static_cast<unsigned>(plan.splits), static_cast<unsigned>(batch * sh.hkv));
+                 w.ml, w.mask, w.acc, tail ? 1 : 0,
+                 tail ? tail->k_ring : nullptr, tail ? tail->v_ring : nullptr, tail && tail->ring_f32 ? 1 : 0,
+                 tail ? tail->ring_cap : 0, w.tail_ml, w.tail_o};
+  // streamed sequences: one more workgroup per unit for the recent tokens
+  const dim3 grid(static_cast<unsigned>(plan.splits + (tail ? 1 : 0)), static_cast<unsigned>(batch * sh.hkv));
   constexpr size_t dyn_bytes = Lds<D, KB, VB>::DYN;
-  static bool attr_set = false;  // dynamic LDS above the 64 KB default needs the attribute
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, KB, VB>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn_bytes));
+  // dynamic LDS above the 64 KB default needs the attribute, once per device (setting it
+  // twice from two threads is harmless)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit == 0 || !(attr_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, KB, VB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn_bytes));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   decode_partial_kernel<D, KB, VB><<<grid, kWaves * 64, dyn_bytes, st>>>(pa);
   return hipGetLastError();
@@ -1225,12 +1289,12 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
 hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan, const float* q,
                                  const int32_t* seq_lens, int batch, int64_t max_len, const uint32_t* kc,
                                  const uint16_t* km, const uint16_t* ks, const uint32_t* vc, const uint16_t* vs,
-                                 const uint8_t* mod, int64_t t_cap, float scale, void* ws, bool stream,
+                                 const uint8_t* mod, int64_t t_cap, float scale, void* ws, const StreamTail* tail,
                                  hipStream_t st) {
 #define OMNIKV_DEC(D_, KB_, VB_)                                                                           \
   if (sh.d == D_ && sh.kbits == KB_ && sh.vbits == VB_)                                                    \
     return launch_partial_t<D_, KB_, VB_>(sh, tb, plan, q, seq_lens, batch, max_len, kc, km, ks, vc, vs, mod, \
-                                          t_cap, scale, ws, stream, st);
+                                          t_cap, scale, ws, tail, st);
   OMNIKV_DEC(128, 2, 2)
   OMNIKV_DEC(128, 4, 4)
   OMNIKV_DEC(128, 2, 4)
@@ -1246,20 +1310,17 @@ hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const 
 hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
                                  const int32_t* seq_lens, int batch, const void* ws, float* out,
                                  const StreamTail* tail, hipStream_t st) {
-  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv * plan.splits, sh.d);
+  const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv, plan.splits, sh.d);
   CombineArgs ca{tb.rotations_t, sh.hq, sh.hkv, sh.group, sh.modalities, plan.splits, w.ml, w.mask, w.acc, out,
-                 tb.signs, sh.kbits, tail ? *tail : StreamTail{}};
+                 w.tail_ml, w.tail_o};
   (void)seq_lens;
   const dim3 grid(static_cast<unsigned>(sh.group), static_cast<unsigned>(batch * sh.hkv));
-  const bool k4 = sh.kbits == 4;
   if (sh.d == 128) {
-    if (!tail) decode_combine_kernel<128, 2, false><<<grid, kCombineThreads, 0, st>>>(ca);
-    else if (k4) decode_combine_kernel<128, 4, true><<<grid, kCombineThreads, 0, st>>>(ca);
-    else decode_combine_kernel<128, 2, true><<<grid, kCombineThreads, 0, st>>>(ca);
+    if (!tail) decode_combine_kernel<128, false><<<grid, kCombineThreads, 0, st>>>(ca);
+    else decode_combine_kernel<128, true><<<grid, kCombineThreads, 0, st>>>(ca);
   } else {
-    if (!tail) decode_combine_kernel<64, 2, false><<<grid, kCombineThreads, 0, st>>>(ca);
-    else if (k4) decode_combine_kernel<64, 4, true><<<grid, kCombineThreads, 0, st>>>(ca);
-    else decode_combine_kernel<64, 2, true><<<grid, kCombineThreads, 0, st>>>(ca);
+    if (!tail) decode_combine_kernel<64, false><<<grid, kCombineThreads, 0, st>>>(ca);
+    else decode_combine_kernel<64, true><<<grid, kCombineThreads, 0, st>>>(ca);
   }
   return hipGetLastError();
 }

@@ -68,36 +68,31 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 
-DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested_splits);
+// stream: the plan of omnikv_decode_attention_streaming (one workgroup per (sequence, KV
+// head) more, for the recent tokens)
+DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested_splits, bool stream = false);
 
-// stream = true: each sequence's seq_lens value is a streamed length n, and only its
-// value-packed prefix (tokens below stream_value_packed(n)) is attended here.
-hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
-                                 const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
-                                 const uint32_t* k_codes, const uint16_t* k_min, const uint16_t* k_scale,
-                                 const uint32_t* v_codes, const uint16_t* v_scale, const uint8_t* modality,
-                                 int64_t t_cap, float softmax_scale, void* workspace, bool stream,
-                                 hipStream_t stream_handle);
-
-// The recent (unquantized) tokens of streamed sequences, attended inside the combine:
-// keys of tokens [stream_key_packed(n), n) and values of [stream_value_packed(n), n) come
-// from the rings (token t at row t % ring_cap); older keys of the recent span come from
-// the packed cache.
+// The recent (unquantized) tokens of streamed sequences: keys of tokens
+// [stream_key_packed(n), n) and values of [stream_value_packed(n), n) come from the rings
+// (token t at row t % ring_cap); older keys of the recent span come from the packed cache.
 struct StreamTail {
-  const float* q = nullptr;          // [B][Hq][d]
-  const int32_t* seq_lens = nullptr; // [B] streamed lengths
-  int64_t max_len = 0;
-  const uint32_t* k_codes = nullptr;
-  const uint16_t* k_min = nullptr;
-  const uint16_t* k_scale = nullptr;
-  int64_t t_cap = 0;
   const void* k_ring = nullptr;      // [B][ring_cap][Hkv][d], bf16 or fp32
   const void* v_ring = nullptr;
   bool ring_f32 = false;
   int ring_cap = 0;
-  float scale_log2 = 0.0f;           // softmax scale * log2(e)
 };
 
+// tail != nullptr: each sequence's seq_lens value is a streamed length n; the split
+// workgroups attend over its value-packed prefix (tokens below stream_value_packed(n)) and
+// one more workgroup per (sequence, KV head) over the recent tokens.
+hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
+                                 const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
+                                 const uint32_t* k_codes, const uint16_t* k_min, const uint16_t* k_scale,
+                                 const uint32_t* v_codes, const uint16_t* v_scale, const uint8_t* modality,
+                                 int64_t t_cap, float softmax_scale, void* workspace, const StreamTail* tail,
+                                 hipStream_t stream_handle);
+
+// tail != nullptr: the recent tokens' partial (written by the partial launch) joins the merge.
 hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
                                  const int32_t* seq_lens, int batch, const void* workspace, float* out,
                                  const StreamTail* tail, hipStream_t stream);
