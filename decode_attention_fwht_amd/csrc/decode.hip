@@ -170,6 +170,7 @@ struct PartialArgs {
   int64_t max_len;   // host bound of seq_lens; device lengths are clamped to it
   float scale_log2;  // softmax scale * log2(e)
   int wpw, splits;   // windows per wave; splits (= workgroups) per (sequence, KV head)
+  int split_old, wpw_young;  // splits [split_old, splits) take wpw_young windows per wave
   float2* ws_ml;     // [unit][split][8] (max, sum) in log2 units
   uint32_t* ws_mask; // [unit][split] modalities present
   float* ws_acc;     // [unit][split][M][8][D]
@@ -495,10 +496,15 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int unit = blockIdx.y;                     // b * hkv + kvh
+  const int unit = blockIdx.x;                     // b * hkv + kvh
+  const int split = blockIdx.y;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
   const int h0 = 2 * wave;                         // this wave's two query heads
-  const int wbeg = (blockIdx.x * kWaves + wave) * a.wpw;  // this wave's run of windows
+  // this wave's run of windows: splits below split_old (dispatched first, so older on
+  // their SIMDs) take wpw windows per wave, the later ones wpw_young
+  const int wbeg = split < a.split_old ? (split * kWaves + wave) * a.wpw
+                                       : a.split_old * kWaves * a.wpw + ((split - a.split_old) * kWaves + wave) * a.wpw_young;
+  const int my_wpw = split < a.split_old ? a.wpw : a.wpw_young;
 
   // ---- first copies, before anything waits for memory: this wave's two heads of the
   // query, the signs of D, the level-pair table (wave 0), then the first windows.  The
@@ -572,7 +578,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   {
     const int64_t bound = a.stream ? stream_value_packed(a.max_len) : a.max_len;
     const int nwin_bound = static_cast<int>((bound + kWindow - 1) / kWindow);
-    issue_upto(min(max(0, min(nwin_bound, wbeg + a.wpw) - wbeg), RING - 1));
+    issue_upto(min(max(0, min(nwin_bound, wbeg + my_wpw) - wbeg), RING - 1));
   }
 
   // ---- the staging copies (issued before any window's) have landed: the sequence's
@@ -587,7 +593,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   const int len_streamed = len;
   if (a.stream) len = stream_value_packed(len);
   const int nwin = (len + kWindow - 1) / kWindow;
-  const int wend = min(nwin, wbeg + a.wpw);
+  const int wend = min(nwin, wbeg + my_wpw);
   const int nw = max(0, wend - wbeg);
   float qv[2][NC];
   {
@@ -686,7 +692,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   __syncthreads();
 
   // ---- streamed sequences: the extra workgroup of the unit takes the recent tokens
-  if (a.stream && static_cast<int>(blockIdx.x) == a.splits) {
+  if (a.stream && split == a.splits) {
     static_assert(kBqaInRegs, "the recent tokens read the rotated queries from q_lds");
     // the split workgroups sharing this CU raise their priority while they start: this short
     // one takes the highest too, or it would only get their leftover issue slots
@@ -994,7 +1000,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     stage(2, accA, 1);
   }
   __syncthreads();
-  const size_t pidx = static_cast<size_t>(unit) * a.splits + blockIdx.x;
+  const size_t pidx = static_cast<size_t>(unit) * a.splits + split;
   uint32_t present = 0u;
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) present |= seen_lds[v];
@@ -1223,6 +1229,8 @@ WorkspaceView carve(const void* ws, size_t units, size_t splits, int d) {
 
 }  // namespace
 
+constexpr int64_t kOldShareNum = 570, kOldShareDen = 1000;  // the older half's share of the windows
+
 DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requested, bool stream) {
   // A split is one workgroup of kWaves waves; each wave takes wpw consecutive windows
   // and the block merges its waves' partials before writing one.  Default: as many
@@ -1246,6 +1254,21 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
   const int64_t splits = (waves + kWaves - 1) / kWaves;
   p.splits = static_cast<int>(splits);
   p.windows_per_wave = static_cast<int>(wpw);
+  p.split_old = 0;
+  p.wpw_young = static_cast<int>(wpw);
+  // The launch is split-major: the workgroups of splits below 256 / units are dispatched
+  // first, one per CU, and the SIMD arbiter favours their waves over the later ones that
+  // share the CU.  With a full machine they take a larger share of the windows, so the two
+  // finish together.
+  const int64_t old = 256 / units;
+  if (requested <= 0 && old >= 1 && old < splits && splits * units >= 2 * 256 - units) {
+    const int64_t wo = std::max<int64_t>(1, (nwin * kOldShareNum + kWaves * old * kOldShareDen - 1) / (kWaves * old * kOldShareDen));
+    const int64_t rest = std::max<int64_t>(0, nwin - kWaves * old * wo);
+    const int64_t wy = (rest + kWaves * (splits - old) - 1) / (kWaves * (splits - old));
+    p.split_old = static_cast<int>(old);
+    p.windows_per_wave = static_cast<int>(wo);
+    p.wpw_young = static_cast<int>(wy);
+  }
   const size_t parts = static_cast<size_t>(units) * splits;
   p.workspace_bytes = align256(parts * kMaxGroup * sizeof(float2)) + align256(parts * sizeof(uint32_t)) +
                       align256(parts * kMaxModalities * kMaxGroup * sh.d * sizeof(float)) +
@@ -1263,11 +1286,11 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
   const WorkspaceView w = carve(ws, static_cast<size_t>(batch) * sh.hkv, plan.splits, sh.d);
   PartialArgs pa{q, seq_lens, kc, km, ks, vc, vs, mod, tb.signs, tb.pair_table, sh.hq, sh.hkv, sh.group,
                  sh.modalities, t_cap, max_len, scale * 1.4426950408889634f, plan.windows_per_wave, plan.splits,
-                 w.ml, w.mask, w.acc, tail ? 1 : 0,
+                 plan.split_old, plan.wpw_young, w.ml, w.mask, w.acc, tail ? 1 : 0,
                  tail ? tail->k_ring : nullptr, tail ? tail->v_ring : nullptr, tail && tail->ring_f32 ? 1 : 0,
                  tail ? tail->ring_cap : 0, w.tail_ml, w.tail_o};
   // streamed sequences: one more workgroup per unit for the recent tokens
-  const dim3 grid(static_cast<unsigned>(plan.splits + (tail ? 1 : 0)), static_cast<unsigned>(batch * sh.hkv));
+  const dim3 grid(static_cast<unsigned>(batch * sh.hkv), static_cast<unsigned>(plan.splits + (tail ? 1 : 0)));
   constexpr size_t dyn_bytes = Lds<D, KB, VB>::DYN;
   // dynamic LDS above the 64 KB default needs the attribute, once per device (setting it
   // twice from two threads is harmless)

@@ -64,8 +64,10 @@ hipError_t launch_quantize_values(const Shape& sh, const DeviceTables& tb, const
 // log-sum-exp merge and the batched inverse value rotation.
 struct DecodePlan {
   int splits;            // splits (one workgroup each) per (sequence, KV head)
-  int windows_per_wave;  // consecutive 32-token windows per wave of a split
+  int windows_per_wave;  // consecutive 32-token windows per wave of a split (splits below split_old)
   size_t workspace_bytes;
+  int split_old = 0;     // splits [split_old, splits) take wpw_young windows per wave
+  int wpw_young = 0;
 };
 
 // stream: the plan of omnikv_decode_attention_streaming (one workgroup per (sequence, KV
