@@ -45,6 +45,13 @@ codes and metadata can be compared bit for bit):
              fp16 round-to-nearest-even).
   key code   theta_j = m + s * (j + 1/2) (product and sum each rounded to fp32),
              code = #{ j < L : y >= theta_j }.
+  MXFP4 key metadata (the pages' default format, [paper] §3.1 Implementation
+             details): the window's vectors mn and (mx - mn) / L are each cut into
+             blocks of 32 consecutive channels; a block stores one E8M0 exponent
+             e = floor(log2 max|x|) - 2 (clamped to [-127, 127]; -127 for an
+             all-zero block) and 32 E2M1 elements, x * 2^-e rounded to the nearest
+             of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even code, sign kept.
+             The codes use the decoded m and s in the key-code rule above.
   value scale  S = sum of v_i^2 by the stride-halving tree (pairs (i, i + d/2),
              then (i, i + d/4), ..., each square and sum rounded to fp32);
              sigma = sqrt(S / d) (correctly rounded); stored fp16.
@@ -239,18 +246,114 @@ def key_window_quantize(y: np.ndarray, bits: int):
     return codes, m16, s16
 
 
-def quantize_keys(k: np.ndarray, signs: np.ndarray, bits: int):
+# ----------------------------------------------------------------------------- MXFP4 metadata
+# E2M1 element values by code (sign bit 3 clear), from the element format: code bits
+# (e1 e0 m), exponent bias 1, exponent 0 subnormal with value m / 2.
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+MX_BLOCK = 32
+
+
+def mx_record_bytes(d: int) -> int:
+    """Bytes of one window's MXFP4 metadata record for one vector (m or s): d/2 bytes
+    of E2M1 codes (channel 2i in the low nibble of byte i), d/32 exponent bytes, then
+    zero padding to a multiple of 16 bytes."""
+    return (d // 2 + d // MX_BLOCK + 15) // 16 * 16
+
+
+def mxfp4_encode(x: np.ndarray):
+    """fp32 [..., n*32] -> (codes uint8 [..., n*32] in 0..15, exponent bytes uint8 [..., n]).
+
+    Each block of 32 consecutive elements shares the exponent e = floor(log2 amax) - 2,
+    stored as e + 127; every element is x * 2^-e rounded to the nearest E2M1 value with
+    ties to the even code (values beyond 6 take 6), its sign in bit 3.
+    """
+    x = np.asarray(x, dtype=np.float64)   # fp32 inputs are exact in fp64
+    shape = x.shape
+    blocks = x.reshape(shape[:-1] + (shape[-1] // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    _, k = np.frexp(amax)                  # amax = f * 2^k, f in [0.5, 1): floor(log2 amax) = k - 1
+    e = np.where(amax > 0, k - 1 - 2, -127)
+    e = np.clip(e, -127, 127)
+    v = np.abs(blocks) * np.exp2(-e.astype(np.float64))[..., None]   # exact scaling
+    dist = np.abs(v[..., None] - E2M1_VALUES)                         # [..., 32, 8]
+    best = dist.min(axis=-1, keepdims=True)
+    tie = dist == best
+    # the nearest code; where two are equally near, the even one
+    even_pick = np.where(tie[..., 0::2].any(axis=-1),
+                         2 * np.argmax(tie[..., 0::2], axis=-1), -1)
+    code = np.where(tie.sum(axis=-1) > 1, even_pick, np.argmax(tie, axis=-1))
+    sign = np.signbit(blocks).astype(np.int64)
+    codes = (code + 8 * sign).astype(np.uint8).reshape(shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mxfp4_decode(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """Inverse of mxfp4_encode: float64 values (exact)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    shape = codes.shape
+    c = codes.reshape(shape[:-1] + (shape[-1] // MX_BLOCK, MX_BLOCK))
+    mag = E2M1_VALUES[c & 7] * np.exp2(np.asarray(exps, np.float64) - 127.0)[..., None]
+    return np.where(c & 8, -mag, mag).reshape(shape)
+
+
+def mx_pack_record(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """Per-window record bytes [..., mx_record_bytes(d)] from codes [..., d], exps [..., d/32]."""
+    codes = np.asarray(codes, np.uint8)
+    d = codes.shape[-1]
+    rec = np.zeros(codes.shape[:-1] + (mx_record_bytes(d),), np.uint8)
+    rec[..., :d // 2] = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    rec[..., d // 2:d // 2 + d // MX_BLOCK] = exps
+    return rec
+
+
+def mx_unpack_record(rec: np.ndarray, d: int):
+    """(codes [..., d], exps [..., d/32]) from record bytes."""
+    rec = np.asarray(rec, np.uint8)
+    codes = np.empty(rec.shape[:-1] + (d,), np.uint8)
+    codes[..., 0::2] = rec[..., :d // 2] & 15
+    codes[..., 1::2] = rec[..., :d // 2] >> 4
+    return codes, rec[..., d // 2:d // 2 + d // MX_BLOCK]
+
+
+def mx_record_values(rec: np.ndarray, d: int) -> np.ndarray:
+    """Decoded float64 vector [..., d] of a record."""
+    return mxfp4_decode(*mx_unpack_record(rec, d))
+
+
+def key_window_quantize_mx(y: np.ndarray, bits: int):
+    """key_window_quantize with MXFP4 metadata.  Returns (codes uint8 [..., 32, d],
+    m record uint8 [..., R], s record uint8 [..., R]), R = mx_record_bytes(d)."""
+    L = 2**bits - 1
+    y = np.asarray(y, dtype=F32)
+    mn = y.min(axis=-2) + F32(0)
+    mx = y.max(axis=-2) + F32(0)
+    step = (mx - mn) / F32(L)
+    mc, me = mxfp4_encode(mn)
+    sc, se = mxfp4_encode(step)
+    m = mxfp4_decode(mc, me).astype(F32)   # exact: E2M1 times a power of two
+    s = mxfp4_decode(sc, se).astype(F32)
+    codes = np.zeros(y.shape, dtype=np.uint8)
+    for j in range(L):
+        theta = m + s * F32(j + 0.5)
+        codes += (y >= theta[..., None, :]).astype(np.uint8)
+    return codes, mx_pack_record(mc, me), mx_pack_record(sc, se)
+
+
+def quantize_keys(k: np.ndarray, signs: np.ndarray, bits: int, meta: str = "fp16"):
     """Quantize a chunk of keys.  k: fp32 [B][n][Hkv][d], n a multiple of 32.
 
-    Returns (k_codes uint32 [B][Hkv][n/32][d*bits], k_min, k_scale fp16 bits
-    [B][Hkv][n/32][d]); window w of the result is window t0/32 + w of the cache.
+    Returns (k_codes uint32 [B][Hkv][n/32][d*bits], k_min, k_scale); the metadata are
+    fp16 bits [B][Hkv][n/32][d] (meta "fp16") or MXFP4 records uint8
+    [B][Hkv][n/32][mx_record_bytes(d)] (meta "mxfp4").  Window w of the result is
+    window t0/32 + w of the cache.
     """
     B, n, H, d = k.shape
-    assert n % WINDOW == 0
+    assert n % WINDOW == 0 and meta in ("fp16", "mxfp4")
     y = rotate_keys_f32(k, signs)                                # [B][n][H][d]
     y = y.transpose(0, 2, 1, 3).reshape(B, H, n // WINDOW, WINDOW, d)
-    codes, m16, s16 = key_window_quantize(y, bits)
-    return pack_windows(codes, "key", bits), m16, s16
+    quant = key_window_quantize if meta == "fp16" else key_window_quantize_mx
+    codes, km, ks = quant(y, bits)
+    return pack_windows(codes, "key", bits), km, ks
 
 
 # ----------------------------------------------------------------------------- value codec
@@ -341,11 +444,19 @@ def rotated_values_f64(v: np.ndarray, tags: np.ndarray, U: np.ndarray) -> np.nda
 
 # ----------------------------------------------------------------------------- dequantization
 def dequantize_keys(k_codes, k_min, k_scale, signs, bits: int, length: Optional[int] = None):
-    """Original-space keys x_hat = R^{-1}(m + s * code), float64 [B][Hkv][T][d]."""
+    """Original-space keys x_hat = R^{-1}(m + s * code), float64 [B][Hkv][T][d].
+
+    k_min, k_scale: fp16 bits (uint16 [B][Hkv][nw][d]) or MXFP4 records (uint8
+    [B][Hkv][nw][mx_record_bytes(d)]), told apart by their dtype.
+    """
     B, H, nw, _ = k_codes.shape
-    d = k_min.shape[-1]
+    d = np.asarray(signs).shape[-1]
     codes = unpack_windows(k_codes, "key", d, bits).astype(np.float64)   # [B][H][nw][32][d]
-    yhat = f16_to_f64(k_min)[:, :, :, None, :] + f16_to_f64(k_scale)[:, :, :, None, :] * codes
+    if np.asarray(k_min).dtype == np.uint8:
+        m, s = mx_record_values(k_min, d), mx_record_values(k_scale, d)
+    else:
+        m, s = f16_to_f64(k_min), f16_to_f64(k_scale)
+    yhat = m[:, :, :, None, :] + s[:, :, :, None, :] * codes
     yhat = yhat.reshape(B, H, nw * WINDOW, d)
     if length is not None:
         yhat = yhat[:, :, :length]

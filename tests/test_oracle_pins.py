@@ -188,6 +188,130 @@ def test_key_window_bounds(bits):
     assert np.all(yhat >= m[:, None, :]) and np.all(yhat <= (m + L * s)[:, None, :] + 1e-9)
 
 
+# ----------------------------------------------------------------------------- MXFP4 key metadata
+def test_e2m1_values_from_bit_definition():
+    # E2M1: sign bit 3, exponent bits 2-1 with bias 1 (exponent 0: subnormal, value m/2),
+    # mantissa bit 0.  Decoding a block with exponent byte 127 (scale 1) gives the
+    # element values themselves.
+    codes = np.array([c % 16 for c in range(32)], np.uint8)
+    got = O.mxfp4_decode(codes, np.array([127], np.uint8))
+    for c in range(32):
+        sg, ex, m = (c % 16) >> 3, ((c % 16) >> 1) & 3, c & 1
+        mag = m * 0.5 if ex == 0 else 2.0 ** (ex - 1) * (1 + m / 2)
+        assert got[c] == (-mag if sg else mag), c
+
+
+def _rne_e2m1(v):
+    # round to nearest even significand, binade by binade (numpy's round is half-to-even):
+    # step 0.5 below 2, step 1 in [2, 4), step 2 from 4, largest value 6
+    v = np.abs(np.asarray(v, np.float64))
+    r = np.where(v < 2, 0.5 * np.round(v / 0.5), np.where(v < 4, np.round(v), 2 * np.round(v / 2)))
+    return np.minimum(r, 6.0)
+
+
+def test_mxfp4_rounding_is_round_to_nearest_even():
+    rng = np.random.default_rng(5)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.125, 6.0, 7.0, 7.99], np.float64)
+    for trial in range(200):
+        blk = rng.uniform(-8, 8, 32)
+        blk[:len(ties)] = ties * rng.choice([-1, 1], len(ties))
+        blk[len(ties)] = 7.5  # the block maximum lies in [4, 8): shared exponent 0
+        blk = np.clip(blk, -7.99, 7.99)
+        k = int(rng.integers(-20, 21))   # the same block scaled by 2^k: exponent moves by k
+        x = (blk * 2.0 ** k).astype(np.float32)
+        codes, e = O.mxfp4_encode(x)
+        assert int(e[0]) == 127 + k
+        got = O.mxfp4_decode(codes, e)
+        want = np.sign(blk) * _rne_e2m1(blk) * 2.0 ** k
+        assert np.array_equal(np.abs(got), np.abs(want)), trial
+        assert np.array_equal(np.signbit(got) | (got == 0), np.signbit(x.astype(np.float64)) | (want == 0))
+
+
+def test_mxfp4_shared_exponent_examples():
+    def exp_of(amax):
+        x = np.zeros(32, np.float32)
+        x[7] = amax
+        return int(O.mxfp4_encode(x)[1][0])
+    # e = floor(log2 amax) - 2, stored + 127
+    assert exp_of(6.0) == 127
+    assert exp_of(4.0) == 127
+    assert exp_of(3.99) == 126
+    assert exp_of(1.0) == 125
+    assert exp_of(0.75) == 124
+    assert exp_of(-12.0) == 128
+    assert exp_of(3e38) == 127 + 127 - 2
+    assert exp_of(np.float32(2.0 ** -130)) == 0      # clamped at -127
+    codes, e = O.mxfp4_encode(np.zeros(64, np.float32))  # all-zero blocks
+    assert np.all(codes == 0) and np.all(e == 0)
+    # the block maximum keeps at least 3/4 of its magnitude (x / 2^e in [4, 8) -> 4 or 6)
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((100, 32)) * np.exp(rng.uniform(-10, 10, (100, 1)))).astype(np.float32)
+    dec = O.mxfp4_decode(*O.mxfp4_encode(x))
+    i = np.argmax(np.abs(x), axis=1)
+    a = np.abs(x[np.arange(100), i]).astype(np.float64)
+    b = np.abs(dec[np.arange(100), i])
+    assert np.all(b >= 0.75 * a * (1 - 1e-12)) and np.all(b <= a * 1.5)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_mx_record_layout(d):
+    assert O.mx_record_bytes(d) == {64: 48, 128: 80}[d]
+    rng = np.random.default_rng(d)
+    codes = rng.integers(0, 16, (3, d)).astype(np.uint8)
+    exps = rng.integers(0, 255, (3, d // 32)).astype(np.uint8)
+    rec = O.mx_pack_record(codes, exps)
+    # channel 2i in the low nibble of byte i, channel 2i + 1 in the high nibble
+    assert rec[0, 0] == codes[0, 0] | (codes[0, 1] << 4)
+    assert rec[1, d // 2 - 1] == codes[1, d - 2] | (codes[1, d - 1] << 4)
+    assert np.array_equal(rec[:, d // 2:d // 2 + d // 32], exps)
+    assert np.all(rec[:, d // 2 + d // 32:] == 0)
+    c2, e2 = O.mx_unpack_record(rec, d)
+    assert np.array_equal(c2, codes) and np.array_equal(e2, exps)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_key_window_mx_codes_are_nearest_levels(bits):
+    # with MXFP4 metadata every code is still the nearest level m + s c of the decoded
+    # m and s (ties up), clamped to 0 .. L outside the levels
+    L = 2**bits - 1
+    rng = np.random.default_rng(10 + bits)
+    y = (rng.standard_normal((40, 32, 64)) * rng.uniform(0.1, 3, (40, 1, 64))
+         + rng.uniform(-2, 2, (40, 1, 64))).astype(np.float32)
+    codes, mrec, srec = O.key_window_quantize_mx(y, bits)
+    m, s = O.mx_record_values(mrec, 64), O.mx_record_values(srec, 64)
+    yy = y.astype(np.float64)
+    lev = m[:, None, :, None] + s[:, None, :, None] * np.arange(L + 1)     # [40][1][64][L+1]
+    dist = np.abs(yy[..., None] - lev)
+    best = dist.min(-1)
+    d_code = np.take_along_axis(dist, codes[..., None].astype(np.int64), -1)[..., 0]
+    # a code may differ from the exact nearest only by the fp32 rounding of a threshold
+    assert np.all(d_code <= best + 1e-5 * (np.abs(yy) + 1))
+    assert codes.max() <= L
+    # the MX block scale of m bounds how far m can sit from the window minimum
+    mn = yy.min(1)
+    # (grid spacing at most 2 * 2^e, and saturation from below 8 * 2^e to 6 * 2^e)
+    amax_m = np.abs(mn.reshape(40, 2, 32)).max(-1)
+    unit = np.repeat(2.0 ** (np.floor(np.log2(amax_m)) - 2), 32, axis=1)
+    assert np.all(np.abs(m - mn) <= 2 * unit)
+
+
+def test_mx_cache_dequantizes_to_its_levels():
+    cfg = synth.CONFIGS[1]
+    T, d = 128, 64
+    tags = synth.modality_layout(cfg, 0, T)
+    k = synth.drifting_tensor(cfg, tags, 0, 0, 0, T)
+    signs = synth.rademacher_signs(d, 0)
+    kc, mrec, srec = O.quantize_keys(k, signs, 2, meta="mxfp4")
+    assert mrec.dtype == np.uint8 and mrec.shape == (1, 1, T // 32, 48)
+    x = O.dequantize_keys(kc, mrec, srec, signs, 2)[0, 0]
+    # rotate back and compare with m + s * code from the records, window by window
+    y = O.rotate_keys_f32(x.astype(np.float32), signs).astype(np.float64)
+    codes = O.unpack_windows(kc, "key", d, 2)[0, 0]
+    m, s = O.mx_record_values(mrec, d)[0, 0], O.mx_record_values(srec, d)[0, 0]
+    want = (m[:, None, :] + s[:, None, :] * codes).reshape(T, d)
+    assert np.max(np.abs(y - want)) < 1e-5 * (np.max(np.abs(want)) + 1)
+
+
 # ----------------------------------------------------------------------------- value codec
 def test_lloyd_max_matches_textbook_table():
     for line in open(os.path.join(GOLDEN, "lloyd_max_gaussian.txt")):
