@@ -37,11 +37,18 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
 
-def algorithmic_bytes(cfg, kbits, vbits, lens):
+def mx_record_bytes(d):
+    """Bytes of one window's MXFP4 key-metadata record (one vector): d/2 code bytes,
+    d/32 exponent bytes, padded to 16 (the storage format of include/omnikv.h)."""
+    return (d // 2 + d // 32 + 15) // 16 * 16
+
+
+def algorithmic_bytes(cfg, kbits, vbits, lens, key_meta="fp16"):
     """Bytes one decode step must read: packed codes, window metadata, value
     scales and modality tags of every cached token (queries/outputs excluded)."""
     d, H = cfg.head_dim, cfg.kv_heads
-    per_token_head = d * kbits / 8 + d * vbits / 8 + 2 * 2 * d / 32 + 2
+    meta = 2 * 2 * d / 32 if key_meta == "fp16" else 2 * mx_record_bytes(d) / 32
+    per_token_head = d * kbits / 8 + d * vbits / 8 + meta + 2
     total = 0.0
     for L in lens:
         nwin = math.ceil(L / 32)
@@ -265,6 +272,31 @@ def main():
     part_ms, _ = timed_replay(g_part)
     comb_ms, _ = timed_replay(g_comb)
     stream_ms, _ = timed_replay(g_stream)
+
+    # the same step with MXFP4 key metadata (the paper's default format): its own context
+    # and caches, enough of them to exceed the MALL
+    ctx_mx = binding.Context(d, cfg.q_heads, cfg.kv_heads, args.kbits, args.vbits, signs, U, key_meta="mxfp4")
+    alg_mx = algorithmic_bytes(cfg, args.kbits, args.vbits, lens_np, key_meta="mxfp4")
+    nbuf_mx = args.buffers or max(2, math.ceil(2.5 * MALL_BYTES / alg_mx))
+    caches_mx, _ = build_caches(ctx_mx, cfg, nbuf_mx, args.kbits, args.vbits)
+    ws_mx = torch.empty(ctx_mx.workspace_size(cfg.batch, T, args.splits), dtype=torch.uint8, device="cuda")
+
+    def step_mx(i):
+        c = caches_mx[i % nbuf_mx]
+        ctx_mx.decode_partial(q, lens, T, c, ws_mx, num_splits=args.splits)
+        ctx_mx.decode_combine(lens, cfg.batch, T, ws_mx, out, num_splits=args.splits)
+
+    for i in range(args.warmup):
+        step_mx(i)
+    g_mx = capture(lambda i: step_mx(args.warmup + i), args.steps)
+    g_mx_part = capture(lambda i: ctx_mx.decode_partial(q, lens, T, caches_mx[i % nbuf_mx], ws_mx,
+                                                        num_splits=args.splits), args.steps)
+    g_mx.replay()
+    torch.cuda.synchronize()
+    mx_ms, _ = timed_replay(g_mx)
+    mx_part_ms, _ = timed_replay(g_mx_part)
+    del caches_mx, g_mx, g_mx_part
+    ctx_mx.close()
     kp, vp = binding.Context.stream_packed_lengths(T)
     ms_per_step = step_ms / args.steps
     us_step_med = ms_per_step * 1e3
@@ -302,6 +334,11 @@ def main():
         "write_path": write_path,
         "streaming": {"us_per_step": round(stream_ms / args.steps * 1e3, 2),
                       "recent_tokens_per_sequence": T - vp, "packed_key_tokens": kp},
+        "key_meta_mxfp4": {"us_per_step": round(mx_ms / args.steps * 1e3, 2),
+                           "decode_partial_avg_us": round(mx_part_ms / args.steps * 1e3, 2),
+                           "algorithmic_bytes_per_step": int(alg_mx),
+                           "GBps": round(alg_mx / (mx_ms / args.steps / 1e3) / 1e9, 1),
+                           "cache_buffers": nbuf_mx},
     }
     if args.copy_reference_mib:
         n = args.copy_reference_mib * (1 << 20) // 4

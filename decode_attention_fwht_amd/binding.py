@@ -18,12 +18,14 @@ LIB_PATH = os.path.join(_PKG, "libomnikv.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
+META_FP16, META_MXFP4 = 0, 1
 
 EXPORTED = (
     "omnikv_create", "omnikv_destroy", "omnikv_value_codebook", "omnikv_quantize_keys",
     "omnikv_quantize_values", "omnikv_decode_workspace_size", "omnikv_decode_attention",
     "omnikv_decode_partial", "omnikv_decode_combine", "omnikv_stream_packed_lengths", "omnikv_stream_append",
-    "omnikv_decode_attention_streaming", "omnikv_calibrate_value_rotation", "omnikv_last_error",
+    "omnikv_decode_attention_streaming", "omnikv_calibrate_value_rotation", "omnikv_key_meta_bytes",
+    "omnikv_last_error",
 )
 
 
@@ -51,7 +53,8 @@ class OmniKVError(RuntimeError):
 
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "head_dim", "num_q_heads", "num_kv_heads", "key_bits", "value_bits", "window", "num_modalities")]
+        "head_dim", "num_q_heads", "num_kv_heads", "key_bits", "value_bits", "window", "num_modalities",
+        "key_meta")]
 
 
 _lib = None
@@ -69,6 +72,7 @@ def load() -> ctypes.CDLL:
     L.omnikv_create.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, ctypes.POINTER(vp)]
     L.omnikv_destroy.argtypes = [vp]
     L.omnikv_value_codebook.argtypes = [vp, vp]
+    L.omnikv_key_meta_bytes.argtypes = [vp, ctypes.POINTER(sz)]
     L.omnikv_quantize_keys.argtypes = [vp, vp, ctypes.c_int, i32, i64, i64, i64, vp, vp, vp, vp]
     L.omnikv_quantize_values.argtypes = [vp, vp, ctypes.c_int, vp, i32, i64, i64, i64, vp, vp, vp]
     L.omnikv_decode_workspace_size.argtypes = [vp, i32, i64, i32, ctypes.POINTER(sz)]
@@ -114,12 +118,13 @@ class Context:
 
     def __init__(self, head_dim: int, num_q_heads: int, num_kv_heads: int, key_bits: int = 2,
                  value_bits: int = 2, key_signs=None, value_rotations=None, value_codebook=None,
-                 num_modalities: Optional[int] = None):
+                 num_modalities: Optional[int] = None, key_meta: str = "fp16"):
         L = load()
         signs = np.ascontiguousarray(key_signs, dtype=np.int8)
         rots = np.ascontiguousarray(value_rotations, dtype=np.float32)
         M = rots.shape[0] if num_modalities is None else num_modalities
-        cfg = _Config(head_dim, num_q_heads, num_kv_heads, key_bits, value_bits, 32, M)
+        meta = {"fp16": META_FP16, "mxfp4": META_MXFP4}.get(key_meta, -1)
+        cfg = _Config(head_dim, num_q_heads, num_kv_heads, key_bits, value_bits, 32, M, meta)
         cb = None if value_codebook is None else np.ascontiguousarray(value_codebook, dtype=np.uint16)
         h = ctypes.c_void_p()
         _check(L.omnikv_create(ctypes.byref(cfg), signs.ctypes.data, rots.ctypes.data,
@@ -127,6 +132,10 @@ class Context:
         self._h = h
         self.head_dim, self.num_q_heads, self.num_kv_heads = head_dim, num_q_heads, num_kv_heads
         self.key_bits, self.value_bits, self.num_modalities = key_bits, value_bits, M
+        self.key_meta = key_meta
+        nb = ctypes.c_size_t()
+        _check(L.omnikv_key_meta_bytes(h, ctypes.byref(nb)))
+        self.key_meta_bytes = nb.value   # per (sequence, KV head, window), each of k_min, k_scale
 
     def close(self):
         if getattr(self, "_h", None) and self._h.value:
@@ -153,10 +162,13 @@ class Context:
         import torch
         d, H, nw = self.head_dim, self.num_kv_heads, t_cap // 32
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        # key metadata: fp16 bit patterns [B][H][nw][d], or MXFP4 byte records [B][H][nw][R]
+        meta = ((batch, H, nw, d), torch.int16) if self.key_meta == "fp16" else \
+            ((batch, H, nw, self.key_meta_bytes), torch.uint8)
         return dict(
             k_codes=z((batch, H, nw, d * self.key_bits), torch.int32),
-            k_min=z((batch, H, nw, d), torch.int16),
-            k_scale=z((batch, H, nw, d), torch.int16),
+            k_min=z(*meta),
+            k_scale=z(*meta),
             v_codes=z((batch, H, nw, d * self.value_bits), torch.int32),
             v_scale=z((batch, H, t_cap), torch.int16),
             modality=z((batch, t_cap), torch.uint8),

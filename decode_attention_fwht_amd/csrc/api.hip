@@ -134,6 +134,8 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
   if (group > omnikv::kMaxGroup) return fail(OMNIKV_EUNSUPPORTED, "at most 8 query heads per KV head (got %d)", group);
   const int M = cfg->num_modalities;
   if (M < 1 || M > omnikv::kMaxModalities) return fail(OMNIKV_EINVAL, "num_modalities must be 1..3 (got %d)", M);
+  if (cfg->key_meta != OMNIKV_META_FP16 && cfg->key_meta != OMNIKV_META_MXFP4)
+    return fail(OMNIKV_EINVAL, "key_meta must be OMNIKV_META_FP16 or OMNIKV_META_MXFP4 (got %d)", cfg->key_meta);
   for (int i = 0; i < d; ++i)
     if (key_signs[i] != 1 && key_signs[i] != -1) return fail(OMNIKV_EINVAL, "key_signs[%d] = %d is not +-1", i, key_signs[i]);
   for (int m = 0; m < M; ++m) {
@@ -163,7 +165,8 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
 
   auto* ctx = new (std::nothrow) omnikv_ctx();
   if (!ctx) return fail(OMNIKV_ENOMEM, "out of host memory");
-  ctx->sh = omnikv::Shape{d, cfg->num_q_heads, cfg->num_kv_heads, group, cfg->key_bits, cfg->value_bits, M};
+  ctx->sh = omnikv::Shape{d, cfg->num_q_heads, cfg->num_kv_heads, group, cfg->key_bits, cfg->value_bits, M,
+                          cfg->key_meta == OMNIKV_META_MXFP4 ? 1 : 0};
   ctx->levels = levels;
   (void)hipGetDevice(&ctx->device);
 
@@ -262,6 +265,14 @@ omnikv_status omnikv_value_codebook(const omnikv_ctx* ctx, uint16_t* levels) {
   if (check_ctx(ctx) != OMNIKV_OK) return OMNIKV_EINVAL;
   if (!levels) return fail(OMNIKV_EINVAL, "levels is NULL");
   std::copy(ctx->levels.begin(), ctx->levels.end(), levels);
+  return OMNIKV_OK;
+}
+
+omnikv_status omnikv_key_meta_bytes(const omnikv_ctx* ctx, size_t* bytes) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!bytes) return fail(OMNIKV_EINVAL, "key_meta_bytes: bytes is NULL");
+  *bytes = omnikv::key_meta_bytes(ctx->sh);
   return OMNIKV_OK;
 }
 
@@ -453,9 +464,12 @@ omnikv_status omnikv_stream_append(const omnikv_ctx* ctx, const void* k_new, con
     const size_t head_win = static_cast<size_t>(b) * sh.hkv * nwin;  // first window block of sequence b
     if (k1 > k0) {
       const char* src = static_cast<const char*>(k_ring) + (static_cast<size_t>(b) * ring_cap + k0 % ring_cap) * sh.hkv * sh.d * esz;
+      // metadata of sequence b start head_win window records in
+      const size_t mb = head_win * omnikv::key_meta_bytes(sh);
       e = omnikv::launch_quantize_keys(sh, ctx->tb, src, !f32, 1, k0, k1 - k0, t_cap,
-                                       k_codes + head_win * sh.d * sh.kbits, k_min + head_win * sh.d,
-                                       k_scale + head_win * sh.d, stream);
+                                       k_codes + head_win * sh.d * sh.kbits,
+                                       reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(k_min) + mb),
+                                       reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(k_scale) + mb), stream);
       if (e != hipSuccess) return hip_fail(e, "stream_append key flush");
     }
     if (v1 > v0) {

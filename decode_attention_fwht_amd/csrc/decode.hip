@@ -185,28 +185,36 @@ struct PartialArgs {
 
 // ---------------------------------------------------------------------------------------
 // Window staging.  Each wave owns a ring of LDS slots; a slot holds everything one
-// 32-token window needs: [key block | value block | k_scale | k_min | v_scale | tags].
+// 32-token window needs: [key block | value block | k_scale | k_min | v_scale | tags],
+// and with MXFP4 key metadata the two raw records after them (k_scale, k_min), which
+// the wave expands into the fp16 k_scale and k_min areas before the window's visit.
 // Slots are filled by asynchronous global->LDS copies (global_load_lds_dwordx4, 16 bytes
 // per lane), ring depth - 1 windows ahead of the one being computed, so no registers are
 // held by loads in flight.  The copies are tracked by the vmcnt counter only; the waits
 // before reading a slot are explicit.
 constexpr int kWaves = 4;  // waves per workgroup; each owns its own consecutive windows
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, bool MX>
 struct Slot {
   static constexpr int KBYTES = 4 * D * KB;  // 32 tokens x D codes x KB bits
   static constexpr int VBYTES = 4 * D * VB;
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = KBYTES;
-  static constexpr int OFF_S = KBYTES + VBYTES;      // k_scale, 2 D bytes
-  static constexpr int OFF_M = OFF_S + 2 * D;        // k_min, 2 D bytes
+  static constexpr int OFF_S = KBYTES + VBYTES;      // k_scale, 2 D bytes (fp16)
+  static constexpr int OFF_M = OFF_S + 2 * D;        // k_min, 2 D bytes (fp16)
   static constexpr int OFF_SIG = OFF_M + 2 * D;      // v_scale of the 32 tokens, 64 bytes
   static constexpr int OFF_TAG = OFF_SIG + 64;       // modality of the 32 tokens, 32 bytes
-  static constexpr int BYTES = ((OFF_TAG + 32) + 127) / 128 * 128;
+  static constexpr int MXR = mx_record_bytes(D);     // MXFP4: one record
+  static constexpr int OFF_RAW = OFF_TAG + 32;       // MXFP4: k_scale record, then k_min's
+  static constexpr int END = MX ? OFF_RAW + 2 * MXR : OFF_TAG + 32;
+  static constexpr int BYTES = (END + 127) / 128 * 128;
   static constexpr int NK = (KBYTES + 1023) / 1024;  // copies of the key block
   static constexpr int NV = (VBYTES + 1023) / 1024;
-  static constexpr int MISC_LANES = D / 8 + D / 8 + 4 + 2;
+  // the metadata copy: one 16-byte piece per lane, in lane order from OFF_COPY
+  static constexpr int OFF_COPY = MX ? OFF_SIG : OFF_S;
+  static constexpr int MISC_LANES = (END - OFF_COPY) / 16;
   static constexpr int COPIES = NK + NV + 1;          // copy instructions per window
+  static_assert(OFF_RAW % 16 == 0 && MXR % 16 == 0, "copy pieces");
 };
 
 // One 16-byte-per-lane global->LDS copy (lane l writes lds_addr + 16 l).  Issued in asm so
@@ -285,7 +293,7 @@ constexpr bool kBqaInRegs = kBlocksPerCU <= 2;
 // last ring slot (not filled before the first visit) stages its two query heads, the
 // signs of D, the sequence's length and (wave 0) the level-pair table; after them the
 // whole region holds every wave's per-modality accumulators for the block merge.
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, bool MX>
 struct Lds {
   static constexpr int QRAW = 2 * D * 4;         // staging: two heads' queries, fp32
   static constexpr int SGN = D * 4;              // then the signs of D, fp32
@@ -295,15 +303,15 @@ struct Lds {
   static constexpr int MERGE = kWaves * kMaxModalities * kMaxGroup * D * 4;
   static constexpr int STATIC = kMaxGroup * D * 4 + TAB + 1024;  // q_lds, the table, small arrays
   static constexpr int dyn(int ring) {
-    const int r = kWaves * ring * Slot<D, KB, VB>::BYTES;
+    const int r = kWaves * ring * Slot<D, KB, VB, MX>::BYTES;
     return r > MERGE ? r : MERGE;
   }
   static constexpr bool fits(int ring) { return dyn(ring) + STATIC <= 160 * 1024 / kBlocksPerCU; }
   static constexpr int RING = fits(4) ? 4 : (fits(3) ? 3 : 2);
-  static constexpr int RING_BYTES = kWaves * RING * Slot<D, KB, VB>::BYTES;
+  static constexpr int RING_BYTES = kWaves * RING * Slot<D, KB, VB, MX>::BYTES;
   static constexpr int DYN = dyn(RING);
   static_assert(fits(RING), "LDS budget");
-  static_assert(TAB_OFF + TAB <= Slot<D, KB, VB>::BYTES, "staging must fit in one slot");
+  static_assert(TAB_OFF + TAB <= Slot<D, KB, VB, MX>::BYTES, "staging must fit in one slot");
 };
 
 // The recent tokens [T0, n) of a streamed sequence (T0 = max(value-packed length, n -
@@ -313,7 +321,7 @@ struct Lds {
 //   stored key with the query itself;
 //   then per head the max, the sum of 2^(s - max) and the value sum in the original space.
 // scratch: [8][D] original queries, then [8][kMaxRingCap] scores (dynamic LDS).
-template <int D, int KB>
+template <int D, int KB, bool MX>
 __device__ void stream_tail(const PartialArgs& a, const float (*q_rot)[D], float* scratch, int unit, int b,
                             int kvh, int n) {
   constexpr int T = kWaves * 64;
@@ -351,13 +359,39 @@ __device__ void stream_tail(const PartialArgs& a, const float (*q_rot)[D], float
         uint32_t w[NW];
 #pragma unroll
         for (int x = 0; x < NW; ++x) w[x] = wp[x];
-        uint32_t mw[CPT / 2], sw[CPT / 2];
+        float mv_[CPT], sv_[CPT];
+        if constexpr (!MX) {
+          uint32_t mw[CPT / 2], sw[CPT / 2];
 #pragma unroll
-        for (int x = 0; x < CPT; x += 8) {
-          const uint4 m8 = *reinterpret_cast<const uint4*>(a.k_min + wb * D + c0 + x);
-          const uint4 s8 = *reinterpret_cast<const uint4*>(a.k_scale + wb * D + c0 + x);
-          mw[x / 2] = m8.x; mw[x / 2 + 1] = m8.y; mw[x / 2 + 2] = m8.z; mw[x / 2 + 3] = m8.w;
-          sw[x / 2] = s8.x; sw[x / 2 + 1] = s8.y; sw[x / 2 + 2] = s8.z; sw[x / 2 + 3] = s8.w;
+          for (int x = 0; x < CPT; x += 8) {
+            const uint4 m8 = *reinterpret_cast<const uint4*>(a.k_min + wb * D + c0 + x);
+            const uint4 s8 = *reinterpret_cast<const uint4*>(a.k_scale + wb * D + c0 + x);
+            mw[x / 2] = m8.x; mw[x / 2 + 1] = m8.y; mw[x / 2 + 2] = m8.z; mw[x / 2 + 3] = m8.w;
+            sw[x / 2] = s8.x; sw[x / 2 + 1] = s8.y; sw[x / 2 + 2] = s8.z; sw[x / 2 + 3] = s8.w;
+          }
+#pragma unroll
+          for (int cc = 0; cc < CPT; ++cc) {
+            mv_[cc] = f16_value(static_cast<uint16_t>(mw[cc >> 1] >> (16 * (cc & 1))));
+            sv_[cc] = f16_value(static_cast<uint16_t>(sw[cc >> 1] >> (16 * (cc & 1))));
+          }
+        } else {
+          // MXFP4 records: channels c0 .. c0 + CPT - 1 lie in one 32-channel block
+          constexpr int R = mx_record_bytes(D);
+          const uint8_t* rm = reinterpret_cast<const uint8_t*>(a.k_min) + wb * R;
+          const uint8_t* rs = reinterpret_cast<const uint8_t*>(a.k_scale) + wb * R;
+          const int em = static_cast<int>(rm[D / 2 + c0 / 32]) - 127;
+          const int es = static_cast<int>(rs[D / 2 + c0 / 32]) - 127;
+          uint32_t nm[CPT / 8], ns[CPT / 8];
+#pragma unroll
+          for (int x = 0; x < CPT / 8; ++x) {
+            nm[x] = *reinterpret_cast<const uint32_t*>(rm + c0 / 2 + 4 * x);
+            ns[x] = *reinterpret_cast<const uint32_t*>(rs + c0 / 2 + 4 * x);
+          }
+#pragma unroll
+          for (int cc = 0; cc < CPT; ++cc) {
+            mv_[cc] = mx_decode((nm[cc >> 3] >> (4 * (cc & 7))) & 15u, em);
+            sv_[cc] = mx_decode((ns[cc >> 3] >> (4 * (cc & 7))) & 15u, es);
+          }
         }
 #pragma unroll
         for (int cc = 0; cc < CPT; ++cc) {
@@ -368,9 +402,7 @@ __device__ void stream_tail(const PartialArgs& a, const float (*q_rot)[D], float
           else if (KB == 2) { word = w[i & 1]; bit = 16 * e + 2 * (4 * (i >> 1) + 2 * tau + s8i); }
           else { word = w[i]; bit = 16 * e + 4 * (2 * tau + s8i); }
           const float code = static_cast<float>((word >> bit) & ((1u << KB) - 1u));
-          const float mv = f16_value(static_cast<uint16_t>(mw[cc >> 1] >> (16 * (cc & 1))));
-          const float sv = f16_value(static_cast<uint16_t>(sw[cc >> 1] >> (16 * (cc & 1))));
-          const float kval = mv + sv * code;
+          const float kval = mv_[cc] + sv_[cc] * code;
 #pragma unroll
           for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] = fmaf(q_rot[hh][c0 + cc], kval, acc[hh]);
         }
@@ -470,11 +502,11 @@ __device__ void stream_tail(const PartialArgs& a, const float (*q_rot)[D], float
   if (tid < kMaxGroup) a.tail_ml[static_cast<size_t>(unit) * kMaxGroup + tid] = tml[tid];
 }
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, bool MX>
 __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kernel(PartialArgs a) {
-  using SG = Slot<D, KB, VB>;
+  using SG = Slot<D, KB, VB, MX>;
   using KO = KeyOp<D, KB>;
-  constexpr int RING = Lds<D, KB, VB>::RING;
+  constexpr int RING = Lds<D, KB, VB, MX>::RING;
   constexpr int NC = D / 64;        // channels per lane in the query rotation
   constexpr int NS = D / 32;        // K-steps of the score contraction
   constexpr int NU = D / 16;        // channel tiles of the value contraction
@@ -483,7 +515,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   constexpr int PPW = 16 / VB;      // value code pairs per word
   constexpr uint32_t PMASK = (1u << (2 * VB)) - 1u;
   constexpr int L = SG::COPIES;
-  using LY = Lds<D, KB, VB>;
+  using LY = Lds<D, KB, VB, MX>;
 
   // Dynamic LDS (layout in Lds).  Only the asm copies write the ring and the staging
   // areas, and a static LDS array that no visible code stores to would let the optimizer
@@ -537,7 +569,23 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit_win * SG::VBYTES;
   const uint8_t* mbase = nullptr;
   uint32_t mstride = 0;
-  {
+  if constexpr (MX) {
+    // [v_scale: 4 pieces | tags: 2 | k_scale record | k_min record]
+    constexpr int RP = SG::MXR / 16;
+    if (lane < 4) {
+      mbase = reinterpret_cast<const uint8_t*>(a.v_scale) + static_cast<size_t>(unit) * a.t_cap * 2 + 16 * lane;
+      mstride = 64;
+    } else if (lane < 6) {
+      mbase = a.modality + static_cast<size_t>(b) * a.t_cap + 16 * (lane - 4);
+      mstride = 32;
+    } else if (lane < 6 + RP) {
+      mbase = reinterpret_cast<const uint8_t*>(a.k_scale) + unit_win * SG::MXR + 16 * (lane - 6);
+      mstride = SG::MXR;
+    } else {
+      mbase = reinterpret_cast<const uint8_t*>(a.k_min) + unit_win * SG::MXR + 16 * (lane - 6 - RP);
+      mstride = SG::MXR;
+    }
+  } else {
     const int l0 = D / 8, l1 = D / 4, l2 = D / 4 + 4;
     if (lane < l0) {
       mbase = reinterpret_cast<const uint8_t*>(a.k_scale) + unit_win * (2 * D) + 16 * lane;
@@ -564,7 +612,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     for (int x = 0; x < SG::NV; ++x)
       if (1024 * x + 16 * lane < SG::VBYTES)
         copy16_to_lds_sbase(vbase, static_cast<uint32_t>(w * SG::VBYTES + 1024 * x + 16 * lane), dst + SG::OFF_V + 1024 * x);
-    if (lane < SG::MISC_LANES) copy16_to_lds(mbase + static_cast<size_t>(w) * mstride, dst + SG::OFF_S);
+    if (lane < SG::MISC_LANES) copy16_to_lds(mbase + static_cast<size_t>(w) * mstride, dst + SG::OFF_COPY);
   };
 
   // ---- visit order: the wave's windows in order, each visited once whatever modalities
@@ -697,7 +745,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     // the split workgroups sharing this CU raise their priority while they start: this short
     // one takes the highest too, or it would only get their leftover issue slots
     __builtin_amdgcn_s_setprio(3);
-    stream_tail<D, KB>(a, q_lds, reinterpret_cast<float*>(ring_mem), unit, b, kvh, len_streamed);
+    stream_tail<D, KB, MX>(a, q_lds, reinterpret_cast<float*>(ring_mem), unit, b, kvh, len_streamed);
     return;
   }
 
@@ -763,6 +811,30 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
 #pragma unroll
         for (int i = 0; i < 4; ++i) ak[i] = (kw[KO::word(tau, s, i)] >> KO::shift(tau, s, i)) & KO::mask(s);
         cs[tau] = mfma16(ak, bqv, cs[tau]);
+      }
+    }
+  };
+
+  // ---- MXFP4 key metadata: the slot's two raw records -> the fp16 k_scale and k_min
+  // areas the score contractions read.  Lane l takes 2 D / 64 consecutive values of one
+  // vector (l < 32: k_scale, else k_min), all in one 32-channel block, and converts them
+  // with the block's scale (E2M1 times 2^e, exact in fp16 within its range).
+  auto mx_expand = [&](uint8_t* slot) {
+    constexpr int NPL = D / 32;  // values per lane
+    const int vec = lane >> 5, p = lane & 31;
+    if (NPL * p < D) {
+      const uint8_t* raw = slot + SG::OFF_RAW + vec * SG::MXR;
+      const float sc = mx_scale(raw[D / 2 + (NPL * p) / 32]);
+      uint8_t* out = slot + (vec ? SG::OFF_M : SG::OFF_S) + 2 * NPL * p;
+      if constexpr (NPL == 4) {
+        const uint32_t nib = *reinterpret_cast<const uint16_t*>(raw + 2 * p);
+        const half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, sc, 0);
+        const half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, sc, 1);
+        *reinterpret_cast<uint2*>(out) = make_uint2(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1));
+      } else {
+        const uint32_t nib = raw[p];
+        const half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, sc, 0);
+        *reinterpret_cast<uint32_t*>(out) = __builtin_bit_cast(uint32_t, v0);
       }
     }
   };
@@ -963,7 +1035,8 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     issue_upto(min(nw, i + RING));
     // wait for this visit's copies: later visits' copies may stay in flight
     wait_groups<L, RING - 1>(issued - (i + 1));
-    const uint8_t* slot = ring_slot(wave, i % RING);
+    uint8_t* slot = ring_slot(wave, i % RING);
+    if constexpr (MX) mx_expand(slot);
     float4_t cs[2], cm;
     score_mma(slot, cs, cm);
     visit(slot, (wbeg + i) * kWindow, cs, cm);
@@ -1277,7 +1350,7 @@ DecodePlan plan_decode(const Shape& sh, int batch, int64_t max_len, int requeste
   return p;
 }
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, bool MX>
 static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, const DecodePlan& plan,
                                    const float* q, const int32_t* seq_lens, int batch, int64_t max_len,
                                    const uint32_t* kc, const uint16_t* km, const uint16_t* ks,
@@ -1291,7 +1364,7 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
                  tail ? tail->ring_cap : 0, w.tail_ml, w.tail_o};
   // streamed sequences: one more workgroup per unit for the recent tokens
   const dim3 grid(static_cast<unsigned>(batch * sh.hkv), static_cast<unsigned>(plan.splits + (tail ? 1 : 0)));
-  constexpr size_t dyn_bytes = Lds<D, KB, VB>::DYN;
+  constexpr size_t dyn_bytes = Lds<D, KB, VB, MX>::DYN;
   // dynamic LDS above the 64 KB default needs the attribute, once per device (setting it
   // twice from two threads is harmless)
   static std::atomic<uint64_t> attr_set{0};
@@ -1300,12 +1373,12 @@ static hipError_t launch_partial_t(const Shape& sh, const DeviceTables& tb, cons
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
   if (bit == 0 || !(attr_set.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, KB, VB>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, KB, VB, MX>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn_bytes));
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_release);
   }
-  decode_partial_kernel<D, KB, VB><<<grid, kWaves * 64, dyn_bytes, st>>>(pa);
+  decode_partial_kernel<D, KB, VB, MX><<<grid, kWaves * 64, dyn_bytes, st>>>(pa);
   return hipGetLastError();
 }
 
@@ -1314,10 +1387,12 @@ hipError_t launch_decode_partial(const Shape& sh, const DeviceTables& tb, const 
                                  const uint16_t* km, const uint16_t* ks, const uint32_t* vc, const uint16_t* vs,
                                  const uint8_t* mod, int64_t t_cap, float scale, void* ws, const StreamTail* tail,
                                  hipStream_t st) {
-#define OMNIKV_DEC(D_, KB_, VB_)                                                                           \
-  if (sh.d == D_ && sh.kbits == KB_ && sh.vbits == VB_)                                                    \
-    return launch_partial_t<D_, KB_, VB_>(sh, tb, plan, q, seq_lens, batch, max_len, kc, km, ks, vc, vs, mod, \
-                                          t_cap, scale, ws, tail, st);
+#define OMNIKV_DEC(D_, KB_, VB_)                                                                                  \
+  if (sh.d == D_ && sh.kbits == KB_ && sh.vbits == VB_)                                                           \
+    return sh.mx ? launch_partial_t<D_, KB_, VB_, true>(sh, tb, plan, q, seq_lens, batch, max_len, kc, km, ks, vc, \
+                                                        vs, mod, t_cap, scale, ws, tail, st)                       \
+                 : launch_partial_t<D_, KB_, VB_, false>(sh, tb, plan, q, seq_lens, batch, max_len, kc, km, ks, vc, \
+                                                         vs, mod, t_cap, scale, ws, tail, st);
   OMNIKV_DEC(128, 2, 2)
   OMNIKV_DEC(128, 4, 4)
   OMNIKV_DEC(128, 2, 4)

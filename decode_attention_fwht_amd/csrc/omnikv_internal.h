@@ -48,7 +48,29 @@ constexpr int kMaxRingCap = 512;    // largest ring of recent tokens
 
 struct Shape {
   int d, hq, hkv, group, kbits, vbits, modalities;
+  int mx = 0;  // key range metadata: 0 fp16 vectors, 1 MXFP4 records
 };
+
+// Bytes of one MXFP4 metadata record (one vector of one window): d/2 bytes of E2M1
+// codes, d/32 exponent bytes, zero padding to a multiple of 16.
+__host__ __device__ constexpr int mx_record_bytes(int d) { return (d / 2 + d / 32 + 15) / 16 * 16; }
+// Value of MXFP4 element code c (E2M1, sign in bit 3) times 2^e, exact in fp32: codes 0
+// and 1 are 0 and 0.5 (subnormal), codes 2..7 are 2^(c/2 - 1) (1 + (c & 1) / 2).
+__device__ __forceinline__ float mx_decode(uint32_t c, int e) {
+  const uint32_t m = c & 7u;
+  const float mag = m < 2u ? 0.5f * static_cast<float>(m)
+                           : ldexpf(1.0f + 0.5f * static_cast<float>(m & 1u), static_cast<int>(m >> 1) - 1);
+  const float v = ldexpf(mag, e);
+  return (c & 8u) ? -v : v;
+}
+// The fp32 scale 2^(x - 127) of an E8M0 exponent byte x in 0..254 (x = 0: 2^-127).
+__device__ __forceinline__ float mx_scale(uint32_t x) {
+  return __uint_as_float(x ? (x << 23) : 0x00400000u);
+}
+// Bytes of k_min (or k_scale) per window in the shape's format.
+inline size_t key_meta_bytes(const Shape& sh) {
+  return sh.mx ? static_cast<size_t>(mx_record_bytes(sh.d)) : static_cast<size_t>(2 * sh.d);
+}
 
 // ---- launchers (return hipSuccess or the launch error) -----------------------------------
 hipError_t launch_quantize_keys(const Shape& sh, const DeviceTables& tb, const void* k, bool bf16,

@@ -3,7 +3,8 @@
 // codebook {0, ..., 2^bits - 1}.
 //   [paper] "OmniKVQuant: KV Cache Quantization for Omni-LLMs", §1 Introduction
 //   (TurboQuant's rotation; temporal key drift), §3.1 Implementation details
-//   (32-token groups), §3.3 Error comparison (m_gc, s_gc in FP16).
+//   (32-token groups; MXFP4 metadata by default), §3.3 Error comparison (m_gc, s_gc
+//   in FP16).
 //
 // One 64-lane wave owns one window of one (sequence, KV head).  A token spans D/8 lanes
 // of one 16-lane row, eight consecutive channels per lane, so a wave holds 64/(D/8)
@@ -70,6 +71,25 @@ __device__ __forceinline__ void key_slot(int tau, int s, int j, int& lw, int& bi
 
 constexpr int kWavesPerBlock = 4;
 
+// ---- MXFP4 metadata (OCP microscaling: blocks of 32 elements, one E8M0 exponent, E2M1
+// elements).  Shared exponent of a block whose largest magnitude is amax:
+// floor(log2 amax) - 2, at least -127 (zero and subnormal amax give -127).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
+  return ef == 0 ? -127 : max(ef - 127 - 2, -127);
+}
+// E2M1 code (sign in bit 3) of x / 2^e, round to nearest with ties to the even code,
+// magnitudes past 6 saturating.  inv = 2^-e exactly, so |x| * inv is exact wherever it
+// can reach a rounding boundary.
+__device__ __forceinline__ uint32_t mx_encode(float x, float inv) {
+  const float v = fabsf(x) * inv;
+  // boundaries between codes c - 1 and c: the midpoints 0.25, 0.75, ..., 5; a midpoint
+  // goes to the even code, so '>' where that is the lower one and '>=' where the upper
+  const uint32_t c = (v > 0.25f) + (v >= 0.75f) + (v > 1.25f) + (v >= 1.75f) + (v > 2.5f) + (v >= 3.5f) +
+                     (v > 5.0f);
+  return c | ((__float_as_uint(x) >> 31) << 3);
+}
+
 // value of lane l ^ (1 << k) within each 16-lane row (k = 0 .. 3)
 template <int K>
 __device__ __forceinline__ float row_xor(float x) {
@@ -88,7 +108,7 @@ __device__ __forceinline__ float row_xor(float x) {
   }
 }
 
-template <int D, int KB, bool BF16>
+template <int D, int KB, bool BF16, bool MX>
 __global__ __launch_bounds__(256) void quantize_keys_kernel(
     const void* __restrict__ k, int hkv, int64_t n, int64_t w0, int64_t nwin_cap,
     int64_t tasks, const float* __restrict__ signs, uint32_t* __restrict__ k_codes,
@@ -184,26 +204,72 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
       }
     }
     float mf[8], sf[8];
-    uint16_t m16[8], s16[8];
+    if constexpr (!MX) {
+      uint16_t m16[8], s16[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float lo = mn[e] + 0.0f;  // a zero extreme is +0
-      const float hi = mx[e] + 0.0f;
-      const float step = (hi - lo) / static_cast<float>(L);
-      m16[e] = f16_bits(lo);
-      s16[e] = f16_bits(step);
-      mf[e] = f16_value(m16[e]);
-      sf[e] = f16_value(s16[e]);
-    }
-    if (r == 0) {
-      uint32_t pm[4], ps[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        pm[x] = static_cast<uint32_t>(m16[2 * x]) | (static_cast<uint32_t>(m16[2 * x + 1]) << 16);
-        ps[x] = static_cast<uint32_t>(s16[2 * x]) | (static_cast<uint32_t>(s16[2 * x + 1]) << 16);
+      for (int e = 0; e < 8; ++e) {
+        const float lo = mn[e] + 0.0f;  // a zero extreme is +0
+        const float hi = mx[e] + 0.0f;
+        const float step = (hi - lo) / static_cast<float>(L);
+        m16[e] = f16_bits(lo);
+        s16[e] = f16_bits(step);
+        mf[e] = f16_value(m16[e]);
+        sf[e] = f16_value(s16[e]);
       }
-      *reinterpret_cast<uint4*>(k_min + blk * D + 8 * q) = make_uint4(pm[0], pm[1], pm[2], pm[3]);
-      *reinterpret_cast<uint4*>(k_scale + blk * D + 8 * q) = make_uint4(ps[0], ps[1], ps[2], ps[3]);
+      if (r == 0) {
+        uint32_t pm[4], ps[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          pm[x] = static_cast<uint32_t>(m16[2 * x]) | (static_cast<uint32_t>(m16[2 * x + 1]) << 16);
+          ps[x] = static_cast<uint32_t>(s16[2 * x]) | (static_cast<uint32_t>(s16[2 * x + 1]) << 16);
+        }
+        *reinterpret_cast<uint4*>(k_min + blk * D + 8 * q) = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+        *reinterpret_cast<uint4*>(k_scale + blk * D + 8 * q) = make_uint4(ps[0], ps[1], ps[2], ps[3]);
+      }
+    } else {
+      // MXFP4 records: a 32-channel block is the four lanes q = 4k .. 4k + 3 of a token
+      float lo[8], step[8], am = 0.0f, as = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = mn[e] + 0.0f;
+        step[e] = (mx[e] + 0.0f - lo[e]) / static_cast<float>(L);
+        am = fmaxf(am, fabsf(lo[e]));
+        as = fmaxf(as, fabsf(step[e]));
+      }
+      am = fmaxf(am, row_xor<0>(am));
+      am = fmaxf(am, row_xor<1>(am));
+      as = fmaxf(as, row_xor<0>(as));
+      as = fmaxf(as, row_xor<1>(as));
+      const int em = mx_exponent(am), es = mx_exponent(as);
+      const float im = __uint_as_float(static_cast<uint32_t>(127 - em) << 23);  // 2^-em
+      const float is = __uint_as_float(static_cast<uint32_t>(127 - es) << 23);
+      uint32_t wm = 0u, ws = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t cm = mx_encode(lo[e], im), cs = mx_encode(step[e], is);
+        wm |= cm << (4 * e);
+        ws |= cs << (4 * e);
+        mf[e] = mx_decode(cm, em);
+        sf[e] = mx_decode(cs, es);
+      }
+      // exponent bytes of the D/32 blocks, gathered in lane q = 0 of each token row
+      uint32_t xm = 0u, xs = 0u;
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) {
+        xm |= static_cast<uint32_t>(__shfl(em + 127, LPT * r + 4 * kb, 64)) << (8 * kb);
+        xs |= static_cast<uint32_t>(__shfl(es + 127, LPT * r + 4 * kb, 64)) << (8 * kb);
+      }
+      if (r == 0) {
+        uint8_t* rm = reinterpret_cast<uint8_t*>(k_min) + blk * mx_record_bytes(D);
+        uint8_t* rs = reinterpret_cast<uint8_t*>(k_scale) + blk * mx_record_bytes(D);
+        *reinterpret_cast<uint32_t*>(rm + 4 * q) = wm;
+        *reinterpret_cast<uint32_t*>(rs + 4 * q) = ws;
+        if (q == 0) {
+          // exponents, then zeros to the end of the record
+          *reinterpret_cast<uint4*>(rm + D / 2) = make_uint4(xm, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(rs + D / 2) = make_uint4(xs, 0u, 0u, 0u);
+        }
+      }
     }
     // code = #{j : y >= m + s (j + 1/2)}; the thresholds rise with j, so for 4-bit codes a
     // binary search over j finds the same count
@@ -263,19 +329,28 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
   for (int x = 0; x < KW; x += 2) *reinterpret_cast<uint2*>(dst + x) = make_uint2(words[x], words[x + 1]);
 }
 
-template <int D, int KB>
+template <int D, int KB, bool MX>
 hipError_t launch_kb(const DeviceTables& tb, const void* k, bool bf16, int hkv, int batch, int64_t t0,
                      int64_t n, int64_t t_cap, uint32_t* kc, uint16_t* km, uint16_t* ks,
                      hipStream_t stream) {
   const int64_t tasks = static_cast<int64_t>(batch) * hkv * (n / kWindow);
   const dim3 grid(static_cast<unsigned>((tasks + kWavesPerBlock - 1) / kWavesPerBlock));
   if (bf16)
-    quantize_keys_kernel<D, KB, true><<<grid, 256, 0, stream>>>(k, hkv, n, t0 / kWindow, t_cap / kWindow,
-                                                                tasks, tb.signs, kc, km, ks);
+    quantize_keys_kernel<D, KB, true, MX><<<grid, 256, 0, stream>>>(k, hkv, n, t0 / kWindow, t_cap / kWindow,
+                                                                    tasks, tb.signs, kc, km, ks);
   else
-    quantize_keys_kernel<D, KB, false><<<grid, 256, 0, stream>>>(k, hkv, n, t0 / kWindow, t_cap / kWindow,
-                                                                 tasks, tb.signs, kc, km, ks);
+    quantize_keys_kernel<D, KB, false, MX><<<grid, 256, 0, stream>>>(k, hkv, n, t0 / kWindow, t_cap / kWindow,
+                                                                     tasks, tb.signs, kc, km, ks);
   return hipGetLastError();
+}
+
+template <bool MX>
+hipError_t launch_meta(const Shape& sh, const DeviceTables& tb, const void* k, bool bf16, int batch, int64_t t0,
+                       int64_t n, int64_t t_cap, uint32_t* kc, uint16_t* km, uint16_t* ks, hipStream_t stream) {
+  if (sh.d == 128 && sh.kbits == 2) return launch_kb<128, 2, MX>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
+  if (sh.d == 128 && sh.kbits == 4) return launch_kb<128, 4, MX>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
+  if (sh.d == 64 && sh.kbits == 2) return launch_kb<64, 2, MX>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
+  return launch_kb<64, 4, MX>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
 }
 
 }  // namespace
@@ -283,10 +358,8 @@ hipError_t launch_kb(const DeviceTables& tb, const void* k, bool bf16, int hkv, 
 hipError_t launch_quantize_keys(const Shape& sh, const DeviceTables& tb, const void* k, bool bf16,
                                 int batch, int64_t t0, int64_t n, int64_t t_cap, uint32_t* kc,
                                 uint16_t* km, uint16_t* ks, hipStream_t stream) {
-  if (sh.d == 128 && sh.kbits == 2) return launch_kb<128, 2>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
-  if (sh.d == 128 && sh.kbits == 4) return launch_kb<128, 4>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
-  if (sh.d == 64 && sh.kbits == 2) return launch_kb<64, 2>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
-  return launch_kb<64, 4>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
+  if (sh.mx) return launch_meta<true>(sh, tb, k, bf16, batch, t0, n, t_cap, kc, km, ks, stream);
+  return launch_meta<false>(sh, tb, k, bf16, batch, t0, n, t_cap, kc, km, ks, stream);
 }
 
 }  // namespace omnikv

@@ -52,6 +52,8 @@
  *   k_codes  uint32 [B][Hkv][T_cap/32][d*key_bits]     key window blocks
  *   k_min    uint16 [B][Hkv][T_cap/32][d]              fp16 m_gc (bit patterns)
  *   k_scale  uint16 [B][Hkv][T_cap/32][d]              fp16 s_gc
+ *            (with key_meta = OMNIKV_META_MXFP4 both are byte records instead,
+ *            [B][Hkv][T_cap/32][R], R = omnikv_key_meta_bytes(); see below)
  *   v_codes  uint32 [B][Hkv][T_cap/32][d*value_bits]   value window blocks
  *   v_scale  uint16 [B][Hkv][T_cap]                    fp16 per-token scale
  *   modality uint8  [B][T_cap]                         0 text, 1 audio, 2 video
@@ -83,6 +85,23 @@
  *   code = #{ j < L : y >= m + s * (j + 1/2) }, the product and the sum each
  *   rounded to fp32 (no fused multiply-add).
  *   Dequantized key: x_hat = R^{-1}(m + s * code), R = c_d H D.
+ *
+ * MXFP4 key metadata (key_meta = OMNIKV_META_MXFP4; the pages' default format,
+ * [paper] §3.1 Implementation details; the fp16 form above is the variant of
+ * [paper] §3.3).  The window's vectors mn and (mx - mn) / L (fp32, as above) are
+ * each cut into blocks of 32 consecutive channels, OCP microscaling style: a
+ * block keeps one E8M0 exponent e = floor(log2 max|x|) - 2, clamped to
+ * [-127, 127] (-127 for an all-zero block), stored as the byte e + 127, and 32
+ * E2M1 codes, x * 2^-e rounded to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with
+ * ties to the even code (larger magnitudes take 6), the sign of x in bit 3.
+ * m and s are the decoded values (E2M1 value * 2^e, exact in fp32); codes and
+ * the dequantized key follow from them by the rules above.  One record per
+ * (b, kv head, window) and vector: d/2 bytes of codes (channel 2i in the low
+ * nibble of byte i), d/32 exponent bytes, zero bytes up to R = 16 *
+ * ceil((d/2 + d/32) / 16) (80 bytes at d = 128, 48 at d = 64).  Reading: the
+ * pages name the format only; blocks run over the channels of one window.
+ * The decode kernel takes m and s as fp16: their decoded values must lie within
+ * fp16 range (|x| <= 65504); smaller than 2^-24 they count as zero there.
  *
  * Value codec (fp32, fixed order):
  *   sigma = sqrt(S / d) with S the stride-halving tree sum of v_i^2 (pairs
@@ -125,7 +144,11 @@ typedef struct {
   int32_t value_bits;     /* 2 or 4 */
   int32_t window;         /* 32 (the key-range group g of [paper] §3.1) */
   int32_t num_modalities; /* M in 1..3: one value rotation per modality */
+  int32_t key_meta;       /* OMNIKV_META_FP16 (0) or OMNIKV_META_MXFP4 (1) */
 } omnikv_config;
+
+/* Storage of the key range metadata m_gc, s_gc. */
+enum { OMNIKV_META_FP16 = 0, OMNIKV_META_MXFP4 = 1 };
 
 /* Create a context.  cfg (host) as above.
  * key_signs (host, int8 [d], each +1 or -1): the diagonal D of the shared
@@ -148,8 +171,12 @@ omnikv_status omnikv_destroy(omnikv_ctx* ctx);
 /* Copy the context's fp16 value codebook (2^value_bits entries) to host memory. */
 omnikv_status omnikv_value_codebook(const omnikv_ctx* ctx, uint16_t* levels /* host */);
 
+/* Bytes of k_min (and of k_scale) per (sequence, KV head, window) in the
+ * context's metadata format: 2 d for fp16, R for MXFP4 (see above). */
+omnikv_status omnikv_key_meta_bytes(const omnikv_ctx* ctx, size_t* bytes /* host */);
+
 /* Quantize keys of tokens [t0, t0+n) of every sequence ([paper] §3.1: 32-token
- * groups; [paper] §3.3: FP16 m_gc and s_gc).
+ * groups; [paper] §3.3: FP16 m_gc and s_gc, or the MXFP4 records of §3.1).
  * k (device): [B][n][Hkv][d] of dtype dt (fp32 or bf16), token-major.
  * t0 % 32 == 0, n % 32 == 0, n > 0, t0 + n <= t_cap, t_cap % 32 == 0.
  * Writes k_codes / k_min / k_scale for windows t0/32 .. (t0+n)/32 - 1 only. */

@@ -35,13 +35,13 @@ def bf16_tensor(x):
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).cuda()
 
 
-def make_context(cfg, key_bits=None, value_bits=None, seed=0):
+def make_context(cfg, key_bits=None, value_bits=None, seed=0, key_meta="fp16"):
     d = cfg.head_dim
     signs = synth.rademacher_signs(d, seed)
     U = synth.value_rotations(d, seed)
     kb = cfg.key_bits if key_bits is None else key_bits
     vb = cfg.value_bits if value_bits is None else value_bits
-    ctx = binding.Context(d, cfg.q_heads, cfg.kv_heads, kb, vb, signs, U)
+    ctx = binding.Context(d, cfg.q_heads, cfg.kv_heads, kb, vb, signs, U, key_meta=key_meta)
     return ctx, signs, U, ctx.value_codebook()
 
 

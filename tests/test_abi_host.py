@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(**kw):
     base = dict(head_dim=128, num_q_heads=16, num_kv_heads=2, key_bits=2, value_bits=2, window=32,
-                num_modalities=3)
+                num_modalities=3, key_meta=binding.META_FP16)
     base.update(kw)
     return binding._Config(*[base[f] for f, _ in binding._Config._fields_])
 
@@ -62,6 +62,7 @@ def _create(cfg, signs=None, rots=None, codebook=None):
     (dict(num_q_heads=32, num_kv_heads=2), binding.EUNSUPPORTED, "8 query heads"),
     (dict(num_modalities=4), binding.EINVAL, "num_modalities"),
     (dict(num_kv_heads=0), binding.EINVAL, "num_kv_heads"),
+    (dict(key_meta=2), binding.EINVAL, "key_meta"),
 ])
 def test_create_rejects_bad_config(kw, status, needle):
     st, h, msg = _create(_cfg(**kw))
@@ -95,6 +96,7 @@ def test_null_context_and_null_out():
     assert L.omnikv_decode_workspace_size(None, 1, 32, 0, ctypes.byref(sz)) == binding.EINVAL
     assert L.omnikv_create(None, None, None, None, None) == binding.EINVAL
     assert L.omnikv_destroy(None) == binding.OK
+    assert L.omnikv_key_meta_bytes(None, ctypes.byref(sz)) == binding.EINVAL
 
 
 def test_stream_schedule_host_function_matches_the_oracle():
