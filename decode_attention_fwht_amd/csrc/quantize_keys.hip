@@ -71,23 +71,10 @@ __device__ __forceinline__ void key_slot(int tau, int s, int j, int& lw, int& bi
 
 constexpr int kWavesPerBlock = 4;
 
-// ---- MXFP4 metadata (OCP microscaling: blocks of 32 elements, one E8M0 exponent, E2M1
-// elements).  Shared exponent of a block whose largest magnitude is amax:
-// floor(log2 amax) - 2, at least -127 (zero and subnormal amax give -127).
-__device__ __forceinline__ int mx_exponent(float amax) {
-  const int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
-  return ef == 0 ? -127 : max(ef - 127 - 2, -127);
-}
-// E2M1 code (sign in bit 3) of x / 2^e, round to nearest with ties to the even code,
-// magnitudes past 6 saturating.  inv = 2^-e exactly, so |x| * inv is exact wherever it
-// can reach a rounding boundary.
-__device__ __forceinline__ uint32_t mx_encode(float x, float inv) {
-  const float v = fabsf(x) * inv;
-  // boundaries between codes c - 1 and c: the midpoints 0.25, 0.75, ..., 5; a midpoint
-  // goes to the even code, so '>' where that is the lower one and '>=' where the upper
-  const uint32_t c = (v > 0.25f) + (v >= 0.75f) + (v > 1.25f) + (v >= 1.75f) + (v > 2.5f) + (v >= 3.5f) +
-                     (v > 5.0f);
-  return c | ((__float_as_uint(x) >> 31) << 3);
+// value of lane l + N within each 16-lane row (0 past the row's end)
+template <int N>
+__device__ __forceinline__ uint32_t row_shl(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x100 + N, 0xF, 0xF, false));
 }
 
 // value of lane l ^ (1 << k) within each 16-lane row (k = 0 .. 3)
@@ -106,6 +93,30 @@ __device__ __forceinline__ float row_xor(float x) {
   } else {  // row_ror:8
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
   }
+}
+
+// ---- MXFP4 metadata (OCP microscaling: blocks of 32 elements, one E8M0 exponent, E2M1
+// elements).  Shared exponent of a block whose largest magnitude is amax:
+// floor(log2 amax) - 2, at least -127 (zero and subnormal amax give -127).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
+  return ef == 0 ? -127 : max(ef - 127 - 2, -127);
+}
+// E2M1 code (sign in bit 3) of x / 2^e, rounded to nearest with ties to the even code and
+// magnitudes past 6 saturating, and its decoded value (E2M1 value times 2^e, exact).
+// inv = 2^-e exactly, so v = |x| * inv is exact wherever it can reach a rounding boundary.
+// Round-to-nearest-even of the significand is rint(v / step) * step with the step of v's
+// binade: 0.5 below 2 (with the subnormal code 0.5), 1 in [2, 4), 2 from 4.
+__device__ __forceinline__ uint32_t mx_encode(float x, float inv, int e, float& value) {
+  const float v = fabsf(x) * inv;
+  const bool b0 = v < 2.0f, b1 = v < 4.0f;
+  const float step = b0 ? 0.5f : (b1 ? 1.0f : 2.0f);
+  const float rstep = b0 ? 2.0f : (b1 ? 1.0f : 0.5f);
+  const float qv = fminf(__builtin_rintf(v * rstep) * step, 6.0f);  // powers of two: exact
+  // code: 2 qv below 1 (0 or 1), else 2 (binade + 1) + mantissa bit = (fp32 bits >> 22) - 252
+  const uint32_t c = qv < 1.0f ? static_cast<uint32_t>(2.0f * qv) : (__float_as_uint(qv) >> 22) - 252u;
+  value = __builtin_copysignf(ldexpf(qv, e), x);
+  return c | ((__float_as_uint(x) >> 31) << 3);
 }
 
 template <int D, int KB, bool BF16, bool MX>
@@ -246,18 +257,19 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
       uint32_t wm = 0u, ws = 0u;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t cm = mx_encode(lo[e], im), cs = mx_encode(step[e], is);
+        const uint32_t cm = mx_encode(lo[e], im, em, mf[e]), cs = mx_encode(step[e], is, es, sf[e]);
         wm |= cm << (4 * e);
         ws |= cs << (4 * e);
-        mf[e] = mx_decode(cm, em);
-        sf[e] = mx_decode(cs, es);
       }
-      // exponent bytes of the D/32 blocks, gathered in lane q = 0 of each token row
-      uint32_t xm = 0u, xs = 0u;
-#pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb) {
-        xm |= static_cast<uint32_t>(__shfl(em + 127, LPT * r + 4 * kb, 64)) << (8 * kb);
-        xs |= static_cast<uint32_t>(__shfl(es + 127, LPT * r + 4 * kb, 64)) << (8 * kb);
+      // exponent bytes of the D/32 blocks, gathered in lane q = 0 of each token (lanes q = 4,
+      // 8, 12 of the same 16-lane row, read by row shifts)
+      const uint32_t bm = static_cast<uint32_t>(em + 127), bs = static_cast<uint32_t>(es + 127);
+      uint32_t xm = bm, xs = bs;
+      xm |= row_shl<4>(bm) << 8;
+      xs |= row_shl<4>(bs) << 8;
+      if constexpr (D == 128) {
+        xm |= (row_shl<8>(bm) << 16) | (row_shl<12>(bm) << 24);
+        xs |= (row_shl<8>(bs) << 16) | (row_shl<12>(bs) << 24);
       }
       if (r == 0) {
         uint8_t* rm = reinterpret_cast<uint8_t*>(k_min) + blk * mx_record_bytes(D);
