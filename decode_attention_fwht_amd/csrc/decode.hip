@@ -1124,7 +1124,7 @@ struct CombineArgs {
   const float* tail_o;       // [unit][8][D]
 };
 
-// One block per (query head, sequence x KV head).  Every global load that depends on
+// One block per (sequence x KV head, query head).  Every global load that depends on
 // nothing is issued first - all of this thread's rotation rows, the first batch of split
 // accumulators, the first 64 splits' maxima, sums and masks - so the kernel waits for
 // memory about once.  Every wave derives the split weights itself (no barrier for them).
@@ -1148,7 +1148,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   __shared__ __attribute__((aligned(16))) float A[J];
   __shared__ float red[KQ][D];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int h = blockIdx.x, unit = blockIdx.y;
+  const int h = blockIdx.y, unit = blockIdx.x;
   if (h >= a.group) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
   const size_t base = static_cast<size_t>(unit) * a.splits;
@@ -1412,7 +1412,10 @@ hipError_t launch_decode_combine(const Shape& sh, const DeviceTables& tb, const 
   CombineArgs ca{tb.rotations_t, sh.hq, sh.hkv, sh.group, sh.modalities, plan.splits, w.ml, w.mask, w.acc, out,
                  w.tail_ml, w.tail_o};
   (void)seq_lens;
-  const dim3 grid(static_cast<unsigned>(sh.group), static_cast<unsigned>(batch * sh.hkv));
+  // units fastest: workgroup i runs on XCD i % 8, and the partial's workgroups of a unit
+  // (split-major grid) ran on XCD unit % 8 when the unit count is a multiple of 8, so each
+  // unit's partials are read where they were written
+  const dim3 grid(static_cast<unsigned>(batch * sh.hkv), static_cast<unsigned>(sh.group));
   if (sh.d == 128) {
     if (!tail) decode_combine_kernel<128, false><<<grid, kCombineThreads, 0, st>>>(ca);
     else decode_combine_kernel<128, true><<<grid, kCombineThreads, 0, st>>>(ca);
