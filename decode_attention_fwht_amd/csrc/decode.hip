@@ -32,6 +32,11 @@
 //   contractions per window with k_min as the operand.
 //   Value levels come from a per-context table of fp16 level pairs indexed by
 //   two packed codes (LDS, conflict-free for 2-bit).
+//   MXFP4 key metadata ([paper] §3.1 Implementation details: the default format)
+//   arrive as per-window records of E2M1 codes and E8M0 block exponents; each wave
+//   expands a window's two records into the fp16 k_scale / k_min areas of its LDS
+//   slot (v_cvt_scalef32_pk_f16_fp4, exact in fp16's range) before the window's
+//   contractions, which are then the same as with fp16 metadata.
 #include <math.h>
 
 #include <atomic>
