@@ -156,7 +156,7 @@ def test_mx_decode_record_sweep(cid, kbits, vbits):
     ctx.close()
 
 
-@pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (5, 2, 2)])
+@pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (4, 2, 2), (4, 4, 4), (5, 2, 2)])
 def test_mx_decode_full_size_sampled(cid, kbits, vbits):
     """The configurations' full sizes, in the launch the benchmark times: records drawn as
     in the sweep, sampled rows against the oracle."""
