@@ -1138,7 +1138,7 @@ struct CombineArgs {
 // stacked (m, k) rows, the groups summed through LDS, then normalised.  For streamed
 // sequences the recent tokens' partial (max, sum, value sums in the original space) joins
 // the merge and is added after the rotation.
-constexpr int kCombineThreads = 1024;
+constexpr int kCombineThreads = 768;
 constexpr int kCombineXB = 32;    // splits per batch of accumulator loads
 constexpr int kMaxSplits = 1024;  // splits per (sequence, KV head)
 
