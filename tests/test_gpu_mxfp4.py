@@ -251,3 +251,55 @@ def test_mx_stream_append_key_flush():
     assert np.array_equal(from_dev(cache["k_scale"], np.uint8)[:, :, :nw], oks)
     assert np.array_equal(from_dev(cache["k_codes"], np.uint32)[:, :, :nw], okc)
     ctx.close()
+
+
+def test_mx_decode_split_invariance():
+    import torch
+    cfg = synth.CONFIGS[2]
+    T = 10240
+    say("[mx-split-invariance] cfg2")
+    ctx, signs, U, lv = make_context(cfg, key_meta="mxfp4")
+    cache = cache_to_device(_record_sweep_cache(cfg, T, 2, 2, 31))
+    q = to_dev(synth.queries(cfg, 7) * np.float32(0.05))
+    lens = to_dev(np.array([T - 3], np.int32))
+    outs = [from_dev(ctx.decode(q, lens, T, cache, num_splits=s)) for s in (1, 3, 0, 64, 320)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert row_errors(o, outs[0]).max() < 3e-5
+    ctx.close()
+
+
+def test_mx_decode_graph_replay_matches_eager():
+    """The MXFP4 decode step captured in a HIP graph gives the eager result bit for bit
+    on every replay, with eager work between replays."""
+    import torch
+    cfg = synth.CONFIGS[2]
+    T = 4096
+    say("[mx-graph-replay] cfg2")
+    ctx, signs, U, lv = make_context(cfg, key_meta="mxfp4")
+    caches = [cache_to_device(_record_sweep_cache(cfg, T, 2, 2, 40 + i)) for i in range(2)]
+    q = to_dev(synth.queries(cfg, 5) * np.float32(0.05))
+    lens = to_dev(np.array([T - 9], np.int32))
+    ws = torch.empty(ctx.workspace_size(cfg.batch, T), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((cfg.batch, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+            for _ in range(2)]
+    eager = []
+    for i in range(2):
+        ctx.decode(q, lens, T, caches[i], out=outs[i], workspace=ws)
+        eager.append(outs[i].clone())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(2):
+            ctx.decode_partial(q, lens, T, caches[i], ws)
+            ctx.decode_combine(lens, cfg.batch, T, ws, outs[i])
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+        ctx.decode(q, lens, T, caches[(rep + 1) % 2])
+        torch.cuda.synchronize()
+    ctx.close()
