@@ -305,7 +305,7 @@ struct Lds {
   static constexpr int LEN = QRAW + SGN;         // then the length (4 bytes, 16 reserved)
   static constexpr int TAB_OFF = LEN + 16;       // then the level-pair table
   static constexpr int TAB = 4 << (2 * VB);
-  static constexpr int MERGE = kWaves * kMaxModalities * kMaxGroup * D * 4;
+  static constexpr int MERGE = kWaves * kMaxModalities * kMaxGroup * (D + 16) * 4;  // padded rows
   static constexpr int STATIC = kMaxGroup * D * 4 + TAB + 1024;  // q_lds, the table, small arrays
   static constexpr int dyn(int ring) {
     const int r = kWaves * ring * Slot<D, KB, VB, MX>::BYTES;
@@ -1056,12 +1056,15 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   // barrier.
   wait_vmcnt<0>();
   __shared__ float2 ml_lds[kWaves][kMaxGroup];
-  __shared__ uint32_t seen_lds[kWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t seen_lds[kWaves];
   const float l = group_sum(l_part);
   if (lane < kMaxGroup) ml_lds[wave][lane] = make_float2(m_ref, l);  // lane < 8: column = head
   if (lane == 0) seen_lds[wave] = seen;
   __syncthreads();
-  constexpr int RES = kMaxModalities * kMaxGroup * D;  // floats per wave
+  // rows of D + 16 floats: the 32 lanes of a staging write (8 heads x 4 channel quads)
+  // then cover the 64 banks twice, where unpadded rows put all 8 heads on 16 banks
+  constexpr int DP = D + 16;
+  constexpr int RES = kMaxModalities * kMaxGroup * DP;  // floats per wave
   {
     float* const res = reinterpret_cast<float*>(ring_mem) + wave * RES;
     // modality m lives in accumulator A (audio: half 0, video: half 1) or B (text: half 0);
@@ -1070,7 +1073,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       if (((seen >> m) & 1u) && part == half) {
 #pragma unroll
         for (int u = 0; u < NU; ++u)
-          *reinterpret_cast<float4_t*>(res + (m * kMaxGroup + h) * D + 16 * u + 4 * g) = X[u];
+          *reinterpret_cast<float4_t*>(res + (m * kMaxGroup + h) * DP + 16 * u + 4 * g) = X[u];
       }
     };
     stage(0, accB, 0);
@@ -1079,26 +1082,37 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   }
   __syncthreads();
   const size_t pidx = static_cast<size_t>(unit) * a.splits + split;
-  uint32_t present = 0u;
-#pragma unroll
-  for (int v = 0; v < kWaves; ++v) present |= seen_lds[v];
+  // every LDS read of the merge is unconditional and independent, so they are all in
+  // flight together; what a wave did not stage (garbage) is dropped by a select
+  const uint4 seen4 = *reinterpret_cast<const uint4*>(seen_lds);
+  const uint32_t seen_v[kWaves] = {seen4.x, seen4.y, seen4.z, seen4.w};
+  const uint32_t present = seen4.x | seen4.y | seen4.z | seen4.w;
   if (tid == 0) a.ws_mask[pidx] = present;
   const int e4 = 4 * tid;  // four consecutive elements of [head][D] per thread
   if (e4 < a.group * D) {
-    const int hh = e4 / D;
+    const int hh = e4 / D, c4 = e4 % D;
+    float2 mlv[kWaves];
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) mlv[v] = ml_lds[v][hh];
+    float4_t xs[kMaxModalities][kWaves];
+#pragma unroll
+    for (int m = 0; m < kMaxModalities; ++m)
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v)
+        if ((present >> m) & 1u)
+          xs[m][v] = *reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(ring_mem) + v * RES +
+                                                        (m * kMaxGroup + hh) * DP + c4);
     // the factors that bring each wave's sums to the block's max
     float mb = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-      if (ml_lds[v][hh].y > 0.0f) mb = fmaxf(mb, ml_lds[v][hh].x);
+    for (int v = 0; v < kWaves; ++v) mb = fmaxf(mb, mlv[v].y > 0.0f ? mlv[v].x : -INFINITY);
     float fac[kWaves];
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) fac[v] = ml_lds[v][hh].y > 0.0f ? exp2f(ml_lds[v][hh].x - mb) : 0.0f;
-    if (e4 % D == 0) {
+    for (int v = 0; v < kWaves; ++v) fac[v] = mlv[v].y > 0.0f ? exp2f(mlv[v].x - mb) : 0.0f;
+    if (c4 == 0) {
       float lsum = 0.0f;
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v)
-        if (ml_lds[v][hh].y > 0.0f) lsum += fac[v] * ml_lds[v][hh].y;
+      for (int v = 0; v < kWaves; ++v) lsum += mlv[v].y > 0.0f ? fac[v] * mlv[v].y : 0.0f;
       a.ws_ml[pidx * kMaxGroup + hh] = make_float2(mb, lsum);
     }
 #pragma unroll
@@ -1107,10 +1121,9 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       float4_t sum = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
-        if (!((seen_lds[v] >> m) & 1u)) continue;
-        const float4_t x = *reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(ring_mem) + v * RES +
-                                                             m * kMaxGroup * D + e4);
-        sum += x * fac[v];
+        const float4_t t = xs[m][v] * fac[v];
+        const bool on = (seen_v[v] >> m) & 1u;
+        sum += float4_t{on ? t[0] : 0.f, on ? t[1] : 0.f, on ? t[2] : 0.f, on ? t[3] : 0.f};
       }
       *reinterpret_cast<float4_t*>(a.ws_acc + (pidx * kMaxModalities + m) * kMaxGroup * D + e4) = sum;
     }
