@@ -1142,15 +1142,17 @@ struct CombineArgs {
   const float* tail_o;       // [unit][8][D]
 };
 
-// One block per (sequence x KV head, query head).  Every global load that depends on
-// nothing is issued first - all of this thread's rotation rows, the first batch of split
-// accumulators, the first 64 splits' maxima, sums and masks - so the kernel waits for
-// memory about once.  Every wave derives the split weights itself (no barrier for them).
+// One block per (sequence x KV head, query head).  Loads that depend on nothing are issued
+// first, in the order they are used: the first 64 splits' maxima, sums and masks, the
+// first batch of split accumulators, then the thread's rotation rows.  Loads complete in
+// issue order, and there are few enough of them (about 50) for the waits to name each one,
+// so the merge starts as soon as its inputs are in.  Every wave derives the split weights
+// itself (no barrier for them).
 // (1) log-sum-exp merge of the splits' rotated-space accumulators, one (m, k) item per
-// thread, into LDS; (2) out = sum_m U_m A_m, each thread a column c over one group of
-// stacked (m, k) rows, the groups summed through LDS, then normalised.  For streamed
-// sequences the recent tokens' partial (max, sum, value sums in the original space) joins
-// the merge and is added after the rotation.
+// thread, into LDS; (2) out = sum_m U_m A_m, each thread four adjacent columns over one
+// group of stacked (m, k) rows (one coalesced 16-byte load per row), the groups summed
+// through LDS, then normalised.  For streamed sequences the recent tokens' partial (max,
+// sum, value sums in the original space) joins the merge and is added after the rotation.
 constexpr int kCombineThreads = 768;
 constexpr int kCombineXB = 32;    // splits per batch of accumulator loads
 constexpr int kMaxSplits = 1024;  // splits per (sequence, KV head)
@@ -1159,46 +1161,54 @@ constexpr int kMaxSplits = 1024;  // splits per (sequence, KV head)
 template <int D, bool STREAM>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a) {
   constexpr int J = kMaxModalities * D;       // stacked rotation rows (m, k)
-  constexpr int KQ = kCombineThreads / D;     // row groups
+  constexpr int CQ = D / 4;                   // threads per row group (4 columns each)
+  constexpr int KQ = kCombineThreads / CQ;    // row groups
   constexpr int JPG = J / KQ;                 // rows per group
   static_assert(J % KQ == 0 && JPG % 4 == 0 && J <= kCombineThreads, "combine tiling");
   constexpr int PSTRIDE = kMaxModalities * kMaxGroup * D;  // floats per split
   __shared__ __attribute__((aligned(16))) float A[J];
-  __shared__ float red[KQ][D];
+  __shared__ __attribute__((aligned(16))) float red[KQ][D];
   const int tid = threadIdx.x, lane = tid & 63;
   const int h = blockIdx.y, unit = blockIdx.x;
   if (h >= a.group) return;
   const int b = unit / a.hkv, kvh = unit % a.hkv;
   const size_t base = static_cast<size_t>(unit) * a.splits;
   const int S = a.splits;
-  const int c = tid % D, kq = tid / D;
   const int jrows = a.modalities * D;
-
-  // ---- loads that depend on nothing
-  const int j0 = kq * JPG;
-  const float* up = a.rotations_t + static_cast<size_t>(j0) * D + c;
-  const bool merger = tid < jrows;  // item (m, k) = (tid / D, tid % D)
+  // merge item (m, k) = (tid / D, tid % D); rotation: columns 4 c4 .. 4 c4 + 3 over the
+  // JPG rows of group kq
+  const bool merger = tid < jrows;
   const int im = tid / D;
-  const float* src = a.ws_acc + base * PSTRIDE + (im * kMaxGroup + h) * D + c;
-  float u[JPG];
-  float x[kCombineXB];
-  // lane t: split t's (max, sum) and modality mask (splits 64.. are read in the loop)
+  const int c4 = tid % CQ, kq = tid / CQ;
+  const int j0 = kq * JPG;
+
+  // ---- loads that depend on nothing, in the order they are used (loads complete in issue
+  // order): lane t's split t (max, sum) and modality mask (splits 64.. are read in the
+  // loop), the first batch of split accumulators, then this thread's rotation rows - one
+  // 16-byte load per row, coalesced across the row - so the merge and its barrier overlap
+  // the rows still in flight
   float2 ml0 = make_float2(-INFINITY, 0.0f);
   uint32_t mk0 = 0u;
-#pragma unroll
-  for (int i = 0; i < JPG; ++i) u[i] = (j0 + i < jrows) ? up[static_cast<size_t>(i) * D] : 0.0f;
-#pragma unroll
-  for (int t = 0; t < kCombineXB; ++t) x[t] = (merger && t < S) ? src[static_cast<size_t>(t) * PSTRIDE] : 0.0f;
   if (lane < S) {
     ml0 = a.ws_ml[(base + lane) * kMaxGroup + h];
     mk0 = a.ws_mask[base + lane];
   }
+  const float* src = a.ws_acc + base * PSTRIDE + (im * kMaxGroup + h) * D + (tid % D);
+  float x[kCombineXB];
+#pragma unroll
+  for (int t = 0; t < kCombineXB; ++t) x[t] = (merger && t < S) ? src[static_cast<size_t>(t) * PSTRIDE] : 0.0f;
+  // rows past the context's modalities read its spare rotation slots (copies of U_0, finite)
+  // and meet zeros in A
+  const float* up = a.rotations_t + static_cast<size_t>(j0) * D + 4 * c4;
+  float4 u[JPG];
+#pragma unroll
+  for (int i = 0; i < JPG; ++i) u[i] = *reinterpret_cast<const float4*>(up + static_cast<size_t>(i) * D);
   // streamed sequences: the recent tokens' (max, sum) and, for row group 0, value sums
   float2 tml = make_float2(-INFINITY, 0.0f);
-  float to = 0.0f;
+  float4 to = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (STREAM) {
     tml = a.tail_ml[static_cast<size_t>(unit) * kMaxGroup + h];
-    if (kq == 0) to = a.tail_o[(static_cast<size_t>(unit) * kMaxGroup + h) * D + c];
+    if (kq == 0) to = *reinterpret_cast<const float4*>(a.tail_o + (static_cast<size_t>(unit) * kMaxGroup + h) * D + 4 * c4);
   }
   const float tmx = tml.y > 0.0f ? tml.x : -INFINITY;
 
@@ -1260,28 +1270,33 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   if (tid < J) A[tid] = merger ? acc : 0.0f;
   // ---- streamed sequences: probabilities of the recent tokens and their values, which
   // are in the original space (added after the inverse rotation)
-  float ot = 0.0f;
+  float4 ot = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (STREAM) {
     if (tml.y > 0.0f) {
       const float wt = exp2f(tml.x - mx);
       lsum += wt * tml.y;
-      ot = wt * to;
+      ot = make_float4(wt * to.x, wt * to.y, wt * to.z, wt * to.w);
     }
   }
   const float inv_l = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   __syncthreads();
 
-  // ---- (2) rotation over this thread's row group
-  float o = 0.0f;
+  // ---- (2) rotation over this thread's row group: four columns
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int i = 0; i < JPG; i += 4) {
     const float4 av = *reinterpret_cast<const float4*>(&A[j0 + i]);
-    o = fmaf(u[i], av.x, o);
-    o = fmaf(u[i + 1], av.y, o);
-    o = fmaf(u[i + 2], av.z, o);
-    o = fmaf(u[i + 3], av.w, o);
+    const float ai[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      o.x = fmaf(u[i + r].x, ai[r], o.x);
+      o.y = fmaf(u[i + r].y, ai[r], o.y);
+      o.z = fmaf(u[i + r].z, ai[r], o.z);
+      o.w = fmaf(u[i + r].w, ai[r], o.w);
+    }
   }
-  red[kq][c] = o + ot;
+  *reinterpret_cast<float4*>(&red[kq][4 * c4]) =
+      make_float4(o.x + ot.x, o.y + ot.y, o.z + ot.z, o.w + ot.w);
   __syncthreads();
   if (tid < D) {
     float r = 0.0f;
