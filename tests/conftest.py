@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped, not failed, on a host without a GPU when they are
-    # collected together with CPU tests (the round-end runner selects -m gpu on a GPU machine).
+    # collected together with CPU tests (select them with -m gpu on an MI355X).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
