@@ -1226,31 +1226,10 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
   // split without modality m left that block unwritten: the mask selects, it never
   // multiplies.
   float acc = 0.0f, lsum = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    float2 ml = ml0;
-    uint32_t mk = mk0;
-    if (s0 > 0) {
-      ml = make_float2(-INFINITY, 0.0f);
-      mk = 0u;
-      if (s0 + lane < S) {
-        ml = a.ws_ml[(base + s0 + lane) * kMaxGroup + h];
-        mk = a.ws_mask[base + s0 + lane];
-      }
-    }
-    float w = 0.0f;
-    if (ml.y > 0.0f) {
-      w = exp2f(ml.x - mx);
-      lsum += w * ml.y;
-    }
-    // splits 0 .. kCombineXB - 1 were loaded up front; later ones 8 at a time
-#pragma unroll
-    for (int t = 0; t < kCombineXB; ++t) {
-      if (s0 > 0 || t >= S) break;
-      const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t));
-      const uint32_t ms = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mk), t));
-      if ((ms >> im) & 1u) acc = fmaf(ws, x[t], acc);
-    }
-    for (int sb = s0 == 0 ? kCombineXB : s0; sb < min(S, s0 + 64); sb += 8) {
+  // splits s0 .. s0 + 63 with lane t's weight w and mask mk; the first kCombineXB of all were
+  // loaded up front, the rest are read 8 at a time
+  auto merge_rest = [&](int s0, float w, uint32_t mk, int from) {
+    for (int sb = from; sb < min(S, s0 + 64); sb += 8) {
       float y[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) y[t] = (merger && sb + t < S) ? src[static_cast<size_t>(sb + t) * PSTRIDE] : 0.0f;
@@ -1263,6 +1242,40 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
         const uint32_t ms = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mk), li));
         if ((ms >> im) & 1u) acc = fmaf(ws, y[t], acc);
       }
+    }
+  };
+  {
+    // the first 64 splits, straight-line: a loop here would carry a wait for every load in
+    // flight (the rotation rows included) into its first iteration
+    float w = 0.0f;
+    if (ml0.y > 0.0f) {
+      w = exp2f(ml0.x - mx);
+      lsum += w * ml0.y;
+    }
+#pragma unroll
+    for (int t = 0; t < kCombineXB; ++t) {
+      if (t < S) {
+        const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t));
+        const uint32_t ms = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mk0), t));
+        if ((ms >> im) & 1u) acc = fmaf(ws, x[t], acc);
+      }
+    }
+    if (S > kCombineXB) merge_rest(0, w, mk0, kCombineXB);
+  }
+  if (S > 64) {
+    for (int s0 = 64; s0 < S; s0 += 64) {
+      float2 ml = make_float2(-INFINITY, 0.0f);
+      uint32_t mk = 0u;
+      if (s0 + lane < S) {
+        ml = a.ws_ml[(base + s0 + lane) * kMaxGroup + h];
+        mk = a.ws_mask[base + s0 + lane];
+      }
+      float w = 0.0f;
+      if (ml.y > 0.0f) {
+        w = exp2f(ml.x - mx);
+        lsum += w * ml.y;
+      }
+      merge_rest(s0, w, mk, s0);
     }
   }
 #pragma unroll
