@@ -113,15 +113,19 @@ DECODE_SOURCE = os.path.join(ROOT, "decode_attention_fwht_amd", "csrc", "decode.
 
 
 def decode_code_sha256(path: str = None) -> str:
-    """sha256 of the decode source with comments and blank lines removed: a change to
-    the kernel's code changes it, a change to its comments does not."""
+    """sha256 of the decode source with comments and blank lines removed, and of its build
+    flags: a change to the kernel's code or to how it is compiled changes it, a change to
+    its comments does not."""
     import hashlib
     import re
+    from decode_attention_fwht_amd import build as _build
     text = open(path or DECODE_SOURCE).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
     code = "\n".join(ln for ln in lines if ln.strip())
-    return hashlib.sha256(code.encode()).hexdigest()
+    # the flags without the include directories (their absolute paths depend on the checkout)
+    flags = " ".join(f for f in _build.FLAGS + _build.EXTRA.get("decode.hip", []) if f != "-I" and "/" not in f)
+    return hashlib.sha256((code + "\n" + flags).encode()).hexdigest()
 
 
 def measured_traffic(workload: str):

@@ -17,7 +17,10 @@ SOURCES = ["api.hip", "quantize_keys.hip", "quantize_values.hip", "decode.hip", 
 # The decode kernel keeps its matrix-core accumulators in ordinary VGPRs: with the
 # accumulation-register form the compiler shuttles all of them between register files
 # every window.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# decode.hip: matrix-core results in ordinary VGPRs, and the scheduler strategy that maximizes
+# instruction-level parallelism (the decode partial is bound by instruction issue at two waves
+# per SIMD; this ordering measured ~2 us faster per launch at 16 x 32k tokens, same results)
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
