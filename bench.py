@@ -6,14 +6,18 @@ omnikv_decode_combine) over every cached token of every sequence.  The packed
 caches are built before timing by the library's own write path (keys and values
 of synthetic drifting K/V, quantized in prefill-sized chunks), and several
 independent caches are cycled so that a step never finds its cache in the 256 MB
-Infinity Cache: the timed bytes come from HBM.  The K timed steps are captured in
-one HIP graph and replayed once between two synchronisations (two short kernels per
-step would otherwise wait on Python launch overhead); the per-kernel averages come
-from graphs of K partial-only and K combine-only launches.  The write path itself is
-timed separately on one prefill chunk per sequence and reported under "write_path".
+Infinity Cache: the timed bytes come from HBM.
+
+Timing.  The K timed steps are captured in one HIP graph (two short kernels per step
+would otherwise wait on Python launch overhead).  The headline is one replay of that
+graph between two synchronisations: exactly K steps.  The spread (median / p10 / p90
+per step) comes from further replays of the same graph, each bracketed by events; the
+per-kernel figures from graphs of K partial-only and K combine-only launches, replayed
+the same way.  The write path is timed separately on one prefill chunk per sequence.
 
 Prints one JSON line: the headline (effective KV GB/s of the decode step), the
-roofline of the partial kernel, the write-path timings and a CPU-oracle
+roofline of the partial kernel, the write-path timings, the other configurations
+(configs 4 and 5 at K2V2 and K4V4, the config-5 prefill write path) and a CPU-oracle
 baseline on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -151,11 +155,12 @@ def cpu_baseline(cfg, kbits, vbits, budget_s=15.0, seed=11):
     sample of the same workload: whole (sequence, KV head) units of a synthetic
     packed cache of this configuration's shape, until the time budget is spent."""
     from oracle import omnikv_oracle as O
+    cores = len(os.sched_getaffinity(0))   # the host cores this process may run on
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        blas_threads = 1
     d = cfg.head_dim
     signs = synth.rademacher_signs(d, seed)
     U = synth.value_rotations(d, seed)
@@ -183,7 +188,120 @@ def cpu_baseline(cfg, kbits, vbits, budget_s=15.0, seed=11):
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done_units} of {cfg.batch * cfg.kv_heads} (sequence, KV head) units at "
                       f"{cfg.context} tokens, {cfg.group} query heads each, float64 brute force "
-                      f"({t_used:.1f} s)"}
+                      f"({t_used:.1f} s; numpy, its BLAS on {blas_threads} threads)"}
+
+
+def _graph(fn, n):
+    """One HIP graph holding fn(0) .. fn(n - 1)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    return g
+
+
+def _replay_ms(g, reps):
+    """Milliseconds of each of `reps` replays of g, each bracketed by events on the stream the
+    graph runs on (the current stream)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for r in range(reps):
+        g.replay()
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
+
+
+def _spread(us):
+    a = np.asarray(us, np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "samples": int(a.size)}
+
+
+def time_decode(ctx, cfg, caches, alg, steps, warmup, replays, splits=0):
+    """Decode-step timings over the cycled caches.  One step = omnikv_decode_partial +
+    omnikv_decode_combine over every cached token of the batch.
+
+    head: one replay of a graph of `steps` steps, bracketed by synchronizations (the headline
+    timed region: exactly `steps` steps).  spread: `replays` further replays of the same graph,
+    each timed by events; a sample is the replay's time / steps.  partial / combine: graphs of
+    `steps` launches of one kernel each, replayed `replays` times, medians per launch."""
+    import torch
+    nbuf = len(caches)
+    B, T, d = cfg.batch, cfg.context, cfg.head_dim
+    q = torch.from_numpy(synth.queries(cfg, 1)).cuda()
+    lens = torch.from_numpy(np.full(B, T, np.int32)).cuda()
+    ws = torch.empty(ctx.workspace_size(B, T, splits), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, cfg.q_heads, d), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        c = caches[i % nbuf]
+        ctx.decode_partial(q, lens, T, c, ws, num_splits=splits)
+        ctx.decode_combine(lens, B, T, ws, out, num_splits=splits)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g_step = _graph(lambda i: step(warmup + i), steps)
+    g_part = _graph(lambda i: ctx.decode_partial(q, lens, T, caches[i % nbuf], ws, num_splits=splits), steps)
+    g_comb = _graph(lambda i: ctx.decode_combine(lens, B, T, ws, out, num_splits=splits), steps)
+    g_step.replay()  # untimed first replay
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    g_step.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    head_ms = e0.elapsed_time(e1)
+    spread = [ms * 1e3 / steps for ms in _replay_ms(g_step, replays)]
+    part = [ms * 1e3 / steps for ms in _replay_ms(g_part, replays)]
+    comb = [ms * 1e3 / steps for ms in _replay_ms(g_comb, replays)]
+    del g_step, g_part, g_comb
+    us_head = head_ms * 1e3 / steps
+    us_med = float(np.median(spread))
+    part_med = float(np.median(part))
+    return {
+        "head_ms": head_ms, "wall_s": wall, "us_per_step": us_head,
+        "step_us": _spread(spread),
+        "GBps_median": round(alg / (us_med * 1e-6) / 1e9, 1),
+        "pct_of_hbm_peak_median": round(100 * alg / (us_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "kernels_us": {"decode_partial": _spread(part), "decode_combine": _spread(comb)},
+        "partial_frac_of_peak": round(alg / (part_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "partial_us_median": part_med,
+        "q": q, "lens": lens, "ws": ws, "out": out,
+    }
+
+
+def decode_config(cid, kbits, vbits, key_meta, steps, warmup, replays, buffers=0):
+    """Build this configuration's caches with the write path and time its decode step."""
+    import torch
+    cfg = synth.CONFIGS[cid]
+    d = cfg.head_dim
+    ctx = binding.Context(d, cfg.q_heads, cfg.kv_heads, kbits, vbits, synth.rademacher_signs(d, 0),
+                          synth.value_rotations(d, 0), key_meta=key_meta)
+    lens_np = np.full(cfg.batch, cfg.context, np.int32)
+    alg = algorithmic_bytes(cfg, kbits, vbits, lens_np, key_meta)
+    nbuf = buffers or max(2, math.ceil(2.5 * MALL_BYTES / alg))
+    caches, _ = build_caches(ctx, cfg, nbuf, kbits, vbits)
+    r = time_decode(ctx, cfg, caches, alg, steps, warmup, replays)
+    res = {"workload": f"{cfg.name} decode step (config {cid})", "codec": f"K{kbits}V{vbits}",
+           "key_meta": key_meta, "batch": cfg.batch, "q_heads": cfg.q_heads, "kv_heads": cfg.kv_heads,
+           "context": cfg.context, "algorithmic_bytes_per_step": int(alg), "cache_buffers": nbuf,
+           "step_us": r["step_us"], "GBps_median": r["GBps_median"],
+           "pct_of_hbm_peak_median": r["pct_of_hbm_peak_median"], "kernels_us": r["kernels_us"],
+           "partial_frac_of_peak": r["partial_frac_of_peak"]}
+    del caches, r
+    ctx.close()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -191,12 +309,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replays", type=int, default=30, help="timed replays of the step graph for the spread")
     ap.add_argument("--config", type=int, default=3, help="workload id (default 3: 16 x 32k, 16Q/2KV/d128)")
     ap.add_argument("--kbits", type=int, default=2)
     ap.add_argument("--vbits", type=int, default=2)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--buffers", type=int, default=0, help="independent caches cycled (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the other configurations (configs 4 and 5, K2V2 and K4V4, and the config-5 write path)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run a plain device copy (out = 1 * in, fp32) of this many MiB, the "
@@ -221,91 +342,30 @@ def main():
     nbuf = args.buffers or max(2, math.ceil(2.5 * MALL_BYTES / alg))
     caches, tags_np = build_caches(ctx, cfg, nbuf, args.kbits, args.vbits)
     write_path = time_write_path(ctx, cfg, tags_np)
-
-    q = torch.from_numpy(synth.queries(cfg, 1)).cuda()
-    lens = torch.from_numpy(lens_np).cuda()
     T = cfg.context
-    ws = torch.empty(ctx.workspace_size(cfg.batch, T, args.splits), dtype=torch.uint8, device="cuda")
-    out = torch.empty((cfg.batch, cfg.q_heads, d), dtype=torch.float32, device="cuda")
 
-    def step(i):
-        c = caches[i % nbuf]
-        ctx.decode_partial(q, lens, T, c, ws, num_splits=args.splits)
-        ctx.decode_combine(lens, cfg.batch, T, ws, out, num_splits=args.splits)
+    r = time_decode(ctx, cfg, caches, alg, args.steps, args.warmup, args.replays, args.splits)
+    q, lens, ws, out = r["q"], r["lens"], r["ws"], r["out"]
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # The timed work is replayed from HIP graphs: one decode step is two short kernels, and
-    # launching them one by one from Python would leave the GPU waiting for the host.
-    def capture(fn, n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i)
-        return g
-
-    def timed_replay(g):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        stream = torch.cuda.current_stream()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1), time.perf_counter() - t0
-
-    g_step = capture(lambda i: step(args.warmup + i), args.steps)
-    g_part = capture(lambda i: ctx.decode_partial(q, lens, T, caches[i % nbuf], ws, num_splits=args.splits),
-                     args.steps)
-    g_comb = capture(lambda i: ctx.decode_combine(lens, cfg.batch, T, ws, out, num_splits=args.splits),
-                     args.steps)
     # the same step for streamed sequences: the last stream_value_packed tokens (the
     # 128-token sliding value window) come from rings of recent tokens
     rings = ctx.alloc_rings(cfg.batch, 256)
     rings["k"].normal_()
     rings["v"].normal_()
-    g_stream = capture(lambda i: ctx.decode_streaming(q, lens, T, caches[i % nbuf], rings, out=out, workspace=ws,
-                                                      num_splits=args.splits), args.steps)
-    g_step.replay()  # untimed first replay
+    g_stream = _graph(lambda i: ctx.decode_streaming(q, lens, T, caches[i % nbuf], rings, out=out, workspace=ws,
+                                                     num_splits=args.splits), args.steps)
     g_stream.replay()
     torch.cuda.synchronize()
-    step_ms, wall = timed_replay(g_step)
-    part_ms, _ = timed_replay(g_part)
-    comb_ms, _ = timed_replay(g_comb)
-    stream_ms, _ = timed_replay(g_stream)
+    stream_us = [ms * 1e3 / args.steps for ms in _replay_ms(g_stream, max(5, args.replays // 3))]
+    del g_stream
 
     # the same step with MXFP4 key metadata (the paper's default format): its own context
     # and caches, enough of them to exceed the MALL
-    ctx_mx = binding.Context(d, cfg.q_heads, cfg.kv_heads, args.kbits, args.vbits, signs, U, key_meta="mxfp4")
-    alg_mx = algorithmic_bytes(cfg, args.kbits, args.vbits, lens_np, key_meta="mxfp4")
-    nbuf_mx = args.buffers or max(2, math.ceil(2.5 * MALL_BYTES / alg_mx))
-    caches_mx, _ = build_caches(ctx_mx, cfg, nbuf_mx, args.kbits, args.vbits)
-    ws_mx = torch.empty(ctx_mx.workspace_size(cfg.batch, T, args.splits), dtype=torch.uint8, device="cuda")
-
-    def step_mx(i):
-        c = caches_mx[i % nbuf_mx]
-        ctx_mx.decode_partial(q, lens, T, c, ws_mx, num_splits=args.splits)
-        ctx_mx.decode_combine(lens, cfg.batch, T, ws_mx, out, num_splits=args.splits)
-
-    for i in range(args.warmup):
-        step_mx(i)
-    g_mx = capture(lambda i: step_mx(args.warmup + i), args.steps)
-    g_mx_part = capture(lambda i: ctx_mx.decode_partial(q, lens, T, caches_mx[i % nbuf_mx], ws_mx,
-                                                        num_splits=args.splits), args.steps)
-    g_mx.replay()
-    torch.cuda.synchronize()
-    mx_ms, _ = timed_replay(g_mx)
-    mx_part_ms, _ = timed_replay(g_mx_part)
-    del caches_mx, g_mx, g_mx_part
-    ctx_mx.close()
+    mx = decode_config(args.config, args.kbits, args.vbits, "mxfp4", args.steps, args.warmup,
+                       max(5, args.replays // 3), args.buffers)
     kp, vp = binding.Context.stream_packed_lengths(T)
-    ms_per_step = step_ms / args.steps
-    us_step_med = ms_per_step * 1e3
-    part_avg_s = part_ms / args.steps / 1e3
-
+    ms_per_step = r["head_ms"] / args.steps
+    part_avg_s = r["partial_us_median"] * 1e-6
     value = alg / (ms_per_step / 1e3) / 1e9
     achieved = alg / part_avg_s / 1e9
     res = {
@@ -324,26 +384,35 @@ def main():
         "config": {
             "workload": f"{cfg.name} decode step (config {cfg.cid})",
             "batch": cfg.batch, "q_heads": cfg.q_heads, "kv_heads": cfg.kv_heads, "head_dim": d,
-            "context": cfg.context, "codec": f"K{args.kbits}V{args.vbits}", "window": 32,
+            "context": cfg.context, "codec": f"K{args.kbits}V{args.vbits}", "key_meta": "fp16", "window": 32,
             "cache_buffers": nbuf, "algorithmic_bytes_per_step": int(alg),
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
-        "wall_s_timed_region": round(wall, 6),
+        "step_us": r["step_us"],
+        "wall_s_timed_region": round(r["wall_s"], 6),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "kernels_us": {"decode_partial_avg": round(part_avg_s * 1e6, 2),
-                       "decode_combine_avg": round(comb_ms / args.steps * 1e3, 2)},
+        "kernels_us": r["kernels_us"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(f"{cfg.name} K{args.kbits}V{args.vbits} splits {args.splits}")},
         "write_path": write_path,
-        "streaming": {"us_per_step": round(stream_ms / args.steps * 1e3, 2),
-                      "recent_tokens_per_sequence": T - vp, "packed_key_tokens": kp},
-        "key_meta_mxfp4": {"us_per_step": round(mx_ms / args.steps * 1e3, 2),
-                           "decode_partial_avg_us": round(mx_part_ms / args.steps * 1e3, 2),
-                           "algorithmic_bytes_per_step": int(alg_mx),
-                           "GBps": round(alg_mx / (mx_ms / args.steps / 1e3) / 1e9, 1),
-                           "cache_buffers": nbuf_mx},
+        "streaming": {"step_us": _spread(stream_us), "recent_tokens_per_sequence": T - vp, "packed_key_tokens": kp},
+        "key_meta_mxfp4": mx,
     }
+    del caches, rings, r, q, lens, ws, out
+    ctx.close()
+    torch.cuda.empty_cache()
+    if not args.no_other_configs:
+        others = {}
+        for cid, kb, vb in ((4, 2, 2), (4, 4, 4), (5, 2, 2), (5, 4, 4)):
+            others[f"config{cid}_K{kb}V{vb}"] = decode_config(cid, kb, vb, "fp16", 10, 3, 10)
+        cfg5 = synth.CONFIGS[5]
+        ctx5 = binding.Context(cfg5.head_dim, cfg5.q_heads, cfg5.kv_heads, 2, 2, signs, U)
+        others["config5_prefill_write_K2V2"] = time_write_path(ctx5, cfg5, synth.modality_layout(cfg5, 0, cfg5.prefill),
+                                                               reps=10)
+        ctx5.close()
+        torch.cuda.empty_cache()
+        res["configs"] = others
     if args.copy_reference_mib:
         n = args.copy_reference_mib * (1 << 20) // 4
         src = torch.rand(n, device="cuda")

@@ -52,7 +52,27 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
-constexpr float kLazyRescale = 8.0f;  // rescale the accumulators only when the max grows by > 2^8
+// The value operand of token t is x_t = p_t sigma_t, p_t = 2^(s_t - R) with R the running
+// reference (log2 units), split into fp16 hi and lo parts.  R follows a bound of
+// log2(p_t sigma_t) instead of the score alone, so x stays inside fp16's range whatever the
+// value scales are: R moves (and the accumulators are rescaled) only when that bound exceeds
+// 2^kXMax, and then so that it becomes 2^kXAfter.  Between moves x < 2^15 (fp16 holds up to
+// 65504); right after one the tokens that dominate the sums have x near 2^kXAfter, where
+// both fp16 parts are normal numbers and the pair keeps ~22 bits.
+constexpr float kXMax = 15.0f;
+constexpr float kXAfter = 7.0f;
+typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
+
+// Biased exponent field e of the largest of a lane's eight fp16 value scales (two per word):
+// every one of them is below 2^(e - 14) (e = 0 for zero and subnormal scales).  Scales are
+// non-negative, so their bit patterns order like their values.
+__device__ __forceinline__ float scale_exponent_field(const uint32_t (&sgw)[4]) {
+  const ushort2_t a = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, sgw[0]), __builtin_bit_cast(ushort2_t, sgw[1]));
+  const ushort2_t b = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, sgw[2]), __builtin_bit_cast(ushort2_t, sgw[3]));
+  const ushort2_t c = __builtin_elementwise_max(a, b);
+  const uint32_t m = max(static_cast<uint32_t>(c.x), static_cast<uint32_t>(c.y));
+  return static_cast<float>((m >> 10) & 31u);
+}
 
 __device__ __forceinline__ float f16_value(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
@@ -898,13 +918,15 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, sc[tau][i]);
-    // The reference max only has to move when some score exceeds it by more than the
-    // lazy margin; the column-wide max (a cross-lane reduction) is needed only then.
-    if (__any(fresh || lmax > kLazyRescale)) {
+    // log2(p sigma) + 14 < lx for every token of the lane (uncounted tokens' scales are zero)
+    const float lx = lmax + scale_exponent_field(sgw);
+    // The reference only has to move when that bound exceeds 2^kXMax; the column-wide max
+    // (a cross-lane reduction) is needed only then.
+    if (__any(fresh || lx > kXMax + 14.0f)) {
       // every visit has a counted token, so the column max is finite
-      const float wmax = group_max(lmax);
-      const bool grow = fresh || wmax > kLazyRescale;
-      const float delta = grow ? wmax : 0.0f;
+      const float wmax = group_max(lx);
+      const bool grow = fresh || wmax > kXMax + 14.0f;
+      const float delta = grow ? wmax - (kXAfter + 14.0f) : 0.0f;
       // the first visit's accumulators are still zero (and -delta may overflow exp2)
       const float alf = fresh ? 0.0f : exp2_raw(-delta);
       if (grow) m_ref = (fresh ? 0.0f : m_ref) + delta;

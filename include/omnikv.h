@@ -111,6 +111,10 @@
  *   code = #{ j : v' >= fp32(sigma_fp16) * beta_j }, beta_j the fp32 midpoint of
  *   fp16 codebook levels l_j, l_{j+1}.
  *   Dequantized value: v_hat = U_m (sigma_fp16 * l[code]).
+ *   A token whose RMS exceeds fp16's largest finite value (65504) gets an infinite
+ *   scale; the decode's result over such a token is undefined.  Every finite scale,
+ *   subnormals included, is within the decode's range: it keeps each probability
+ *   times scale inside fp16's normal range for the tokens that dominate the sums.
  */
 #ifndef OMNIKV_H_
 #define OMNIKV_H_

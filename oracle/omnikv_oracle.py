@@ -432,16 +432,6 @@ def quantize_values(v: np.ndarray, tags: np.ndarray, U: np.ndarray, levels16: np
     return pack_windows(codes, "value", bits), sigma16.transpose(0, 2, 1).copy()
 
 
-def rotated_values_f64(v: np.ndarray, tags: np.ndarray, U: np.ndarray) -> np.ndarray:
-    """v' = U_m^T v in float64 (for distance-to-boundary diagnostics)."""
-    out = np.empty(v.shape, dtype=np.float64)
-    for m in range(U.shape[0]):
-        sel = tags == m
-        if sel.any():
-            out[sel] = np.asarray(v[sel], np.float64) @ np.asarray(U[m], np.float64)
-    return out
-
-
 # ----------------------------------------------------------------------------- dequantization
 def dequantize_keys(k_codes, k_min, k_scale, signs, bits: int, length: Optional[int] = None):
     """Original-space keys x_hat = R^{-1}(m + s * code), float64 [B][Hkv][T][d].

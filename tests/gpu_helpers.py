@@ -35,14 +35,28 @@ def bf16_tensor(x):
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).cuda()
 
 
-def make_context(cfg, key_bits=None, value_bits=None, seed=0, key_meta="fp16"):
+_CODEBOOKS = {}
+
+
+def oracle_codebook(bits):
+    """The oracle's own value codebook (fp16 bits), computed once per width.  Every parity
+    reference dequantizes with this table, never with the one the library builds."""
+    if bits not in _CODEBOOKS:
+        _CODEBOOKS[bits] = O.value_codebook_f16(bits)
+    return _CODEBOOKS[bits].copy()
+
+
+def make_context(cfg, key_bits=None, value_bits=None, seed=0, key_meta="fp16", modalities=3):
+    """A context with the configuration's seeded signs and rotations (the first `modalities`
+    of them) and the library's built-in codebook.  Returns (ctx, signs, U, levels) with
+    `levels` the oracle's codebook, which the references use."""
     d = cfg.head_dim
     signs = synth.rademacher_signs(d, seed)
-    U = synth.value_rotations(d, seed)
+    U = synth.value_rotations(d, seed, modalities)
     kb = cfg.key_bits if key_bits is None else key_bits
     vb = cfg.value_bits if value_bits is None else value_bits
     ctx = binding.Context(d, cfg.q_heads, cfg.kv_heads, kb, vb, signs, U, key_meta=key_meta)
-    return ctx, signs, U, ctx.value_codebook()
+    return ctx, signs, U, oracle_codebook(vb)
 
 
 def cache_to_device(cache):
@@ -58,3 +72,13 @@ def row_errors(got, ref):
     den = np.max(np.abs(ref), axis=-1)
     den = np.where(den > 0, den, 1.0)
     return np.max(np.abs(got - ref), axis=-1) / den
+
+
+def sampled_unit_rows(cfg, seed, units=3):
+    """(b, h) rows of every query head of a few sampled (sequence, KV head) units, always
+    including the first and the last unit.  The oracle's cost is per unit, so checking
+    all G heads of a unit costs little more than one."""
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0), (cfg.batch - 1, cfg.kv_heads - 1)}
+    picks |= {(int(rng.integers(cfg.batch)), int(rng.integers(cfg.kv_heads))) for _ in range(units)}
+    return sorted((b, kv * cfg.group + j) for b, kv in picks for j in range(cfg.group))

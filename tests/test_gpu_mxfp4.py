@@ -10,8 +10,8 @@ import pytest
 
 from oracle import omnikv_oracle as O
 from decode_attention_fwht_amd import synth
-from tests.gpu_helpers import (bf16_tensor, cache_to_device, from_dev, make_context, row_errors, say,
-                               to_dev)
+from tests.gpu_helpers import (bf16_tensor, cache_to_device, from_dev, make_context, row_errors,
+                               sampled_unit_rows, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -156,24 +156,35 @@ def test_mx_decode_record_sweep(cid, kbits, vbits):
     ctx.close()
 
 
-@pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (4, 2, 2), (4, 4, 4), (5, 2, 2)])
+def _drift_range_mx_cache(cfg, T, kbits, vbits, seed):
+    """Packed cache whose MXFP4 records encode (with the oracle's encoder) the key minima and
+    steps of the fp16-metadata tests' synthetic cache, i.e. the ranges a drifting N(0,1)-like
+    cache produces, so that unscaled queries give the same softmax sharpness as there."""
+    base = synth.random_packed_cache(cfg, seed, key_bits=kbits, value_bits=vbits, length=T)
+    m = O.f16_to_f32(base["k_min"])
+    s = O.f16_to_f32(base["k_scale"])
+    base["k_min"] = O.mx_pack_record(*O.mxfp4_encode(m))
+    base["k_scale"] = O.mx_pack_record(*O.mxfp4_encode(s))
+    return base
+
+
+@pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (4, 2, 2), (4, 4, 4), (5, 2, 2), (5, 4, 4)])
 def test_mx_decode_full_size_sampled(cid, kbits, vbits):
-    """The configurations' full sizes, in the launch the benchmark times: records drawn as
-    in the sweep, sampled rows against the oracle."""
+    """The configurations' full sizes, in the launch the benchmark times: records encoding the
+    drifting cache's key ranges, unscaled queries, every query head of sampled units against
+    the oracle."""
     import torch
     cfg = synth.CONFIGS[cid]
     T = cfg.context
     say(f"[mx-decode-sampled] cfg{cid} K{kbits}V{vbits} B={cfg.batch} T={T}")
     ctx, signs, U, lv = make_context(cfg, kbits, vbits, key_meta="mxfp4")
-    cache = _record_sweep_cache(cfg, T, kbits, vbits, 21)
+    cache = _drift_range_mx_cache(cfg, T, kbits, vbits, 21)
     lens = synth.seq_lens(cfg, ragged=True, seed=cid)
     lens[0] = T
-    q = synth.queries(cfg, 4) * np.float32(0.05)
+    q = synth.queries(cfg, 4)
     out = from_dev(ctx.decode(to_dev(q), to_dev(lens), T, cache_to_device(cache)))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(cid)
-    rows = sorted({(int(rng.integers(cfg.batch)), int(rng.integers(cfg.q_heads))) for _ in range(4)}
-                  | {(0, 0), (cfg.batch - 1, cfg.q_heads - 1)})
+    rows = sampled_unit_rows(cfg, cid)
     ref = O.decode_attention(q, lens, cache, signs, U, lv, rows=rows)
     bi, hi = [r[0] for r in rows], [r[1] for r in rows]
     err = row_errors(out[bi, hi], ref[bi, hi])

@@ -16,8 +16,8 @@ import pytest
 
 from oracle import omnikv_oracle as O
 from decode_attention_fwht_amd import synth
-from tests.gpu_helpers import (bf16_tensor, cache_to_device, from_dev, make_context, row_errors, say,
-                               to_dev)
+from tests.gpu_helpers import (bf16_tensor, cache_to_device, from_dev, make_context, row_errors,
+                               sampled_unit_rows, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -172,13 +172,13 @@ def test_quantize_keys_degenerate_windows(cid, kbits):
 
 
 # ----------------------------------------------------------------------------- codec at full size, sampled
-@pytest.mark.parametrize("cid", [3, 5])
-def test_quantize_parity_prefill_sampled(cid):
+@pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (5, 2, 2), (5, 4, 4)])
+def test_quantize_parity_prefill_sampled(cid, kbits, vbits):
     import torch
     cfg = synth.CONFIGS[cid]
     n = cfg.prefill
-    say(f"[codec-sampled] cfg{cid} prefill {n} tokens x batch {cfg.batch}")
-    ctx, signs, U, lv = make_context(cfg)
+    say(f"[codec-sampled] cfg{cid} K{kbits}V{vbits} prefill {n} tokens x batch {cfg.batch}")
+    ctx, signs, U, lv = make_context(cfg, kbits, vbits)
     tags, k, v = _inputs(cfg, n)
     cache = ctx.alloc_cache(cfg.batch, n)
     cache["modality"].copy_(to_dev(tags[:, :n]))
@@ -196,10 +196,10 @@ def test_quantize_parity_prefill_sampled(cid):
     picks += [(cfg.batch - 1, cfg.kv_heads - 1, n // 32 - 1), (0, 0, 0)]
     for b, h, w in picks:
         ks_ = slice(32 * w, 32 * w + 32)
-        kc, km, ksc = O.quantize_keys(k[b:b + 1, ks_, h:h + 1], signs, cfg.key_bits)
+        kc, km, ksc = O.quantize_keys(k[b:b + 1, ks_, h:h + 1], signs, kbits)
         assert np.array_equal(gk[b, h, w], kc[0, 0, 0]), (b, h, w)
         assert np.array_equal(gkm[b, h, w], km[0, 0, 0]) and np.array_equal(gks[b, h, w], ksc[0, 0, 0])
-        vc, vs = O.quantize_values(v[b:b + 1, ks_, h:h + 1], tags[b:b + 1, ks_], U, lv, cfg.value_bits)
+        vc, vs = O.quantize_values(v[b:b + 1, ks_, h:h + 1], tags[b:b + 1, ks_], U, lv, vbits)
         assert np.array_equal(gv[b, h, w], vc[0, 0, 0]), (b, h, w)
         assert np.array_equal(gvs[b, h, ks_], vs[0, 0])
     ctx.close()
@@ -317,7 +317,7 @@ def test_decode_graph_replay_matches_eager():
 
 
 # ----------------------------------------------------------------------------- decode at full size, sampled rows
-@pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (4, 2, 2), (5, 2, 2), (4, 4, 4)])
+@pytest.mark.parametrize("cid,kbits,vbits", [(3, 2, 2), (4, 2, 2), (5, 2, 2), (4, 4, 4), (5, 4, 4)])
 def test_decode_parity_full_size_sampled(cid, kbits, vbits):
     import torch
     cfg = synth.CONFIGS[cid]
@@ -330,9 +330,7 @@ def test_decode_parity_full_size_sampled(cid, kbits, vbits):
     q = synth.queries(cfg, 4)
     out = from_dev(ctx.decode(to_dev(q), to_dev(lens), T, cache_to_device(cache)))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(cid)
-    rows = sorted({(int(rng.integers(cfg.batch)), int(rng.integers(cfg.q_heads))) for _ in range(5)}
-                  | {(0, 0), (cfg.batch - 1, cfg.q_heads - 1)})
+    rows = sampled_unit_rows(cfg, cid)
     ref = O.decode_attention(q, lens, cache, signs, U, lv, rows=rows)
     bi = [r[0] for r in rows]
     hi = [r[1] for r in rows]
