@@ -285,8 +285,10 @@ omnikv_status omnikv_stream_append(const omnikv_ctx* ctx, const void* k_new, con
  * seq_lens[b] tokens, where token t attends with its packed key when t < kp and
  * with its ring key otherwise, and with its packed value when t < vp and its ring
  * value otherwise (ring tokens are not quantized; their values enter in the
- * original space).  The packed prefix [0, vp) runs through the split-KV pass;
- * the recent tokens [vp, n) are attended in the combine.  Arguments as for
+ * original space).  The packed prefix [0, vp) runs through the split-KV pass; the
+ * recent tokens [vp, n) are scored by one more workgroup per (sequence, KV head) of
+ * the same launch, and the second launch merges their partial with the splits'
+ * and adds their values after the inverse rotation.  Arguments as for
  * omnikv_decode_attention, plus the rings (ring_dtype F32 or BF16, ring_cap as
  * above, each sequence's recent tokens present in its ring); the workspace size
  * is the one omnikv_decode_workspace_size gives for (batch, max_len,

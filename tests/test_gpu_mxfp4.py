@@ -281,8 +281,8 @@ def test_mx_decode_split_invariance():
 
 
 def test_mx_decode_graph_replay_matches_eager():
-    """The MXFP4 decode step captured in a HIP graph gives the eager result bit for bit
-    on every replay, with eager work between replays."""
+    """The MXFP4 two-launch decode step captured in a HIP graph gives the eager result bit
+    for bit on every replay, with eager work between replays."""
     import torch
     cfg = synth.CONFIGS[2]
     T = 4096
@@ -296,7 +296,8 @@ def test_mx_decode_graph_replay_matches_eager():
             for _ in range(2)]
     eager = []
     for i in range(2):
-        ctx.decode(q, lens, T, caches[i], out=outs[i], workspace=ws)
+        ctx.decode_partial(q, lens, T, caches[i], ws)
+        ctx.decode_combine(lens, cfg.batch, T, ws, outs[i])
         eager.append(outs[i].clone())
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()

@@ -281,8 +281,9 @@ def test_decode_split_invariance():
 
 
 def test_decode_graph_replay_matches_eager():
-    """The decode step captured in a HIP graph (as the benchmark times it) gives the
-    eager result bit for bit on every replay, with eager work between replays."""
+    """The two-launch decode step (omnikv_decode_partial + omnikv_decode_combine) captured in
+    a HIP graph gives the eager result bit for bit on every replay, with eager work between
+    replays."""
     import torch
     cfg = synth.CONFIGS[2]
     T = 4096
@@ -295,7 +296,8 @@ def test_decode_graph_replay_matches_eager():
             for _ in range(2)]
     eager = []
     for i in range(2):
-        ctx.decode(q, lens, T, caches[i], out=outs[i], workspace=ws)
+        ctx.decode_partial(q, lens, T, caches[i], ws)
+        ctx.decode_combine(lens, cfg.batch, T, ws, outs[i])
         eager.append(outs[i].clone())
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -338,4 +340,66 @@ def test_decode_parity_full_size_sampled(cid, kbits, vbits):
     say(f"    rows {rows} max row error {err.max():.3e}")
     assert err.max() <= TOL
     assert np.all(np.isfinite(out))
+    ctx.close()
+
+
+# ----------------------------------------------------------------------------- the whole step
+def test_decode_workspace_reused_across_plans():
+    """One workspace, NaN-patterned on entry, serves decode steps of different batch sizes,
+    lengths and split counts: every result equals the one computed on a fresh workspace, bit
+    for bit (no state is carried from one call to the next)."""
+    import torch
+    cfg = synth.CONFIGS[2]
+    T = 10240
+    say("[workspace-reuse] cfg2")
+    ctx, signs, U, lv = make_context(cfg)
+    big = synth.Config(**{**cfg.__dict__, "batch": 4})
+    cache = cache_to_device(synth.random_packed_cache(big, 13, length=T))
+    q = to_dev(synth.queries(big, 13))
+    need = max(ctx.workspace_size(B, n, s) for B in (1, 4) for n in (T, 2048) for s in (0, 7, 200))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for B, n, s in ((4, T, 0), (1, 2048, 7), (4, 2048, 200), (1, T, 0), (4, T, 3)):
+            sub = {k: (v[:B] if k != "t_cap" else v) for k, v in cache.items()}
+            lens = to_dev(np.array([n - 3 * b for b in range(B)], np.int32))
+            got = ctx.decode(q[:B].contiguous(), lens, n, sub, workspace=ws, num_splits=s)
+            ref = ctx.decode(q[:B].contiguous(), lens, n, sub, num_splits=s)
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref), (rep, B, n, s)
+    ctx.close()
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """omnikv_decode_attention captured in a HIP graph gives the eager result bit for bit on
+    every replay, with eager work on the same workspace between replays."""
+    import torch
+    cfg = synth.CONFIGS[3]
+    T = 4096
+    one = synth.Config(**{**cfg.__dict__, "context": T})
+    say("[step-graph-replay] cfg3")
+    ctx, signs, U, lv = make_context(cfg)
+    caches = [cache_to_device(synth.random_packed_cache(one, 30 + i, length=T)) for i in range(2)]
+    q = to_dev(synth.queries(cfg, 5))
+    lens = to_dev(np.full(cfg.batch, T - 9, np.int32))
+    ws = torch.empty(ctx.workspace_size(cfg.batch, T), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((cfg.batch, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+            for _ in range(2)]
+    eager = []
+    for i in range(2):
+        ctx.decode(q, lens, T, caches[i], out=outs[i], workspace=ws)
+        eager.append(outs[i].clone())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(2):
+            ctx.decode(q, lens, T, caches[i], out=outs[i], workspace=ws)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+        ctx.decode(q, lens, T, caches[(rep + 1) % 2], workspace=ws)
+        torch.cuda.synchronize()
     ctx.close()
