@@ -25,7 +25,7 @@ EXPORTED = (
     "omnikv_quantize_values", "omnikv_decode_workspace_size", "omnikv_decode_attention",
     "omnikv_decode_partial", "omnikv_decode_combine", "omnikv_stream_packed_lengths", "omnikv_stream_append",
     "omnikv_decode_attention_streaming", "omnikv_calibrate_value_rotation", "omnikv_key_meta_bytes",
-    "omnikv_last_error",
+    "omnikv_decode_attention_noalloc", "omnikv_last_error",
 )
 
 
@@ -80,6 +80,8 @@ def load() -> ctypes.CDLL:
                                           ctypes.c_float, i32, vp, sz, vp, vp]
     L.omnikv_decode_partial.argtypes = [vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, i64,
                                         ctypes.c_float, i32, vp, sz, vp]
+    L.omnikv_decode_attention_noalloc.argtypes = [vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, i64,
+                                                  ctypes.c_float, i32, vp, vp]
     L.omnikv_decode_combine.argtypes = [vp, vp, i32, i64, i32, vp, sz, vp, vp]
     L.omnikv_stream_packed_lengths.argtypes = [i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.omnikv_stream_append.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i32, vp, vp, i32,
@@ -215,6 +217,16 @@ class Context:
             _ptr(cache["k_scale"]), _ptr(cache["v_codes"]), _ptr(cache["v_scale"]), _ptr(cache["modality"]),
             cache["t_cap"], softmax_scale, num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
             _stream(stream)))
+        return out
+
+    def decode_noalloc(self, q, seq_lens, max_len: int, cache: dict, out, softmax_scale: float = 0.0,
+                       num_splits: int = 0, stream=None):
+        """omnikv_decode_attention_noalloc: the library's static scratch as the workspace; the
+        caller passes the output."""
+        _check(load().omnikv_decode_attention_noalloc(
+            self._h, _ptr(q), _ptr(seq_lens), int(q.shape[0]), max_len, _ptr(cache["k_codes"]),
+            _ptr(cache["k_min"]), _ptr(cache["k_scale"]), _ptr(cache["v_codes"]), _ptr(cache["v_scale"]),
+            _ptr(cache["modality"]), cache["t_cap"], softmax_scale, num_splits, _ptr(out), _stream(stream)))
         return out
 
     def decode_partial(self, q, seq_lens, max_len: int, cache: dict, workspace, softmax_scale: float = 0.0,

@@ -11,14 +11,23 @@
 #include <vector>
 
 #include <climits>
+#include <mutex>
 
 #include "omnikv_internal.h"
+
+// Decode workspace of omnikv_decode_attention_noalloc, for callers that cannot allocate:
+// one array per GPU, held until the process ends.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress (per device, kept in
+// g_scratch_ptr) and is the only form ever passed to a kernel or runtime call.
+constexpr size_t kScratchBytes = size_t{12} << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 struct omnikv_ctx {
   omnikv::Shape sh{};
   omnikv::DeviceTables tb{};
   std::vector<uint16_t> levels;  // fp16 value codebook
   int device = 0;
+  void* scratch = nullptr;       // device address of `scratch` on `device`
 };
 
 namespace {
@@ -40,6 +49,24 @@ omnikv_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device address of `scratch` on `device` (the current device), looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 // Lloyd-Max quantizer of a unit Gaussian with n levels: alternate the midpoint
 // condition for the thresholds and the centroid condition for the levels, the
@@ -169,6 +196,10 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
                           cfg->key_meta == OMNIKV_META_MXFP4 ? 1 : 0};
   ctx->levels = levels;
   (void)hipGetDevice(&ctx->device);
+  if (const hipError_t e = scratch_address(ctx->device, &ctx->scratch); e != hipSuccess) {
+    delete ctx;
+    return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  }
 
   std::vector<float> sg(d);
   for (int i = 0; i < d; ++i) sg[i] = static_cast<float>(key_signs[i]);
@@ -481,6 +512,27 @@ omnikv_status omnikv_stream_append(const omnikv_ctx* ctx, const void* k_new, con
     }
   }
   return OMNIKV_OK;
+}
+
+omnikv_status omnikv_decode_attention_noalloc(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens,
+                                              int32_t batch, int64_t max_len, const uint32_t* k_codes,
+                                              const uint16_t* k_min, const uint16_t* k_scale, const uint32_t* v_codes,
+                                              const uint16_t* v_scale, const uint8_t* modality, int64_t t_cap,
+                                              float softmax_scale, int32_t num_splits, float* out, hipStream_t stream) {
+  omnikv_status st;
+  if ((st = check_ctx(ctx)) != OMNIKV_OK) return st;
+  if (!ctx->scratch) return fail(OMNIKV_EHIP, "decode_attention_noalloc: no scratch address for device %d", ctx->device);
+  if (batch <= 0) return fail(OMNIKV_EINVAL, "batch must be positive (got %d)", batch);
+  if (max_len < 0) return fail(OMNIKV_EINVAL, "max_len must be >= 0 (got %lld)", (long long)max_len);
+  if (num_splits < 0) return fail(OMNIKV_EINVAL, "num_splits must be >= 0");
+  const size_t need = omnikv::plan_decode(ctx->sh, batch, max_len, num_splits).workspace_bytes;
+  if (need > kScratchBytes)
+    return fail(OMNIKV_EINVAL,
+                "decode_attention_noalloc: this step needs %zu bytes of workspace, the static scratch holds %zu; "
+                "use omnikv_decode_attention with a caller workspace (or fewer splits)",
+                need, kScratchBytes);
+  return omnikv_decode_attention(ctx, q, seq_lens, batch, max_len, k_codes, k_min, k_scale, v_codes, v_scale, modality,
+                                 t_cap, softmax_scale, num_splits, ctx->scratch, kScratchBytes, out, stream);
 }
 
 omnikv_status omnikv_decode_attention_streaming(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens,

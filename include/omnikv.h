@@ -247,6 +247,24 @@ omnikv_status omnikv_decode_combine(const omnikv_ctx* ctx, const int32_t* seq_le
                                     int64_t max_len, int32_t num_splits, const void* workspace,
                                     size_t workspace_bytes, float* out, hipStream_t stream);
 
+/* omnikv_decode_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, which is a static array of the library instead,
+ * 12 MiB per GPU, held from the first omnikv_create on that GPU until the process ends.
+ * The call allocates nothing.  Steps whose plan needs more workspace than that
+ * (omnikv_decode_workspace_size(..) > 12 MiB) return OMNIKV_EINVAL and launch nothing;
+ * with the library's default split count (num_splits = 0) every step of at most 512
+ * (sequence, KV head) units fits (at most 512 partials of 12 KiB, d = 128).  All calls
+ * on one GPU share the array: calls that overlap in time on one GPU
+ * (different streams, or different contexts) race and must be ordered by the caller.
+ * The array's contents between calls are scratch (nothing is carried over). */
+omnikv_status omnikv_decode_attention_noalloc(const omnikv_ctx* ctx, const float* q, const int32_t* seq_lens,
+                                              int32_t batch, int64_t max_len, const uint32_t* k_codes,
+                                              const uint16_t* k_min, const uint16_t* k_scale,
+                                              const uint32_t* v_codes, const uint16_t* v_scale,
+                                              const uint8_t* modality, int64_t t_cap, float softmax_scale,
+                                              int32_t num_splits, float* out, hipStream_t stream);
+
 /* ---- Streaming generation ([paper] §3.1 Implementation details, captioning:
  * keys are quantized every 128 tokens in groups of 32; values keep a 128-token
  * sliding FP16 window before quantization).
