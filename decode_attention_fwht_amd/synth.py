@@ -114,7 +114,7 @@ def to_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def drifting_tensor(cfg: Config, tags: np.ndarray, seed: int, stream: int,
-                         t0: int = 0, n: Optional[int] = None) -> np.ndarray:
+                         t0: int = 0, n: Optional[int] = None, modality_offset: float = 0.0) -> np.ndarray:
     """fp32 [batch][n][kv_heads][head_dim] keys or values with window drift.
 
     Per (sequence, KV head): z ~ N(0,1); for every 32-token window w a shift
@@ -123,6 +123,9 @@ def drifting_tensor(cfg: Config, tags: np.ndarray, seed: int, stream: int,
     x = lambda_w * (z + mu_w); a seeded set of outlier channels is multiplied
     by outlier_gain; bf16 configs round to bf16.  `stream` separates keys (0)
     from values (1); tokens [t0, t0+n) of the sequence are drawn.
+    modality_offset > 0 adds a per-(KV head, modality) channel offset
+    modality_offset * N(0, 1) to every token of that modality (keys that cluster by
+    modality); 0 (the default) draws exactly as without it.
     """
     T = tags.shape[1]
     n = T - t0 if n is None else int(n)
@@ -141,7 +144,12 @@ def drifting_tensor(cfg: Config, tags: np.ndarray, seed: int, stream: int,
             lam = np.exp(s * r.standard_normal(nw, dtype=np.float32))[:, None, None]
             x = lam * (z + mu)
             x[:, :, outl] *= np.float32(cfg.outlier_gain)
-            out[b, :, h, :] = x.reshape(n, d)
+            x = x.reshape(n, d)
+            if modality_offset > 0:
+                ro = rng_for(cfg.cid, seed, (stream * 7919 + b) * 131 + h + 100003)
+                off = np.float32(modality_offset) * ro.standard_normal((3, d), dtype=np.float32)
+                x = x + off[tags[b, t0:t0 + n].astype(np.int64)]
+            out[b, :, h, :] = x
     if not cfg.fp32_inputs:
         out = to_bf16(out)
     return out

@@ -29,6 +29,9 @@ Source pages (cited by title and section):
   eigendecomposed).  Reading: the weighted second moment, its eigenvectors in
   descending order composed with the normalized Hadamard ("modality-aware
   correction of the Hadamard rotation", [paper] §2.3).
+* Error metrics ([paper] §3.3 Error comparison, Table 3): key reconstruction MSE,
+  KL divergence of the attention distributions, attention-output MSE, each by its
+  plain definition.
 * Streaming generation ([paper] §3.1 Implementation details, captioning):
   keys are quantized every 128 tokens in groups of 32; values stay in a
   128-token sliding FP16 window before quantization.  Recent tokens enter the
@@ -565,6 +568,41 @@ def decode_attention_streaming(q, seq_lens, cache: dict, k_recent, v_recent, sig
         for h in heads:
             out[b, h] = attention_f64(q[b, h], keys, vals, scale)
     return out
+
+
+# ----------------------------------------------------------------------------- error metrics
+# [paper] §3.3 "Error comparison" (Table 3 caption) compares the codecs by the key
+# reconstruction MSE, the KL divergence between the attention distributions computed
+# with original and with quantized keys, and the MSE of the attention output; the
+# digest's key-results list gives the Table 3 values ([digest] 关键结果与论文证据).
+# The pages print no formulas: the readings below are the plain definitions.
+def key_reconstruction_mse(keys, keys_hat) -> float:
+    """Mean over every element of (k_hat - k)^2 (float64)."""
+    k = np.asarray(keys, np.float64)
+    return float(np.mean((np.asarray(keys_hat, np.float64) - k) ** 2))
+
+
+def _log_softmax(s):
+    s = s - s.max(axis=-1, keepdims=True)
+    return s - np.log(np.exp(s).sum(axis=-1, keepdims=True))
+
+
+def attention_kl(q, keys, keys_hat, scale: float) -> float:
+    """Mean over query rows of KL(p || p_hat), p = softmax(scale q . k_t) over the tokens t with
+    the original keys and p_hat with the quantized keys.  q: [H][d]; keys: [T][d] (float64)."""
+    q = np.asarray(q, np.float64)
+    lp = _log_softmax(scale * (q @ np.asarray(keys, np.float64).T))
+    lph = _log_softmax(scale * (q @ np.asarray(keys_hat, np.float64).T))
+    return float(np.mean(np.sum(np.exp(lp) * (lp - lph), axis=-1)))
+
+
+def attention_output_mse(q, keys, values, keys_hat, values_hat, scale: float) -> float:
+    """Mean over every element of (o_hat - o)^2, o = softmax(scale q . k) v with the original
+    keys and values, o_hat with the quantized ones.  q: [H][d]; keys, values: [T][d]."""
+    q = np.asarray(q, np.float64)
+    o = np.exp(_log_softmax(scale * (q @ np.asarray(keys, np.float64).T))) @ np.asarray(values, np.float64)
+    oh = np.exp(_log_softmax(scale * (q @ np.asarray(keys_hat, np.float64).T))) @ np.asarray(values_hat, np.float64)
+    return float(np.mean((oh - o) ** 2))
 
 
 # ----------------------------------------------------------------------------- calibration

@@ -175,3 +175,51 @@ def test_value_scale_range_sampled_scales():
     say(f"    max row error {err.max():.3e}")
     assert np.all(np.isfinite(out)) and err.max() <= TOL
     ctx.close()
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_error_metrics_of_the_gpu_codec(bits):
+    """The pages' three error metrics ([paper] §3.3 Error comparison: key reconstruction MSE,
+    attention KL, attention-output MSE) on the GPU write path's output for drift data: equal to
+    those of the oracle's own quantization (the codes are the same), and the values are
+    reported.  Both KV heads of a config-2 sequence, 4096 tokens, all 8 query heads each."""
+    import math
+    import torch
+    cfg = synth.CONFIGS[2]
+    n = 4096
+    say(f"[metrics] cfg2 K{bits}V{bits} n={n}")
+    ctx, signs, U, lv = make_context(cfg, bits, bits)
+    tags = synth.modality_layout(cfg, 3, n)
+    k = synth.drifting_tensor(cfg, tags, 3, 0, 0, n)
+    v = synth.drifting_tensor(cfg, tags, 3, 1, 0, n)
+    cache = ctx.alloc_cache(cfg.batch, n)
+    cache["modality"].copy_(to_dev(tags))
+    ctx.quantize_keys(bf16_tensor(k), 0, cache)
+    ctx.quantize_values(bf16_tensor(v), 0, cache)
+    torch.cuda.synchronize()
+    g = {key: from_dev(cache[key], dt) for key, dt in (("k_codes", np.uint32), ("k_min", np.uint16),
+                                                      ("k_scale", np.uint16), ("v_codes", np.uint32),
+                                                      ("v_scale", np.uint16))}
+    kc, km, ks = O.quantize_keys(k, signs, bits)
+    vc, vs = O.quantize_values(v, tags, U, lv, bits)
+    q = synth.queries(cfg, 3)[0]
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+
+    def metrics(kc_, km_, ks_, vc_, vs_):
+        kh = O.dequantize_keys(kc_, km_, ks_, signs, bits)[0]
+        vh = O.dequantize_values(vc_, vs_, tags, U, lv, bits)[0]
+        out = []
+        for h in range(cfg.kv_heads):
+            kk, vv = k[0, :, h].astype(np.float64), v[0, :, h].astype(np.float64)
+            qq = q[h * cfg.group:(h + 1) * cfg.group]
+            out.append((O.key_reconstruction_mse(kk, kh[h]), O.attention_kl(qq, kk, kh[h], scale),
+                        O.attention_output_mse(qq, kk, vv, kh[h], vh[h], scale)))
+        return np.array(out)
+
+    got = metrics(g["k_codes"], g["k_min"], g["k_scale"], g["v_codes"], g["v_scale"])
+    ref = metrics(kc, km, ks, vc, vs)
+    for h in range(cfg.kv_heads):
+        say(f"    KV head {h}: key MSE {got[h, 0]:.4f}  attention KL {got[h, 1]:.4f}  output MSE {got[h, 2]:.5f}")
+    assert np.array_equal(got, ref)
+    assert np.all(np.isfinite(got)) and np.all(got > 0)
+    ctx.close()
