@@ -311,9 +311,8 @@ __device__ __forceinline__ void wait_groups(int ahead) {
 // Ring depth: the deepest of 4, 3, 2 slots per wave that keeps kBlocksPerCU workgroups per
 // CU within the 160 KB of LDS (ring + rotated queries + small tables); deeper rings
 // measured slower.  Two workgroups per CU (two waves per SIMD) measured as fast as three
-// and leave each wave registers for the k_min operand.
+// and leave each wave registers for its operand constants.
 constexpr int kBlocksPerCU = 2;
-constexpr bool kBqaInRegs = kBlocksPerCU <= 2;
 // Dynamic LDS: the ring, filled by the asynchronous copies.  Before the visits a wave's
 // last ring slot (not filled before the first visit) stages its two query heads, the
 // signs of D, the sequence's length and (wave 0) the level-pair table; after them the
@@ -626,9 +625,15 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       mstride = 32;
     }
   }
-  auto issue = [&](int w, int slot) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_slot(wave, slot))));
+  // Ring slots as byte offsets from this wave's first slot; the slot to fill next and the
+  // metadata copy's per-lane source advance by one slot and one window at each issue.
+  constexpr uint32_t RING_SPAN = RING * SG::BYTES;
+  const uint32_t ring_lds = lds_addr(wave * RING * SG::BYTES);
+  uint32_t fill = 0;
+  auto next_slot = [](uint32_t off) { return off + SG::BYTES == RING_SPAN ? 0u : off + SG::BYTES; };
+  const uint8_t* mptr = mbase + static_cast<size_t>(wbeg) * mstride;
+  auto issue = [&](int w) {
+    const uint32_t dst = ring_lds + fill;
 #pragma unroll
     for (int x = 0; x < SG::NK; ++x)
       if (1024 * x + 16 * lane < SG::KBYTES)
@@ -637,7 +642,9 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     for (int x = 0; x < SG::NV; ++x)
       if (1024 * x + 16 * lane < SG::VBYTES)
         copy16_to_lds_sbase(vbase, static_cast<uint32_t>(w * SG::VBYTES + 1024 * x + 16 * lane), dst + SG::OFF_V + 1024 * x);
-    if (lane < SG::MISC_LANES) copy16_to_lds(mbase + static_cast<size_t>(w) * mstride, dst + SG::OFF_COPY);
+    if (lane < SG::MISC_LANES) copy16_to_lds(mptr, dst + SG::OFF_COPY);
+    mptr += mstride;
+    fill = next_slot(fill);
   };
 
   // ---- visit order: the wave's windows in order, each visited once whatever modalities
@@ -646,7 +653,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   // latency.
   int issued = 0;
   auto issue_upto = [&](int lim) {
-    for (; issued < lim; ++issued) issue(wbeg + issued, issued % RING);
+    for (; issued < lim; ++issued) issue(wbeg + issued);
   };
   {
     const int64_t bound = a.stream ? stream_value_packed(a.max_len) : a.max_len;
@@ -712,61 +719,9 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   }
   __syncthreads();
 
-  // Z_h: power of two with |q'/Z_h| <= 1
-  int zexp = 0;
-  {
-    const float zm = zmax_lds[h];
-    if (zm > 0.0f) (void)frexpf(zm, &zexp);
-  }
-  const float zinv = ldexpf(1.0f, -zexp);
-  const float zh = ldexpf(1.0f, zexp);
-  const float zfac = ldexpf(1.0f, zexp + 24);
-
-  // ---- operand constants.  Lane (n, g) feeds column n: head h, part hi (0) or lo (1);
-  // K-step s, dword i hold channels c0, c0 + 1 with c0 = g*D/4 + 8 s + 2 i.
-  //   alpha/beta/gamma: score operand  fp16 split of (q^ s) scaled by 2^-(KB*peff(s))
-  //   bqa:              k_min operand  q^ hi (part 0) or lo (part 1); the same in every wave
-  //                     of the block: kept in registers when they allow, else in LDS (over
-  //                     q_lds)
-  half2_t alpha[NS][4], beta[NS][4], gamma[NS][4];
-  uint4_t bqa[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    uint32_t bw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      half2_t al, be, ga, qa;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float qh = q_lds[h][g * (D / 4) + 8 * s + 2 * i + e] * zinv;   // |qh| <= 1
-        const float qt = qh * ldexpf(1.0f, -KB * KO::peff(s));               // exact scaling
-        const _Float16 th = static_cast<_Float16>(qt);
-        const _Float16 tl = static_cast<_Float16>(qt - static_cast<float>(th));
-        al[e] = th;
-        be[e] = part ? th : static_cast<_Float16>(0.0f);
-        ga[e] = part ? tl : static_cast<_Float16>(0.0f);
-        const _Float16 hh = static_cast<_Float16>(qh);
-        qa[e] = part ? static_cast<_Float16>(qh - static_cast<float>(hh)) : hh;
-      }
-      alpha[s][i] = al;
-      beta[s][i] = be;
-      gamma[s][i] = ga;
-      bw[i] = __builtin_bit_cast(uint32_t, qa);
-    }
-    bqa[s] = uint4_t{bw[0], bw[1], bw[2], bw[3]};
-  }
-  static_assert(NS * 64 * 16 <= kMaxGroup * D * 4, "k_min operand table must fit over q_lds");
-  uint4_t* const bqa_lds = reinterpret_cast<uint4_t*>(&q_lds[0][0]);  // [NS][64 lanes]
-  __syncthreads();  // every wave has read q_lds
-  if (!kBqaInRegs && wave == 0) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) bqa_lds[s * 64 + lane] = bqa[s];
-  }
-  __syncthreads();
-
-  // ---- streamed sequences: the extra workgroup of the unit takes the recent tokens
+  // ---- streamed sequences: the extra workgroup of the unit takes the recent tokens (it
+  // reads the rotated queries from q_lds, before the operand tables below replace them)
   if (a.stream && split == a.splits) {
-    static_assert(kBqaInRegs, "the recent tokens read the rotated queries from q_lds");
     // the split workgroups sharing this CU raise their priority while they start: this short
     // one takes the highest too, or it would only get their leftover issue slots
     __builtin_amdgcn_s_setprio(3);
@@ -774,6 +729,75 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     return;
   }
 
+  // Z_h: power of two with |q'/Z_h| <= 1
+  int zexp = 0;
+  {
+    const float zm = zmax_lds[h];
+    if (zm > 0.0f) (void)frexpf(zm, &zexp);
+  }
+  const float zh = ldexpf(1.0f, zexp);
+  const float zfac = ldexpf(1.0f, zexp + 24);
+
+  // ---- operand constants.  Lane (n, g) feeds column n: head h, part hi (0) or lo (1);
+  // K-step s, dword i hold channels c0, c0 + 1 with c0 = g*D/4 + 8 s + 2 i.
+  //   alpha/beta/gamma: score operand  fp16 split (th, tl) of (q^ s) scaled by 2^-(KB*peff(s)):
+  //                     alpha = th, beta = th (part 1) or 0, gamma = tl (part 1) or 0
+  //   bqa:              k_min operand  fp16 split (qh, ql) of q^: qh (part 0) or ql (part 1)
+  // with q^ = q'/Z_h.  They depend on (head, channel) only, so the block builds four
+  // [head][D] fp16 tables once (a few elements per thread) and every lane loads its rows:
+  // th and tl over q_lds, qh and ql in the staging slots of waves 0 and 1 (free until the
+  // visits begin).
+  constexpr int PER_T = kMaxGroup * D / (kWaves * 64);
+  static_assert(PER_T * kWaves * 64 == kMaxGroup * D, "table elements per thread");
+  static_assert(2 * kMaxGroup * D * 2 <= kMaxGroup * D * 4, "th and tl tables fit over q_lds");
+  static_assert(kMaxGroup * D * 2 <= SG::BYTES, "a qh or ql table fits in a staging slot");
+  _Float16 tv[4][PER_T];
+#pragma unroll
+  for (int x = 0; x < PER_T; ++x) {
+    const int idx = tid + x * kWaves * 64, hh = idx / D, c = idx % D;
+    const int s = (c % (D / 4)) / 8;
+    int ze = 0;
+    const float zm = zmax_lds[hh];
+    if (zm > 0.0f) (void)frexpf(zm, &ze);
+    const float qh = q_lds[hh][c] * ldexpf(1.0f, -ze);                  // |qh| <= 1
+    const float qt = qh * ldexpf(1.0f, -KB * KO::peff(s));               // exact scaling
+    const _Float16 th = static_cast<_Float16>(qt);
+    const _Float16 hq = static_cast<_Float16>(qh);
+    tv[0][x] = th;
+    tv[1][x] = static_cast<_Float16>(qt - static_cast<float>(th));
+    tv[2][x] = hq;
+    tv[3][x] = static_cast<_Float16>(qh - static_cast<float>(hq));
+  }
+  __syncthreads();  // q_lds and every staging slot have been read
+  _Float16* const tab_t = reinterpret_cast<_Float16*>(&q_lds[0][0]);  // [th | tl][head][D]
+  _Float16* const tab_qh = reinterpret_cast<_Float16*>(ring_mem + (0 * RING + RING - 1) * SG::BYTES);
+  _Float16* const tab_ql = reinterpret_cast<_Float16*>(ring_mem + (1 * RING + RING - 1) * SG::BYTES);
+#pragma unroll
+  for (int x = 0; x < PER_T; ++x) {
+    const int idx = tid + x * kWaves * 64;
+    tab_t[idx] = tv[0][x];
+    tab_t[kMaxGroup * D + idx] = tv[1][x];
+    tab_qh[idx] = tv[2][x];
+    tab_ql[idx] = tv[3][x];
+  }
+  __syncthreads();
+  half2_t alpha[NS][4], beta[NS][4], gamma[NS][4];
+  uint4_t bqa[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int c0 = h * D + g * (D / 4) + 8 * s;
+    const uint4_t th4 = *reinterpret_cast<const uint4_t*>(tab_t + c0);
+    const uint4_t tl4 = *reinterpret_cast<const uint4_t*>(tab_t + kMaxGroup * D + c0);
+    bqa[s] = *reinterpret_cast<const uint4_t*>((part ? tab_ql : tab_qh) + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t thw = th4[i], tlw = tl4[i];
+      alpha[s][i] = __builtin_bit_cast(half2_t, thw);
+      beta[s][i] = __builtin_bit_cast(half2_t, part ? thw : 0u);
+      gamma[s][i] = __builtin_bit_cast(half2_t, part ? tlw : 0u);
+    }
+  }
+  __syncthreads();  // every lane has its rows before the visits reuse the staging slots
   // ---- running state.  Scores, l_part and the accumulators are relative to m_ref (per
   // column, log2 units).  The value contraction's 16 columns are the 8 heads of two
   // modalities: accumulator A holds audio (columns 0-7) and video (8-15), accumulator B
@@ -810,10 +834,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     for (int s = 0; s < NS; ++s) {
       const uint4_t sv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_S + g * (D / 2) + 16 * s);
       const uint4_t mv4 = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_M + g * (D / 2) + 16 * s);
-      if constexpr (kBqaInRegs)
-        cm = mfma16(mv4, bqa[s], cm);
-      else
-        cm = mfma16(mv4, bqa_lds[s * 64 + lane], cm);
+      cm = mfma16(mv4, bqa[s], cm);
       // three passes over the four dwords (independent neighbours between dependent steps)
       half2_t sv[4], t[4];
       uint32_t bq[4];
@@ -1054,15 +1075,24 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   // quarter of visits .. 0 for its last), so a wave that falls behind a quarter gets the
   // issue slots until it catches up.
   const int q1 = nw / 4, q2 = nw / 2, q3 = (3 * nw) / 4;
+  int stage = 0, next_change = q1;
+  uint32_t cur = 0;  // ring offset of visit i's slot
   __builtin_amdgcn_s_setprio(3);
   for (int i = 0; i < nw; ++i) {
-    if (i == q1) __builtin_amdgcn_s_setprio(2);
-    if (i == q2) __builtin_amdgcn_s_setprio(1);
-    if (i == q3) __builtin_amdgcn_s_setprio(0);
+    if (i == next_change) {
+      do {
+        ++stage;
+        next_change = stage == 1 ? q2 : (stage == 2 ? q3 : nw);
+      } while (next_change == i);
+      if (stage == 1) __builtin_amdgcn_s_setprio(2);
+      else if (stage == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     issue_upto(min(nw, i + RING));
     // wait for this visit's copies: later visits' copies may stay in flight
     wait_groups<L, RING - 1>(issued - (i + 1));
-    uint8_t* slot = ring_slot(wave, i % RING);
+    uint8_t* slot = ring_mem + wave * RING * SG::BYTES + cur;
+    cur = next_slot(cur);
     if constexpr (MX) mx_expand(slot);
     float4_t cs[2], cm;
     score_mma(slot, cs, cm);
