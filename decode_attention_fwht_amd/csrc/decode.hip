@@ -885,9 +885,52 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     }
   };
 
+  // ---- the value contraction's A operands of the window in `slot` (fp16 levels, channel
+  // tile u: row = channel, the lane's 8 tokens), built from the value block and the
+  // level-pair table; the same for every accumulator.  Built right after the score
+  // contractions are issued, their table reads overlap those contractions.
+  auto value_operands = [&](const uint8_t* slot, uint4_t (&av)[NU]) {
+    // Byte offsets of the pair-table entries: 2-bit values take four offsets per dword at
+    // once (low nibbles of the bytes, then high nibbles).
+    uint32_t vw[VW];
+#pragma unroll
+    for (int x = 0; x < VW / 4; ++x) {
+      const uint4_t t = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_V + 16 * (VW / 4) * lane + 16 * x);
+      vw[4 * x] = t[0]; vw[4 * x + 1] = t[1]; vw[4 * x + 2] = t[2]; vw[4 * x + 3] = t[3];
+    }
+    if constexpr (VW == 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_V + 8 * lane);
+      vw[0] = t.x; vw[1] = t.y;
+    }
+    uint32_t vx[VW], vy[VW];
+    if constexpr (VB == 2) {
+#pragma unroll
+      for (int x = 0; x < VW; ++x) {
+        vx[x] = (vw[x] << 2) & 0x3C3C3C3Cu;
+        vy[x] = (vw[x] >> 2) & 0x3C3C3C3Cu;
+      }
+    }
+    auto entry = [&](int pp) -> uint32_t {
+      if constexpr (VB == 2) {
+        const uint32_t src = (pp & 1) ? vy[pp / 8] : vx[pp / 8];
+        const int byte = (pp % 8) / 2;
+        // one byte-select per offset (v_perm_b32: byte `byte` of src, upper bytes zero)
+        const uint32_t off = __builtin_amdgcn_perm(0u, src, 0x0C0C0C00u | static_cast<uint32_t>(byte));
+        return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(vtab) + off);
+      } else {
+        return vtab[(vw[pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[u][i] = entry(4 * u + i);
+  };
+
   // ---- the rest of one visit of a window, given its score contractions.  Tokens count
   // when they lie inside the sequence and carry a modality tag below 3.
-  auto visit = [&](const uint8_t* slot, int tokb, const float4_t (&cs)[2], const float4_t& cm) {
+  auto visit = [&](const uint8_t* slot, int tokb, const float4_t (&cs)[2], const float4_t& cm,
+                   const uint4_t (&av)[NU]) {
     const uint32_t tg0 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 4 * g);
     const uint32_t tg1 = *reinterpret_cast<const uint32_t*>(slot + SG::OFF_TAG + 16 + 4 * g);
     // value scales of this lane's tokens, fp16 pairs (tokens 4g.., then 16 + 4g..)
@@ -974,38 +1017,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       bhi[qd] = mix_pair(p0, p1, sgw[qd], 0u);
       blo[qd] = mix_pair(p0, p1, sgw[qd], bhi[qd]);
     }
-    // ---- value contractions, one channel tile at a time.
-    // Byte offsets of the pair-table entries: 2-bit values take four offsets per dword at
-    // once (low nibbles of the bytes, then high nibbles).
-    uint32_t vw[VW];
-#pragma unroll
-    for (int x = 0; x < VW / 4; ++x) {
-      const uint4_t t = *reinterpret_cast<const uint4_t*>(slot + SG::OFF_V + 16 * (VW / 4) * lane + 16 * x);
-      vw[4 * x] = t[0]; vw[4 * x + 1] = t[1]; vw[4 * x + 2] = t[2]; vw[4 * x + 3] = t[3];
-    }
-    if constexpr (VW == 2) {
-      const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_V + 8 * lane);
-      vw[0] = t.x; vw[1] = t.y;
-    }
-    uint32_t vx[VW], vy[VW];
-    if constexpr (VB == 2) {
-#pragma unroll
-      for (int x = 0; x < VW; ++x) {
-        vx[x] = (vw[x] << 2) & 0x3C3C3C3Cu;
-        vy[x] = (vw[x] >> 2) & 0x3C3C3C3Cu;
-      }
-    }
-    auto entry = [&](int pp) -> uint32_t {
-      if constexpr (VB == 2) {
-        const uint32_t src = (pp & 1) ? vy[pp / 8] : vx[pp / 8];
-        const int byte = (pp % 8) / 2;
-        // one byte-select per offset (v_perm_b32: byte `byte` of src, upper bytes zero)
-        const uint32_t off = __builtin_amdgcn_perm(0u, src, 0x0C0C0C00u | static_cast<uint32_t>(byte));
-        return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(vtab) + off);
-      } else {
-        return vtab[(vw[pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
-      }
-    };
+    // ---- value contractions, one channel tile at a time (operands built before the visit)
     // the operand of one accumulator keeps, in each lane, the tokens of its column's
     // modality (dword qd holds tokens 2 (qd & 1), + 1 of byte group qd >> 1)
     auto keep = [&](uint32_t mod, uint32_t (&k4)[4]) {
@@ -1027,11 +1039,8 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       const uint4_t bl = uint4_t{blo[0] & k4[0], blo[1] & k4[1], blo[2] & k4[2], blo[3] & k4[3]};
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        uint4_t av;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = entry(4 * u + i);
-        A[u] = mfma16(av, bh, A[u]);
-        A[u] = mfma16(av, bl, A[u]);
+        A[u] = mfma16(av[u], bh, A[u]);
+        A[u] = mfma16(av[u], bl, A[u]);
       }
     };
     // which accumulators the window needs (wave-uniform)
@@ -1096,7 +1105,11 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     if constexpr (MX) mx_expand(slot);
     float4_t cs[2], cm;
     score_mma(slot, cs, cm);
-    visit(slot, (wbeg + i) * kWindow, cs, cm);
+    // (kept apart: mixed into the score section, the table reads serialize its LDS loads)
+    __builtin_amdgcn_sched_barrier(0);
+    uint4_t av[NU];
+    value_operands(slot, av);
+    visit(slot, (wbeg + i) * kWindow, cs, cm, av);
   }
 
   __builtin_amdgcn_s_setprio(0);
