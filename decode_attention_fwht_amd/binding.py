@@ -67,6 +67,10 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    # torch first: its HIP runtime then provides the library's libamdhip64.so.7 too (same
+    # soname), so device memory, streams and graphs all belong to one runtime.  Loaded the
+    # other way round, torch would bind to the system runtime and find no GPU.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.omnikv_create.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, ctypes.POINTER(vp)]

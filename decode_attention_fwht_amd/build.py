@@ -20,7 +20,9 @@ SOURCES = ["api.hip", "quantize_keys.hip", "quantize_values.hip", "decode.hip", 
 # decode.hip: matrix-core results in ordinary VGPRs, and the scheduler strategy that maximizes
 # instruction-level parallelism (the decode partial is bound by instruction issue at two waves
 # per SIMD; this ordering measured ~2 us faster per launch at 16 x 32k tokens, same results)
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+         # (keeps the value quantizer within four waves per SIMD)
+         "quantize_values.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

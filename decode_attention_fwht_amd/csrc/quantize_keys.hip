@@ -77,21 +77,23 @@ __device__ __forceinline__ uint32_t row_shl(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x100 + N, 0xF, 0xF, false));
 }
 
-// value of lane l ^ (1 << k) within each 16-lane row (k = 0 .. 3)
+// value of lane l ^ (1 << k) within each 16-lane row (k = 0 .. 3).  Each move reads a
+// valid source lane for every lane it writes, so no lane needs a prior value (no zero fill
+// or copy before the move).
 template <int K>
 __device__ __forceinline__ float row_xor(float x) {
   const int v = __builtin_bit_cast(int, x);
   if constexpr (K == 0) {  // quad_perm [1, 0, 3, 2]
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
   } else if constexpr (K == 1) {  // quad_perm [2, 3, 0, 1]
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
   } else if constexpr (K == 2) {
     // lanes 0-3 and 8-11 of a row read lane + 4 (row_shl:4), lanes 4-7 and 12-15 lane - 4
     // (row_shr:4); the bank mask picks which lanes each move writes
-    const int lo = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);
+    const int lo = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0x5, false);
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(lo, v, 0x114, 0xF, 0xA, false));
   } else {  // row_ror:8
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
   }
 }
 
@@ -134,8 +136,8 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
   constexpr int XS = D == 128 ? 4 : 3;       // cross-lane stages (lane bits 0 .. XS-1)
   __shared__ uint8_t codes_lds[kWavesPerBlock][kWindow][ROW];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t task = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t task = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;  // wave-uniform (scalar math)
   const bool active = task < tasks;
   const int64_t nw = n / kWindow;
   // task -> (b, window, head), heads fastest so a block reads adjacent token rows
@@ -284,35 +286,38 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
       }
     }
     // code = #{j : y >= m + s (j + 1/2)}; the thresholds rise with j, so for 4-bit codes a
-    // binary search over j finds the same count
+    // binary search over j finds the same count.  A pass's eight codes (one byte each) go
+    // to LDS with one 8-byte store.
+    float th[8][KB == 2 ? L : 1];
+    if constexpr (KB == 2) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (KB == 2) {
-        float th[L];
+      for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int j = 0; j < L; ++j) th[j] = mf[e] + sf[e] * (static_cast<float>(j) + 0.5f);
+        for (int j = 0; j < L; ++j) th[e][j] = mf[e] + sf[e] * (static_cast<float>(j) + 0.5f);
+    }
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp) {
-          int code = 0;
+    for (int pp = 0; pp < NP; ++pp) {
+      uint32_t cw[2] = {0u, 0u};
 #pragma unroll
-          for (int j = 0; j < L; ++j) code += (y[pp][e] >= th[j]) ? 1 : 0;
-          codes_lds[wave][TPI * pp + r][8 * q + e] = static_cast<uint8_t>(code);
-        }
-      } else {
+      for (int e = 0; e < 8; ++e) {
+        int code = 0;
+        if constexpr (KB == 2) {
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp) {
-          int code = 0;  // invariant: y >= theta_j for every j < code
+          for (int j = 0; j < L; ++j) code += (y[pp][e] >= th[e][j]) ? 1 : 0;
+        } else {
+          // invariant: y >= theta_j for every j < code
 #pragma unroll
           for (int stp = 8; stp >= 1; stp >>= 1) {
             const int j = code + stp - 1;  // candidate: is y >= theta_j ?
             if (j < L) {
-              const float th = mf[e] + sf[e] * (static_cast<float>(j) + 0.5f);
-              code = (y[pp][e] >= th) ? code + stp : code;
+              const float thj = mf[e] + sf[e] * (static_cast<float>(j) + 0.5f);
+              code = (y[pp][e] >= thj) ? code + stp : code;
             }
           }
-          codes_lds[wave][TPI * pp + r][8 * q + e] = static_cast<uint8_t>(code);
         }
+        cw[e >> 2] |= static_cast<uint32_t>(code) << (8 * (e & 3));
       }
+      *reinterpret_cast<uint2*>(&codes_lds[wave][TPI * pp + r][8 * q]) = make_uint2(cw[0], cw[1]);
     }
   }
   __syncthreads();
@@ -322,17 +327,20 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
   uint32_t words[KW];
 #pragma unroll
   for (int x = 0; x < KW; ++x) words[x] = 0u;
+  // codes j = 2i and 2i + 1 of a group of eight share a word, 16 bits apart: one byte
+  // select puts both in place, one shift-or adds them to the word
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const uint2 eight = *reinterpret_cast<const uint2*>(&codes_lds[wave][16 * tau + rho][g * (D / 4) + 8 * s]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t code = ((j < 4 ? eight.x : eight.y) >> (8 * (j & 3))) & 0xFFu;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t src = i < 2 ? eight.x : eight.y;
+        const uint32_t pair = __builtin_amdgcn_perm(0u, src, (i & 1) ? 0x0C030C02u : 0x0C010C00u);
         int lw, bit;
-        key_slot<D, KB>(tau, s, j, lw, bit);
-        words[lw] |= code << bit;
+        key_slot<D, KB>(tau, s, 2 * i, lw, bit);
+        words[lw] |= pair << bit;
       }
     }
   }

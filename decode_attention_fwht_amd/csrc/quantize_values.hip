@@ -225,7 +225,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxFlags = 512;  // near-threshold elements per window handled one by one
+constexpr int kNearList = 1024;  // near-threshold elements per block shared out by the block
 
 template <int D, int VB>
 __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
@@ -233,22 +233,23 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
     int64_t t0, int64_t t_cap, int64_t tasks, const uint4_t* __restrict__ rot_b16,
     const float* __restrict__ rot_t, const float* __restrict__ boundaries, float eps_c,
     uint32_t* __restrict__ v_codes, uint16_t* __restrict__ v_scale) {
-  constexpr int NC = D / 64;
   constexpr int NCT = D / 16;                 // channel tiles
   constexpr int NKS = D / 32;                 // k-steps
   constexpr int NB = (1 << VB) - 1;           // boundaries
   constexpr int VW = D * VB / 64;             // output words per lane
   constexpr int PPW = 16 / VB;                // code pairs per word
-  constexpr int ROW = D + 8;
-  __shared__ uint8_t codes_lds[kWaves][kWindow][ROW];
+  constexpr int TPW = PPW / 4;                // channel tiles per output word
   __shared__ float sig_lds[kWaves][kWindow];
   __shared__ float eps_lds[kWaves][kWindow];
-  __shared__ uint8_t tag_lds[kWaves][kWindow];
-  __shared__ uint16_t flag_lds[kWaves][kMaxFlags];
-  __shared__ int nflag_lds[kWaves];
+  // elements near a threshold, block-wide: (wave, token, channel, modality) entries, and
+  // the sequential definition's codes for them
+  __shared__ uint32_t near_list[kNearList];
+  __shared__ int near_count;
+  __shared__ uint64_t row0_lds[kWaves];
+  __shared__ uint8_t fix_lds[kWaves][kWindow][D];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t task = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t task = static_cast<int64_t>(blockIdx.x) * kWaves + wave;  // wave-uniform (scalar math)
   const bool active = task < tasks;
   const int64_t nw = n / kWindow;
   const int64_t b = active ? task / (nw * hkv) : 0;
@@ -258,120 +259,174 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
   const size_t blk = (static_cast<size_t>(b) * hkv + h) * (t_cap / kWindow) + tok0 / kWindow;
   const size_t row0 = ((static_cast<size_t>(b) * n + w * kWindow) * hkv + h) * D;  // element of token 0
   const size_t rstride = static_cast<size_t>(hkv) * D;                             // elements per token
+  const int nn = lane & 15, g = lane >> 4;
 
+  // ---- the window as matrix-core A operands: lane (nn, g) holds token 16 tt + nn,
+  // channels 32 ks + 8 g .. + 7 (bf16 as they come)
+  uint4_t av[2][NKS];
+  uint32_t tw[8];
   if (active) {
-    // ---- tags
-    const uint8_t* tagp = modality + static_cast<size_t>(b) * t_cap + tok0;
-    uint32_t present = 0u;
-    {
-      uint32_t tw[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) tw[x] = reinterpret_cast<const uint32_t*>(tagp)[x];
-#pragma unroll
-      for (int t = 0; t < kWindow; ++t) {
-        const uint32_t tg = min((tw[t >> 2] >> (8 * (t & 3))) & 0xFFu, static_cast<uint32_t>(kMaxModalities - 1));
-        present |= 1u << tg;
-      }
-      if (lane < kWindow)
-        tag_lds[wave][lane] = static_cast<uint8_t>(
-            min((tw[lane >> 2] >> (8 * (lane & 3))) & 0xFFu, static_cast<uint32_t>(kMaxModalities - 1)));
-    }
-    if (lane == 0) nflag_lds[wave] = 0;
-
-    // ---- per-token scale: stride-halving tree of squares (lane l holds channels l, l + 64).
-    // The 32 trees run as one reduce-scatter: the stage across lane bit b (b = 5 .. 1) adds
-    // the partner's partial sums for half of the lane's tokens and leaves the other half to
-    // the partner, so after five stages lane l holds token l >> 1 alone, and the last stage
-    // (bit 0) completes it in both lanes of the pair.  Every sum is the tree's own (each
-    // stage adds the same two partial sums as the stride-halving definition), so the result
-    // is the definition's exactly; no stage waits on another token's shuffles.
-    {
-      float x[kWindow][NC];
-#pragma unroll
-      for (int t = 0; t < kWindow; ++t)
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          x[t][c] = __uint_as_float(static_cast<uint32_t>(v[row0 + t * rstride + lane + 64 * c]) << 16);
-      float part[kWindow];
-      uint32_t nzbits = 0u;  // tokens with a nonzero magnitude bit in this lane (subnormals count)
-#pragma unroll
-      for (int t = 0; t < kWindow; ++t) {
-        part[t] = (NC == 2) ? (x[t][0] * x[t][0] + x[t][1] * x[t][1]) : x[t][0] * x[t][0];
-        uint32_t mag = 0u;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) mag |= __float_as_uint(x[t][c]) & 0x7FFFFFFFu;
-        nzbits |= (mag != 0u ? 1u : 0u) << t;
-      }
-#pragma unroll
-      for (int hh = 32; hh >= 1; hh >>= 1) nzbits |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(nzbits), hh, 64));
-      // reduce-scatter over lane bits 5 .. 1; part[k] is then the partial sum of token base + k
-      int base = 0;
-      auto stage = [&](auto st_c) {
-        constexpr int st = decltype(st_c)::value, cnt = 1 << (st - 1);
-        const bool up = (lane >> st) & 1;
-#pragma unroll
-        for (int k = 0; k < cnt; ++k) {
-          const float give = up ? part[k] : part[cnt + k];
-          const float keep = up ? part[cnt + k] : part[k];
-          part[k] = keep + __shfl_xor(give, 1 << st, 64);
-        }
-        base += up ? cnt : 0;
-      };
-      stage(std::integral_constant<int, 5>{});
-      stage(std::integral_constant<int, 4>{});
-      stage(std::integral_constant<int, 3>{});
-      stage(std::integral_constant<int, 2>{});
-      stage(std::integral_constant<int, 1>{});
-      const float S = part[0] + __shfl_xor(part[0], 1, 64);  // token base = lane >> 1
-      const float sigma = sqrtf(S * (1.0f / static_cast<float>(D)));
-      const uint16_t s16 = f16_bits(sigma);
-      if ((lane & 1) == 0) {
-        const int t = base;
-        sig_lds[wave][t] = f16_value(s16);
-        eps_lds[wave][t] = ((nzbits >> t) & 1u) ? eps_c * sqrtf(S) + 1e-20f : -1.0f;
-        v_scale[(static_cast<size_t>(b) * hkv + h) * t_cap + tok0 + t] = s16;
-      }
-    }
-
-    // ---- the window as matrix-core A operands: token 16 tt + n, channels 32 ks + 8 g ..
-    const int nn = lane & 15, g = lane >> 4;
-    uint4_t av[2][NKS];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         av[tt][ks] = *reinterpret_cast<const uint4_t*>(v + row0 + (16 * tt + nn) * rstride + 32 * ks + 8 * g);
+    const uint32_t* tagp = reinterpret_cast<const uint32_t*>(modality + static_cast<size_t>(b) * t_cap + tok0);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) tw[x] = tagp[x];
+  }
+
+  // ---- per-token scale, from the operands already in registers.  The stride-halving tree
+  // of squares pairs channels c and c + 64 (d = 128: k-steps ks and ks + 2 of the lane),
+  // then c + 32 (k-steps 0 and 1), c + 16 (lanes g and g + 2: lane ^ 32), c + 8 (g and
+  // g + 1: lane ^ 16), then 4, 2, 1 inside the lane.  A cross-lane level adds the two lanes' partial sums,
+  // which both lanes then hold, so the four lanes of a token all end with its S; every sum
+  // is the tree's own, so S is the definition's exactly.
+  float S[2];
+  uint32_t nz[2];
+  if (active) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float sq[NKS][8];
+      uint32_t mag = 0u;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t wd = av[tt][ks][x];
+          mag |= wd & 0x7FFF7FFFu;
+          const float lo = __uint_as_float(wd << 16), hi = __uint_as_float(wd & 0xFFFF0000u);
+          sq[ks][2 * x] = lo * lo;
+          sq[ks][2 * x + 1] = hi * hi;
+        }
+      }
+      float s2[8];
+      if constexpr (NKS == 4) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2[e] = (sq[0][e] + sq[2][e]) + (sq[1][e] + sq[3][e]);
+      } else {  // d = 64: pairs (c, c + 32) are k-steps 0 and 1
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2[e] = sq[0][e] + sq[1][e];
+      }
+      // channel 8 g + e: lanes g and g + 2, then g and g + 1
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(s2[e]), __float_as_uint(s2[e]), false, false);
+        s2[e] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2[e]), __float_as_uint(s2[e]), false, false);
+        s2[e] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+      }
+      const float s5[4] = {s2[0] + s2[4], s2[1] + s2[5], s2[2] + s2[6], s2[3] + s2[7]};
+      S[tt] = (s5[0] + s5[2]) + (s5[1] + s5[3]);
+      // tokens with a nonzero magnitude bit (subnormals count), over the four lanes
+      const auto p32 = __builtin_amdgcn_permlane32_swap(mag, mag, false, false);
+      mag = p32[0] | p32[1];
+      const auto p16 = __builtin_amdgcn_permlane16_swap(mag, mag, false, false);
+      nz[tt] = p16[0] | p16[1];
+    }
+  }
+  if (threadIdx.x == 0) near_count = 0;
+  if (lane == 0) row0_lds[wave] = row0;
+  if (active && g == 0) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const float sigma = sqrtf(S[tt] * (1.0f / static_cast<float>(D)));
+      const uint16_t s16 = f16_bits(sigma);
+      const int t = 16 * tt + nn;
+      sig_lds[wave][t] = f16_value(s16);
+      eps_lds[wave][t] = nz[tt] != 0u ? eps_c * sqrtf(S[tt]) + 1e-20f : -1.0f;
+      v_scale[(static_cast<size_t>(b) * hkv + h) * t_cap + tok0 + t] = s16;
+    }
+  }
+  __syncthreads();
+
+  // ---- rotation on the matrix cores, then the codes.  Lane (nn, g) of channel tile ct holds
+  // channel 16 ct + nn of tokens 16 tt + 4 g + i: exactly the codes of its own output words
+  // in the window-block layout, so the lane packs them in place.
+  uint32_t words[VW];
+#pragma unroll
+  for (int x = 0; x < VW; ++x) words[x] = 0u;
+  uint64_t near_bits = 0u;  // element (ct, tt, i) at bit 8 ct + 4 tt + i
+  uint32_t my_tag[2][4];    // modality of this lane's result tokens 16 tt + 4 g + i
+  if (active) {
+    uint32_t present = 0u;
+#pragma unroll
+    for (int t = 0; t < kWindow; ++t)
+      present |= 1u << min((tw[t >> 2] >> (8 * (t & 3))) & 0xFFu, static_cast<uint32_t>(kMaxModalities - 1));
+    // scales, tolerances and (2-bit) thresholds of the lane's result tokens.  A token whose
+    // thresholds are not all finite (an infinite scale) gets an infinite tolerance: all its
+    // elements take the sequential definition.
+    constexpr bool kTwoBit = NB == 3;
+    float th[2][4][kTwoBit ? NB : 1], my_sg[2][4], my_ep[2][4];
     float beta[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) beta[j] = boundaries[j];
-    // this lane's result tokens (16 tt + 4 g + i) and their modalities
-    uint32_t my_tag[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) my_tag[tt][i] = tag_lds[wave][16 * tt + 4 * g + i];
-    // and their scales and tolerances, read once for all channel tiles
-    float my_sg[2][4], my_ep[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t tword = g == 0 ? tw[4 * tt] : (g == 1 ? tw[4 * tt + 1] : (g == 2 ? tw[4 * tt + 2] : tw[4 * tt + 3]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        my_tag[tt][i] = min((tword >> (8 * i)) & 0xFFu, static_cast<uint32_t>(kMaxModalities - 1));
         my_sg[tt][i] = sig_lds[wave][16 * tt + 4 * g + i];
-        my_ep[tt][i] = eps_lds[wave][16 * tt + 4 * g + i];
+        const float ep = eps_lds[wave][16 * tt + 4 * g + i];
+        my_ep[tt][i] = __builtin_isfinite(my_sg[tt][i]) ? ep : INFINITY;
+        if constexpr (kTwoBit) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) th[tt][i][j] = my_sg[tt][i] * beta[j];
+        }
       }
-
-    // ---- one pass per modality present
+    }
+    // one channel tile's eight results -> codes (tt, i) at bit VB (4 tt + i) of `bits` and
+    // near-threshold flags at bit 4 tt + i of `nearm`, for the tokens of modality m
+    auto classify = [&](const float4_t (&acc)[2], uint32_t m, bool mixed, uint32_t& bits, uint32_t& nearm) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = acc[tt][i];
+          uint32_t code;
+          bool near;
+          if constexpr (kTwoBit) {
+            // the thresholds rise (finite scale), so the three comparisons form a
+            // thermometer: code = c0 + c1 + c2 has high bit c1 and low bit c0 ^ c1 ^ c2
+            const bool c0 = x >= th[tt][i][0], c1 = x >= th[tt][i][1], c2 = x >= th[tt][i][2];
+            code = (c1 ? 2u : 0u) | ((c0 ^ c1 ^ c2) ? 1u : 0u);
+            // a NaN distance (NaN sum) stays NaN through the min and counts as near
+            const float dmin = fminf(fminf(fabsf(x - th[tt][i][0]), fabsf(x - th[tt][i][1])), fabsf(x - th[tt][i][2]));
+            near = !(dmin > my_ep[tt][i]);
+          } else {
+            code = 0u;
+            near = false;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              const float thj = my_sg[tt][i] * beta[j];
+              code += (x >= thj) ? 1u : 0u;
+              near = near || !(fabsf(x - thj) > my_ep[tt][i]);  // NaN or infinite sums count
+            }
+          }
+          const bool mine = !mixed || my_tag[tt][i] == m;
+          bits |= (mine ? code : 0u) << (VB * (4 * tt + i));
+          nearm |= (near && mine ? 1u : 0u) << (4 * tt + i);
+        }
+    };
 #pragma unroll
     for (int m = 0; m < kMaxModalities; ++m) {
       if (!(present & (1u << m))) continue;
+      const bool mixed = present != (1u << m);  // wave-uniform
       const uint4_t* B = rot_b16 + static_cast<size_t>(m) * 3 * NCT * NKS * 64 + lane;
-#pragma unroll 2
+      // U_m's tiles come from L2: all eight of a channel tile are requested before its
+      // products (a barrier keeps the scheduler from sinking each load to its use)
+#pragma unroll 1
       for (int ct = 0; ct < NCT; ++ct) {
         uint4_t bv[2][NKS];
 #pragma unroll
         for (int part = 0; part < 2; ++part)
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) bv[part][ks] = B[((part * NCT + ct) * NKS + ks) * 64];
+        __builtin_amdgcn_sched_barrier(0);
         float4_t acc[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int part = 0; part < 2; ++part)
@@ -381,86 +436,93 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
             for (int tt = 0; tt < 2; ++tt)
               acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[tt][ks]),
                                                                 __builtin_bit_cast(bf16x8_t, bv[part][ks]), acc[tt], 0, 0, 0);
-        const int c = 16 * ct + nn;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (my_tag[tt][i] != static_cast<uint32_t>(m)) continue;
-            const int t = 16 * tt + 4 * g + i;
-            const float x = acc[tt][i];
-            const float sg = my_sg[tt][i], e = my_ep[tt][i];
-            int code = 0;
-            bool near = false;
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-              const float th = sg * beta[j];
-              code += (x >= th) ? 1 : 0;
-              near = near || !(fabsf(x - th) > e);  // NaN or infinite sums count as near
-            }
-            codes_lds[wave][t][c] = static_cast<uint8_t>(code);
-            if (near) {
-              const int idx = atomicAdd(&nflag_lds[wave], 1);
-              if (idx < kMaxFlags) flag_lds[wave][idx] = static_cast<uint16_t>((t << 8) | c);
-            }
-          }
+        uint32_t bits = 0u, nearm = 0u;
+        if (kTwoBit && !mixed)  // (a copy without the modality test for the common case)
+          classify(acc, static_cast<uint32_t>(m), false, bits, nearm);
+        else
+          classify(acc, static_cast<uint32_t>(m), mixed, bits, nearm);
+        // token pair p = 4 ct + 2 tt + (i >> 1) goes to word p / PPW at bit 2 VB (p % PPW) +
+        // VB (i & 1) = 8 VB (ct % TPW) + VB (4 tt + i), TPW = PPW / 4 tiles per word
+        words[ct / TPW] |= bits << (8 * VB * (ct % TPW));
+        near_bits |= static_cast<uint64_t>(nearm) << (8 * ct);
       }
     }
+  }
 
-    // ---- the sequential definition for the elements near a threshold
-    auto exact_code = [&](int t, int c) {
-      const float* ut = rot_t + (static_cast<size_t>(tag_lds[wave][t]) * D + c) * D;
-      const uint16_t* vr = v + row0 + t * rstride;
-      float s = 0.0f;
-      for (int k0 = 0; k0 < D; k0 += 8) {
-        const float4 u0 = *reinterpret_cast<const float4*>(ut + k0);
-        const float4 u1 = *reinterpret_cast<const float4*>(ut + k0 + 4);
-        const uint4_t vb = *reinterpret_cast<const uint4_t*>(vr + k0);
-        const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+  // ---- the sequential definition for the elements near a threshold (rare).  The block's
+  // flagged elements go to one list, which the block's threads share out, so one pass of
+  // the 128-term sum covers what would otherwise cost each wave a pass of its own.
+  auto exact_code = [&](int ew, int t, int c, uint32_t tg) -> uint32_t {
+    const float* ut = rot_t + (static_cast<size_t>(tg) * D + c) * D;
+    const uint16_t* vr = v + row0_lds[ew] + t * rstride;
+    float s = 0.0f;
+    for (int k0 = 0; k0 < D; k0 += 8) {
+      const float4 u0 = *reinterpret_cast<const float4*>(ut + k0);
+      const float4 u1 = *reinterpret_cast<const float4*>(ut + k0 + 4);
+      const uint4_t vb = *reinterpret_cast<const uint4_t*>(vr + k0);
+      const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const uint32_t half = (vb[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu;
-          s = s + uu[kk] * __uint_as_float(half << 16);
-        }
+      for (int kk = 0; kk < 8; ++kk) {
+        const uint32_t half = (vb[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu;
+        s = s + uu[kk] * __uint_as_float(half << 16);
       }
-      const float sg = sig_lds[wave][t];
-      int code = 0;
+    }
+    const float sg = sig_lds[ew][t];
+    uint32_t code = 0;
+    for (int j = 0; j < NB; ++j) code += (s >= sg * boundaries[j]) ? 1u : 0u;
+    return code;
+  };
+  // the modality of this lane's element (tt, i) (selects over the unrolled indices keep
+  // the array in registers)
+  auto tag_of = [&](int tt, int i) {
+    uint32_t tg = 0u;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) code += (s >= sg * beta[j]) ? 1 : 0;
-      codes_lds[wave][t][c] = static_cast<uint8_t>(code);
-    };
-    const int nf = nflag_lds[wave];
-    if (nf <= kMaxFlags) {
-      for (int f = lane; f < nf; f += 64) {
-        const uint32_t e = flag_lds[wave][f];
-        exact_code(static_cast<int>(e >> 8), static_cast<int>(e & 0xFFu));
-      }
-    } else {
-      // too many elements near a threshold (all-zero tokens, say): the whole window by the
-      // definition
-      for (int e = lane; e < kWindow * D; e += 64) exact_code(e / D, e % D);
+    for (int x = 0; x < 8; ++x)
+      if (x == 4 * tt + i) tg = my_tag[x >> 2][x & 3];
+    return tg;
+  };
+  uint64_t own = 0u;  // flagged elements the list had no room for: this lane computes them
+  if (active) {
+    uint64_t todo = near_bits;
+    while (todo != 0u) {
+      const int k = __builtin_ctzll(todo);
+      todo &= todo - 1u;
+      const int ct = k >> 3, tt = (k >> 2) & 1, i = k & 3;
+      const int idx = atomicAdd(&near_count, 1);
+      if (idx < kNearList)
+        near_list[idx] = (static_cast<uint32_t>(wave) << 14) | (static_cast<uint32_t>(16 * tt + 4 * g + i) << 9) |
+                         (static_cast<uint32_t>(16 * ct + nn) << 2) | tag_of(tt, i);
+      else
+        own |= uint64_t{1} << k;
     }
   }
   __syncthreads();
-  if (!active) return;
-  // pack: lane = 16 g + rho holds channels 16 u + rho of tokens {4g..4g+3, 16+4g..16+4g+3}
-  const int rho = lane & 15, g = lane >> 4;
-  uint32_t words[VW];
-#pragma unroll
-  for (int x = 0; x < VW; ++x) words[x] = 0u;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-#pragma unroll
-    for (int u = 0; u < D / 16; ++u) {
-      const uint32_t code = codes_lds[wave][t][16 * u + rho];
-      const int p = 4 * u + (j >> 1);
-      words[p / PPW] |= code << (2 * VB * (p % PPW) + VB * (j & 1));
+  {
+    const int total = min(near_count, kNearList);
+    for (int e = threadIdx.x; e < total; e += kWaves * 64) {
+      const uint32_t en = near_list[e];
+      const int ew = static_cast<int>(en >> 14), t = static_cast<int>((en >> 9) & 31u), c = static_cast<int>((en >> 2) & 127u);
+      fix_lds[ew][t][c] = static_cast<uint8_t>(exact_code(ew, t, c, en & 3u));
     }
   }
-  uint32_t* dst = v_codes + blk * (D * VB) + lane * VW;
+  __syncthreads();
+  if (active) {
+    uint64_t todo = near_bits;
+    while (todo != 0u) {
+      const int k = __builtin_ctzll(todo);
+      todo &= todo - 1u;
+      const int ct = k >> 3, tt = (k >> 2) & 1, i = k & 3;
+      const int t = 16 * tt + 4 * g + i, c = 16 * ct + nn;
+      const uint32_t code = ((own >> k) & 1u) ? exact_code(wave, t, c, tag_of(tt, i)) : fix_lds[wave][t][c];
+      const int bit = 8 * VB * (ct % TPW) + 4 * VB * tt + VB * i;
 #pragma unroll
-  for (int x = 0; x < VW; x += 2) *reinterpret_cast<uint2*>(dst + x) = make_uint2(words[x], words[x + 1]);
+      for (int x = 0; x < VW; ++x)
+        if (x == ct / TPW) words[x] = (words[x] & ~(((1u << VB) - 1u) << bit)) | (code << bit);
+    }
+    uint32_t* dst = v_codes + blk * (D * VB) + lane * VW;
+#pragma unroll
+    for (int x = 0; x < VW; x += 2) *reinterpret_cast<uint2*>(dst + x) = make_uint2(words[x], words[x + 1]);
+  }
 }
 
 // The tolerance eps_t = eps ||v_t||_2 between the matrix-core value and the sequential
