@@ -216,6 +216,31 @@ def _replay_ms(g, reps):
     return [ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
 
 
+def time_stream_append(ctx, cfg, cache, rings, n0, steps=128, reps=10):
+    """omnikv_stream_append for the whole batch in lockstep: `steps` consecutive tokens from
+    length n0, so the 32-token value windows and the 128-token key groups cross their
+    thresholds as in generation (each crossing is one flush launch for the batch).  The
+    calls are captured in one graph; microseconds per append call, from its replays."""
+    import torch
+    B, H, d = cfg.batch, cfg.kv_heads, cfg.head_dim
+    g = torch.Generator(device="cuda").manual_seed(7)
+    k_new = torch.randn(B, H, d, device="cuda", generator=g).to(torch.bfloat16)
+    v_new = torch.randn(B, H, d, device="cuda", generator=g).to(torch.bfloat16)
+    t_new = torch.zeros(B, dtype=torch.uint8, device="cuda")
+    lens_dev = [torch.full((B,), n0 + i, dtype=torch.int32, device="cuda") for i in range(steps)]
+    lens_host = [[n0 + i] * B for i in range(steps)]
+    graph = _graph(lambda i: ctx.stream_append(k_new, v_new, t_new, lens_dev[i], lens_host[i], cache, rings), steps)
+    graph.replay()
+    torch.cuda.synchronize()
+    us = [ms * 1e3 / steps for ms in _replay_ms(graph, reps)]
+    del graph
+    kp = [binding.Context.stream_packed_lengths(n0 + i) for i in range(steps + 1)]
+    key_flushes = sum(kp[i + 1][0] > kp[i][0] for i in range(steps))
+    value_flushes = sum(kp[i + 1][1] > kp[i][1] for i in range(steps))
+    return {"append_us": _spread(us), "tokens": steps, "from_length": n0, "batch": B,
+            "key_flush_launches": int(key_flushes), "value_flush_launches": int(value_flushes)}
+
+
 def _spread(us):
     a = np.asarray(us, np.float64)
     return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
@@ -357,6 +382,7 @@ def main():
     torch.cuda.synchronize()
     stream_us = [ms * 1e3 / args.steps for ms in _replay_ms(g_stream, max(5, args.replays // 3))]
     del g_stream
+    append = time_stream_append(ctx, cfg, caches[0], rings, T - 192)
 
     # the same step with MXFP4 key metadata (the paper's default format): its own context
     # and caches, enough of them to exceed the MALL
@@ -395,7 +421,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(f"{cfg.name} K{args.kbits}V{args.vbits} splits {args.splits}")},
         "write_path": write_path,
-        "streaming": {"step_us": _spread(stream_us), "recent_tokens_per_sequence": T - vp, "packed_key_tokens": kp},
+        "streaming": {"step_us": _spread(stream_us), "recent_tokens_per_sequence": T - vp, "packed_key_tokens": kp,
+                      "append": append},
         "key_meta_mxfp4": mx,
     }
     del caches, rings, r, q, lens, ws, out

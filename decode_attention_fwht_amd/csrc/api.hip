@@ -317,7 +317,10 @@ omnikv_status omnikv_quantize_keys(const omnikv_ctx* ctx, const void* k, omnikv_
     return fail(OMNIKV_EINVAL, "quantize_keys: device pointers must be 16-byte aligned");
   if (dt != OMNIKV_F32 && dt != OMNIKV_BF16) return fail(OMNIKV_EINVAL, "quantize_keys: dtype must be F32 or BF16");
   if ((st = check_chunk(batch, t0, n, t_cap)) != OMNIKV_OK) return st;
-  const hipError_t e = omnikv::launch_quantize_keys(ctx->sh, ctx->tb, k, dt == OMNIKV_BF16, batch, t0, n, t_cap,
+  omnikv::WindowSource src;
+  src.n = n;
+  src.t0 = t0;
+  const hipError_t e = omnikv::launch_quantize_keys(ctx->sh, ctx->tb, k, dt == OMNIKV_BF16, batch, src, t_cap,
                                                     k_codes, k_min, k_scale, stream);
   if (e != hipSuccess) return hip_fail(e, "quantize_keys launch");
   return OMNIKV_OK;
@@ -333,7 +336,10 @@ omnikv_status omnikv_quantize_values(const omnikv_ctx* ctx, const void* v, omnik
     return fail(OMNIKV_EINVAL, "quantize_values: device pointers must be 16-byte aligned");
   if (dt != OMNIKV_F32 && dt != OMNIKV_BF16) return fail(OMNIKV_EINVAL, "quantize_values: dtype must be F32 or BF16");
   if ((st = check_chunk(batch, t0, n, t_cap)) != OMNIKV_OK) return st;
-  const hipError_t e = omnikv::launch_quantize_values(ctx->sh, ctx->tb, v, dt == OMNIKV_BF16, modality, batch, t0, n,
+  omnikv::WindowSource src;
+  src.n = n;
+  src.t0 = t0;
+  const hipError_t e = omnikv::launch_quantize_values(ctx->sh, ctx->tb, v, dt == OMNIKV_BF16, modality, batch, src,
                                                       t_cap, v_codes, v_scale, stream);
   if (e != hipSuccess) return hip_fail(e, "quantize_values launch");
   return OMNIKV_OK;
@@ -483,33 +489,29 @@ omnikv_status omnikv_stream_append(const omnikv_ctx* ctx, const void* k_new, con
   hipError_t e = omnikv::launch_stream_append(sh, k_new, v_new, f32, tags_new, lens, batch, k_ring, v_ring, ring_cap,
                                               modality, t_cap, stream);
   if (e != hipSuccess) return hip_fail(e, "stream_append launch");
-  // tokens that this append pushes past the schedule's thresholds are quantized from
-  // the rings, one sequence at a time (their rows are contiguous: the blocks are 32- or
-  // 128-aligned and ring_cap is a multiple of 128)
-  const size_t esz = f32 ? 4 : 2;
-  const size_t nwin = static_cast<size_t>(t_cap / omnikv::kWindow);
+  // the key groups and value windows this append moves past the schedule's thresholds are
+  // quantized from the rings: one launch for every sequence's keys and one for every
+  // sequence's values (the kernels read each sequence's length from `lens` and leave the
+  // sequences that do not flush alone), each launched only if some sequence flushes
+  bool any_k = false, any_v = false;
   for (int32_t b = 0; b < batch; ++b) {
-    const int64_t n0 = lens_host[b], n1 = n0 + 1;
-    const int64_t k0 = omnikv::stream_key_packed(n0), k1 = omnikv::stream_key_packed(n1);
-    const int64_t v0 = omnikv::stream_value_packed(n0), v1 = omnikv::stream_value_packed(n1);
-    const size_t head_win = static_cast<size_t>(b) * sh.hkv * nwin;  // first window block of sequence b
-    if (k1 > k0) {
-      const char* src = static_cast<const char*>(k_ring) + (static_cast<size_t>(b) * ring_cap + k0 % ring_cap) * sh.hkv * sh.d * esz;
-      // metadata of sequence b start head_win window records in
-      const size_t mb = head_win * omnikv::key_meta_bytes(sh);
-      e = omnikv::launch_quantize_keys(sh, ctx->tb, src, !f32, 1, k0, k1 - k0, t_cap,
-                                       k_codes + head_win * sh.d * sh.kbits,
-                                       reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(k_min) + mb),
-                                       reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(k_scale) + mb), stream);
-      if (e != hipSuccess) return hip_fail(e, "stream_append key flush");
-    }
-    if (v1 > v0) {
-      const char* src = static_cast<const char*>(v_ring) + (static_cast<size_t>(b) * ring_cap + v0 % ring_cap) * sh.hkv * sh.d * esz;
-      e = omnikv::launch_quantize_values(sh, ctx->tb, src, !f32, modality + static_cast<size_t>(b) * t_cap, 1, v0,
-                                         v1 - v0, t_cap, v_codes + head_win * sh.d * sh.vbits,
-                                         v_scale + static_cast<size_t>(b) * sh.hkv * t_cap, stream);
-      if (e != hipSuccess) return hip_fail(e, "stream_append value flush");
-    }
+    const int64_t n0 = lens_host[b];
+    any_k = any_k || omnikv::stream_key_packed(n0 + 1) > omnikv::stream_key_packed(n0);
+    any_v = any_v || omnikv::stream_value_packed(n0 + 1) > omnikv::stream_value_packed(n0);
+  }
+  omnikv::WindowSource src;
+  src.flush_lens = lens;
+  src.ring_cap = ring_cap;
+  if (any_k) {
+    src.flush_keys = 1;
+    e = omnikv::launch_quantize_keys(sh, ctx->tb, k_ring, !f32, batch, src, t_cap, k_codes, k_min, k_scale, stream);
+    if (e != hipSuccess) return hip_fail(e, "stream_append key flush");
+  }
+  if (any_v) {
+    src.flush_keys = 0;
+    e = omnikv::launch_quantize_values(sh, ctx->tb, v_ring, !f32, modality, batch, src, t_cap, v_codes, v_scale,
+                                       stream);
+    if (e != hipSuccess) return hip_fail(e, "stream_append value flush");
   }
   return OMNIKV_OK;
 }

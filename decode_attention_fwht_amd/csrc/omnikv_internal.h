@@ -72,13 +72,62 @@ inline size_t key_meta_bytes(const Shape& sh) {
   return sh.mx ? static_cast<size_t>(mx_record_bytes(sh.d)) : static_cast<size_t>(2 * sh.d);
 }
 
+// ---- which window a quantizer task (one wave: one window of one (sequence, KV head))
+// takes, and where its tokens come from.  Source tokens are rows of [rows][Hkv][d].
+//   dense chunk: the source is [batch][n][Hkv][d]; window w of sequence b covers cache
+//     tokens t0 + 32 w .. of b, read from source rows b n + 32 w ..
+//   streaming flush: the source is the rings [batch][ring_cap][Hkv][d]; lens[b] (device)
+//     is sequence b's length n before an append, and the windows are those the append
+//     moves past the schedule (keys: the 4 windows of [kp(n), kp(n + 1)) when it grows;
+//     values: the window [vp(n), vp(n + 1)) when it grows), at ring rows t % ring_cap
+//     (a 32-token window never wraps: ring_cap is a multiple of 128).  Tasks of sequences
+//     that do not flush are inactive.
+struct WindowSource {
+  const int32_t* flush_lens = nullptr;  // null: dense chunk
+  int flush_keys = 0;                   // flush mode: 1 keys, 0 values
+  int ring_cap = 0;
+  int64_t n = 0, t0 = 0;                // dense chunk
+  __host__ __device__ int64_t windows_per_sequence() const {
+    return flush_lens ? (flush_keys ? 128 / kWindow : 1) : n / kWindow;
+  }
+};
+struct WindowTask {
+  bool active;
+  int64_t b;        // sequence
+  int h;            // KV head
+  int64_t src_row;  // source row of the window's first token
+  int64_t tok0;     // cache position of the window's first token
+};
+__device__ inline WindowTask map_window_task(const WindowSource& s, int64_t task, int64_t tasks, int hkv) {
+  WindowTask r{task < tasks, 0, 0, 0, 0};
+  if (!r.active) return r;
+  const int64_t per = s.windows_per_sequence();
+  r.b = task / (per * hkv);
+  const int64_t w = (task / hkv) % per;
+  r.h = static_cast<int>(task % hkv);
+  if (!s.flush_lens) {
+    r.src_row = r.b * s.n + w * kWindow;
+    r.tok0 = s.t0 + w * kWindow;
+    return r;
+  }
+  const int64_t n0 = s.flush_lens[r.b];
+  const int64_t p0 = s.flush_keys ? stream_key_packed(n0) : stream_value_packed(n0);
+  const int64_t p1 = s.flush_keys ? stream_key_packed(n0 + 1) : stream_value_packed(n0 + 1);
+  r.active = p1 > p0;
+  r.tok0 = p0 + w * kWindow;
+  r.src_row = r.b * s.ring_cap + r.tok0 % s.ring_cap;
+  return r;
+}
+
 // ---- launchers (return hipSuccess or the launch error) -----------------------------------
+// src.n and src.t0 describe a dense chunk (batch sequences of src.n tokens from cache
+// position src.t0); src.flush_lens selects the streaming flush of `batch` sequences.
 hipError_t launch_quantize_keys(const Shape& sh, const DeviceTables& tb, const void* k, bool bf16,
-                                int batch, int64_t t0, int64_t n, int64_t t_cap, uint32_t* k_codes,
+                                int batch, const WindowSource& src, int64_t t_cap, uint32_t* k_codes,
                                 uint16_t* k_min, uint16_t* k_scale, hipStream_t stream);
 
 hipError_t launch_quantize_values(const Shape& sh, const DeviceTables& tb, const void* v, bool bf16,
-                                  const uint8_t* modality, int batch, int64_t t0, int64_t n,
+                                  const uint8_t* modality, int batch, const WindowSource& src,
                                   int64_t t_cap, uint32_t* v_codes, uint16_t* v_scale,
                                   hipStream_t stream);
 

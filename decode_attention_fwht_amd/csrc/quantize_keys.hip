@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t mx_encode(float x, float inv, int e, float& 
 
 template <int D, int KB, bool BF16, bool MX>
 __global__ __launch_bounds__(256) void quantize_keys_kernel(
-    const void* __restrict__ k, int hkv, int64_t n, int64_t w0, int64_t nwin_cap,
+    const void* __restrict__ k, int hkv, WindowSource src, int64_t nwin_cap,
     int64_t tasks, const float* __restrict__ signs, uint32_t* __restrict__ k_codes,
     uint16_t* __restrict__ k_min, uint16_t* __restrict__ k_scale) {
   constexpr int L = (1 << KB) - 1;           // largest code
@@ -138,13 +138,12 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t task = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;  // wave-uniform (scalar math)
-  const bool active = task < tasks;
-  const int64_t nw = n / kWindow;
-  // task -> (b, window, head), heads fastest so a block reads adjacent token rows
-  const int64_t b = active ? task / (nw * hkv) : 0;
-  const int64_t w = active ? (task / hkv) % nw : 0;
-  const int h = active ? static_cast<int>(task % hkv) : 0;
-  const size_t blk = (static_cast<size_t>(b) * hkv + h) * nwin_cap + w0 + w;
+  // task -> (sequence, window, head), heads fastest so a block reads adjacent token rows
+  const WindowTask wt = map_window_task(src, task, tasks, hkv);
+  const bool active = wt.active;
+  const int64_t b = wt.b;
+  const int h = wt.h;
+  const size_t blk = (static_cast<size_t>(b) * hkv + h) * nwin_cap + wt.tok0 / kWindow;
   const int q = lane % LPT, r = lane / LPT;  // channels 8q .. 8q + 7 of token TPI * pass + r
 
   if (active) {
@@ -161,7 +160,7 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
       const int t = TPI * pp + r;
-      const size_t row = ((static_cast<size_t>(b) * n + w * kWindow + t) * hkv + h) * D + 8 * q;
+      const size_t row = ((static_cast<size_t>(wt.src_row) + t) * hkv + h) * D + 8 * q;
       float z[8];
       if constexpr (BF16) {
         const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + row);
@@ -350,36 +349,36 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
 }
 
 template <int D, int KB, bool MX>
-hipError_t launch_kb(const DeviceTables& tb, const void* k, bool bf16, int hkv, int batch, int64_t t0,
-                     int64_t n, int64_t t_cap, uint32_t* kc, uint16_t* km, uint16_t* ks,
-                     hipStream_t stream) {
-  const int64_t tasks = static_cast<int64_t>(batch) * hkv * (n / kWindow);
+hipError_t launch_kb(const DeviceTables& tb, const void* k, bool bf16, int hkv, int batch, const WindowSource& src,
+                     int64_t t_cap, uint32_t* kc, uint16_t* km, uint16_t* ks, hipStream_t stream) {
+  const int64_t tasks = static_cast<int64_t>(batch) * hkv * src.windows_per_sequence();
   const dim3 grid(static_cast<unsigned>((tasks + kWavesPerBlock - 1) / kWavesPerBlock));
   if (bf16)
-    quantize_keys_kernel<D, KB, true, MX><<<grid, 256, 0, stream>>>(k, hkv, n, t0 / kWindow, t_cap / kWindow,
-                                                                    tasks, tb.signs, kc, km, ks);
+    quantize_keys_kernel<D, KB, true, MX><<<grid, 256, 0, stream>>>(k, hkv, src, t_cap / kWindow, tasks, tb.signs,
+                                                                    kc, km, ks);
   else
-    quantize_keys_kernel<D, KB, false, MX><<<grid, 256, 0, stream>>>(k, hkv, n, t0 / kWindow, t_cap / kWindow,
-                                                                     tasks, tb.signs, kc, km, ks);
+    quantize_keys_kernel<D, KB, false, MX><<<grid, 256, 0, stream>>>(k, hkv, src, t_cap / kWindow, tasks, tb.signs,
+                                                                     kc, km, ks);
   return hipGetLastError();
 }
 
 template <bool MX>
-hipError_t launch_meta(const Shape& sh, const DeviceTables& tb, const void* k, bool bf16, int batch, int64_t t0,
-                       int64_t n, int64_t t_cap, uint32_t* kc, uint16_t* km, uint16_t* ks, hipStream_t stream) {
-  if (sh.d == 128 && sh.kbits == 2) return launch_kb<128, 2, MX>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
-  if (sh.d == 128 && sh.kbits == 4) return launch_kb<128, 4, MX>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
-  if (sh.d == 64 && sh.kbits == 2) return launch_kb<64, 2, MX>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
-  return launch_kb<64, 4, MX>(tb, k, bf16, sh.hkv, batch, t0, n, t_cap, kc, km, ks, stream);
+hipError_t launch_meta(const Shape& sh, const DeviceTables& tb, const void* k, bool bf16, int batch,
+                       const WindowSource& src, int64_t t_cap, uint32_t* kc, uint16_t* km, uint16_t* ks,
+                       hipStream_t stream) {
+  if (sh.d == 128 && sh.kbits == 2) return launch_kb<128, 2, MX>(tb, k, bf16, sh.hkv, batch, src, t_cap, kc, km, ks, stream);
+  if (sh.d == 128 && sh.kbits == 4) return launch_kb<128, 4, MX>(tb, k, bf16, sh.hkv, batch, src, t_cap, kc, km, ks, stream);
+  if (sh.d == 64 && sh.kbits == 2) return launch_kb<64, 2, MX>(tb, k, bf16, sh.hkv, batch, src, t_cap, kc, km, ks, stream);
+  return launch_kb<64, 4, MX>(tb, k, bf16, sh.hkv, batch, src, t_cap, kc, km, ks, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quantize_keys(const Shape& sh, const DeviceTables& tb, const void* k, bool bf16,
-                                int batch, int64_t t0, int64_t n, int64_t t_cap, uint32_t* kc,
+                                int batch, const WindowSource& src, int64_t t_cap, uint32_t* kc,
                                 uint16_t* km, uint16_t* ks, hipStream_t stream) {
-  if (sh.mx) return launch_meta<true>(sh, tb, k, bf16, batch, t0, n, t_cap, kc, km, ks, stream);
-  return launch_meta<false>(sh, tb, k, bf16, batch, t0, n, t_cap, kc, km, ks, stream);
+  if (sh.mx) return launch_meta<true>(sh, tb, k, bf16, batch, src, t_cap, kc, km, ks, stream);
+  return launch_meta<false>(sh, tb, k, bf16, batch, src, t_cap, kc, km, ks, stream);
 }
 
 }  // namespace omnikv

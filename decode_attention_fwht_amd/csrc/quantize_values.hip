@@ -35,8 +35,8 @@ constexpr int kWaves = 4;
 
 template <int D, int VB, bool BF16>
 __global__ __launch_bounds__(256) void quantize_values_kernel(
-    const void* __restrict__ v, const uint8_t* __restrict__ modality, int hkv, int64_t n,
-    int64_t t0, int64_t t_cap, int64_t tasks, const float* __restrict__ rot,
+    const void* __restrict__ v, const uint8_t* __restrict__ modality, int hkv, WindowSource src,
+    int64_t t_cap, int64_t tasks, const float* __restrict__ rot,
     const float* __restrict__ boundaries, uint32_t* __restrict__ v_codes,
     uint16_t* __restrict__ v_scale) {
   constexpr int NC = D / 64;
@@ -49,20 +49,19 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(
   __shared__ __attribute__((aligned(16))) float vals[kWaves][D][kWindow];
   __shared__ uint8_t codes_lds[kWaves][kWindow][ROW];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t task = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  const bool active = task < tasks;
-  const int64_t nw = n / kWindow;
-  const int64_t b = active ? task / (nw * hkv) : 0;
-  const int64_t w = active ? (task / hkv) % nw : 0;
-  const int h = active ? static_cast<int>(task % hkv) : 0;
-  const int64_t tok0 = t0 + w * kWindow;                       // absolute token of the window
+  const WindowTask wt = map_window_task(src, task, tasks, hkv);
+  const bool active = wt.active;
+  const int64_t b = wt.b;
+  const int h = wt.h;
+  const int64_t tok0 = wt.tok0;                                // absolute token of the window
   const size_t blk = (static_cast<size_t>(b) * hkv + h) * (t_cap / kWindow) + tok0 / kWindow;
 
   if (active) {
 #pragma unroll 4
     for (int t = 0; t < kWindow; ++t) {
-      const size_t row = ((static_cast<size_t>(b) * n + w * kWindow + t) * hkv + h) * D;
+      const size_t row = ((static_cast<size_t>(wt.src_row) + t) * hkv + h) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) vals[wave][lane + 64 * c][t] = load_elem<BF16>(v, row + lane + 64 * c);
     }
@@ -229,8 +228,8 @@ constexpr int kNearList = 1024;  // near-threshold elements per block shared out
 
 template <int D, int VB>
 __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
-    const uint16_t* __restrict__ v, const uint8_t* __restrict__ modality, int hkv, int64_t n,
-    int64_t t0, int64_t t_cap, int64_t tasks, const uint4_t* __restrict__ rot_b16,
+    const uint16_t* __restrict__ v, const uint8_t* __restrict__ modality, int hkv, WindowSource src,
+    int64_t t_cap, int64_t tasks, const uint4_t* __restrict__ rot_b16,
     const float* __restrict__ rot_t, const float* __restrict__ boundaries, float eps_c,
     uint32_t* __restrict__ v_codes, uint16_t* __restrict__ v_scale) {
   constexpr int NCT = D / 16;                 // channel tiles
@@ -250,14 +249,13 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t task = static_cast<int64_t>(blockIdx.x) * kWaves + wave;  // wave-uniform (scalar math)
-  const bool active = task < tasks;
-  const int64_t nw = n / kWindow;
-  const int64_t b = active ? task / (nw * hkv) : 0;
-  const int64_t w = active ? (task / hkv) % nw : 0;
-  const int h = active ? static_cast<int>(task % hkv) : 0;
-  const int64_t tok0 = t0 + w * kWindow;
+  const WindowTask wt = map_window_task(src, task, tasks, hkv);
+  const bool active = wt.active;
+  const int64_t b = wt.b;
+  const int h = wt.h;
+  const int64_t tok0 = wt.tok0;
   const size_t blk = (static_cast<size_t>(b) * hkv + h) * (t_cap / kWindow) + tok0 / kWindow;
-  const size_t row0 = ((static_cast<size_t>(b) * n + w * kWindow) * hkv + h) * D;  // element of token 0
+  const size_t row0 = (static_cast<size_t>(wt.src_row) * hkv + h) * D;  // element of token 0
   const size_t rstride = static_cast<size_t>(hkv) * D;                             // elements per token
   const int nn = lane & 15, g = lane >> 4;
 
@@ -542,20 +540,20 @@ constexpr double value_eps_unit() {
 
 template <int D, int VB>
 hipError_t launch_vb(const DeviceTables& tb, const void* v, bool bf16, const uint8_t* mod, int hkv,
-                     int batch, int64_t t0, int64_t n, int64_t t_cap, uint32_t* vc, uint16_t* vs,
+                     int batch, const WindowSource& src, int64_t t_cap, uint32_t* vc, uint16_t* vs,
                      hipStream_t stream) {
-  const int64_t tasks = static_cast<int64_t>(batch) * hkv * (n / kWindow);
+  const int64_t tasks = static_cast<int64_t>(batch) * hkv * src.windows_per_sequence();
   const dim3 grid(static_cast<unsigned>((tasks + kWaves - 1) / kWaves));
   if (bf16 && tb.rot_bf16 != nullptr)
     quantize_values_mfma_kernel<D, VB><<<grid, 256, 0, stream>>>(
-        static_cast<const uint16_t*>(v), mod, hkv, n, t0, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
+        static_cast<const uint16_t*>(v), mod, hkv, src, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
         tb.rotations_t, tb.boundaries,
         static_cast<float>(value_eps_unit<D>() * tb.rot_col_norm + 1.02 * tb.rot_lo_col_norm), vc, vs);
   else if (bf16)
-    quantize_values_kernel<D, VB, true><<<grid, 256, 0, stream>>>(v, mod, hkv, n, t0, t_cap, tasks, tb.rotations,
+    quantize_values_kernel<D, VB, true><<<grid, 256, 0, stream>>>(v, mod, hkv, src, t_cap, tasks, tb.rotations,
                                                                   tb.boundaries, vc, vs);
   else
-    quantize_values_kernel<D, VB, false><<<grid, 256, 0, stream>>>(v, mod, hkv, n, t0, t_cap, tasks, tb.rotations,
+    quantize_values_kernel<D, VB, false><<<grid, 256, 0, stream>>>(v, mod, hkv, src, t_cap, tasks, tb.rotations,
                                                                    tb.boundaries, vc, vs);
   return hipGetLastError();
 }
@@ -563,12 +561,12 @@ hipError_t launch_vb(const DeviceTables& tb, const void* v, bool bf16, const uin
 }  // namespace
 
 hipError_t launch_quantize_values(const Shape& sh, const DeviceTables& tb, const void* v, bool bf16,
-                                  const uint8_t* modality, int batch, int64_t t0, int64_t n,
+                                  const uint8_t* modality, int batch, const WindowSource& src,
                                   int64_t t_cap, uint32_t* vc, uint16_t* vs, hipStream_t stream) {
-  if (sh.d == 128 && sh.vbits == 2) return launch_vb<128, 2>(tb, v, bf16, modality, sh.hkv, batch, t0, n, t_cap, vc, vs, stream);
-  if (sh.d == 128 && sh.vbits == 4) return launch_vb<128, 4>(tb, v, bf16, modality, sh.hkv, batch, t0, n, t_cap, vc, vs, stream);
-  if (sh.d == 64 && sh.vbits == 2) return launch_vb<64, 2>(tb, v, bf16, modality, sh.hkv, batch, t0, n, t_cap, vc, vs, stream);
-  return launch_vb<64, 4>(tb, v, bf16, modality, sh.hkv, batch, t0, n, t_cap, vc, vs, stream);
+  if (sh.d == 128 && sh.vbits == 2) return launch_vb<128, 2>(tb, v, bf16, modality, sh.hkv, batch, src, t_cap, vc, vs, stream);
+  if (sh.d == 128 && sh.vbits == 4) return launch_vb<128, 4>(tb, v, bf16, modality, sh.hkv, batch, src, t_cap, vc, vs, stream);
+  if (sh.d == 64 && sh.vbits == 2) return launch_vb<64, 2>(tb, v, bf16, modality, sh.hkv, batch, src, t_cap, vc, vs, stream);
+  return launch_vb<64, 4>(tb, v, bf16, modality, sh.hkv, batch, src, t_cap, vc, vs, stream);
 }
 
 }  // namespace omnikv

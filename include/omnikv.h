@@ -289,10 +289,14 @@ omnikv_status omnikv_stream_packed_lengths(int64_t n, int64_t* key_packed, int64
  * and must agree; lens_host[b] + 1 <= t_cap.  tags_new and lens need no
  * alignment (the other device pointers do, as everywhere).  Every key group and value window
  * that the new length moves past the schedule's thresholds is then quantized
- * from the rings into the packed cache (omnikv_quantize_keys / _values on that
- * sequence's rows), all on `stream`.  The caller advances its lengths by one
- * afterwards.  Errors as for omnikv_quantize_keys; nothing is launched on an
- * argument error. */
+ * from the rings into the packed cache, with the codes omnikv_quantize_keys /
+ * _values give for those rows: one launch appends the tokens, one more launch
+ * quantizes the key groups of every sequence that crosses a 128-token threshold,
+ * and one more the value windows of every sequence whose value window moves (each
+ * made only when some sequence needs it; the kernels read each sequence's length
+ * from lens), all on `stream`, so at most three launches per call whatever the
+ * batch.  The caller advances its lengths by one afterwards.  Errors as for
+ * omnikv_quantize_keys; nothing is launched on an argument error. */
 omnikv_status omnikv_stream_append(const omnikv_ctx* ctx, const void* k_new, const void* v_new, omnikv_dtype dt,
                                    const uint8_t* tags_new, const int32_t* lens, const int64_t* lens_host,
                                    int32_t batch, void* k_ring, void* v_ring, int32_t ring_cap, uint32_t* k_codes,
