@@ -252,11 +252,16 @@ def time_decode(ctx, cfg, caches, alg, steps, warmup, replays, splits=0):
     every cached token of the batch: the split-KV kernel, then the merge of the splits with
     the batched inverse value rotation.
 
-    head: one replay of a graph of `steps` steps, bracketed by synchronizations (the headline
-    timed region: exactly `steps` steps).  spread: `replays` further replays of the same graph,
-    each timed by events; a sample is the replay's time / steps.  partial / combine: graphs
-    of `steps` launches of one kernel each (omnikv_decode_partial, omnikv_decode_combine),
-    replayed `replays` times, medians per launch."""
+    warm-up: exactly `warmup` untimed steps, as replays of the step graph (warmup // steps of
+    them, then the rest eagerly): a replay bracketed by synchronizations approaches the
+    back-to-back replay time only after ~20 ms of back-to-back work (48, 45, 44, ... 41.5 µs
+    per step over its first eight replays at config 3, against 40.6 back to back), and eager
+    steps launched from Python leave the GPU idle between launches.  head: one replay of the graph of `steps` steps, bracketed by
+    synchronizations (the headline timed region: exactly `steps` steps).  spread: `replays`
+    further replays of the same graph, each timed by events; a sample is the replay's time /
+    steps.  partial / combine: graphs of `steps` launches of one kernel each
+    (omnikv_decode_partial, omnikv_decode_combine), replayed `replays` times, medians per
+    launch."""
     import torch
     nbuf = len(caches)
     B, T, d = cfg.batch, cfg.context, cfg.head_dim
@@ -268,13 +273,15 @@ def time_decode(ctx, cfg, caches, alg, steps, warmup, replays, splits=0):
     def step(i):
         ctx.decode(q, lens, T, caches[i % nbuf], out=out, workspace=ws, num_splits=splits)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    g_step = _graph(lambda i: step(warmup + i), steps)
+    warm_replays, warm_rest = divmod(warmup, steps)
+    g_step = _graph(lambda i: step(i), steps)
     g_part = _graph(lambda i: ctx.decode_partial(q, lens, T, caches[i % nbuf], ws, num_splits=splits), steps)
     g_comb = _graph(lambda i: ctx.decode_combine(lens, B, T, ws, out, num_splits=splits), steps)
-    g_step.replay()  # untimed first replay
+    torch.cuda.synchronize()
+    for i in range(warm_rest):
+        step(i)
+    for _ in range(warm_replays):
+        g_step.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
@@ -332,7 +339,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--replays", type=int, default=30, help="timed replays of the step graph for the spread")
     ap.add_argument("--config", type=int, default=3, help="workload id (default 3: 16 x 32k, 16Q/2KV/d128)")
     ap.add_argument("--kbits", type=int, default=2)
@@ -431,7 +438,7 @@ def main():
     if not args.no_other_configs:
         others = {}
         for cid, kb, vb in ((4, 2, 2), (4, 4, 4), (5, 2, 2), (5, 4, 4)):
-            others[f"config{cid}_K{kb}V{vb}"] = decode_config(cid, kb, vb, "fp16", 10, 3, 10)
+            others[f"config{cid}_K{kb}V{vb}"] = decode_config(cid, kb, vb, "fp16", 10, 20, 10)
         cfg5 = synth.CONFIGS[5]
         ctx5 = binding.Context(cfg5.head_dim, cfg5.q_heads, cfg5.kv_heads, 2, 2, signs, U)
         others["config5_prefill_write_K2V2"] = time_write_path(ctx5, cfg5, synth.modality_layout(cfg5, 0, cfg5.prefill),
