@@ -549,6 +549,8 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   __shared__ __attribute__((aligned(16))) float q_lds[kMaxGroup][D];
   __shared__ float zmax_lds[kMaxGroup];
   __shared__ uint32_t vtab[1 << (2 * VB)];
+  // 2-bit values: the level quads of a code byte (its low and high nibbles' level pairs)
+  __shared__ __attribute__((aligned(8))) uint2 vquad[VB == 2 ? 256 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -768,6 +770,10 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     tv[2][x] = hq;
     tv[3][x] = static_cast<_Float16>(qh - static_cast<float>(hq));
   }
+  if constexpr (VB == 2) {
+    static_assert(kWaves * 64 == 256, "one quad per thread");
+    vquad[tid] = make_uint2(vtab[tid & 15], vtab[tid >> 4]);
+  }
   __syncthreads();  // q_lds and every staging slot have been read
   _Float16* const tab_t = reinterpret_cast<_Float16*>(&q_lds[0][0]);  // [th | tl][head][D]
   _Float16* const tab_qh = reinterpret_cast<_Float16*>(ring_mem + (0 * RING + RING - 1) * SG::BYTES);
@@ -886,12 +892,12 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   };
 
   // ---- the value contraction's A operands of the window in `slot` (fp16 levels, channel
-  // tile u: row = channel, the lane's 8 tokens), built from the value block and the
-  // level-pair table; the same for every accumulator.  Built right after the score
-  // contractions are issued, their table reads overlap those contractions.
+  // tile u: row = channel, the lane's 8 tokens), built from the value block and the level
+  // tables; the same for every accumulator.  Built right after the score contractions are
+  // issued, their table reads overlap those contractions.  Dwords 2 h, 2 h + 1 of tile u
+  // are the level pairs of the low and high nibble of byte 2 (u & 1) + h of word u / 2:
+  // 2-bit values read both with one 8-byte load of that byte's quad.
   auto value_operands = [&](const uint8_t* slot, uint4_t (&av)[NU]) {
-    // Byte offsets of the pair-table entries: 2-bit values take four offsets per dword at
-    // once (low nibbles of the bytes, then high nibbles).
     uint32_t vw[VW];
 #pragma unroll
     for (int x = 0; x < VW / 4; ++x) {
@@ -902,29 +908,25 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       const uint2 t = *reinterpret_cast<const uint2*>(slot + SG::OFF_V + 8 * lane);
       vw[0] = t.x; vw[1] = t.y;
     }
-    uint32_t vx[VW], vy[VW];
     if constexpr (VB == 2) {
 #pragma unroll
-      for (int x = 0; x < VW; ++x) {
-        vx[x] = (vw[x] << 2) & 0x3C3C3C3Cu;
-        vy[x] = (vw[x] >> 2) & 0x3C3C3C3Cu;
-      }
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint32_t byte = (vw[u / 2] >> (8 * (2 * (u & 1) + h2))) & 0xFFu;
+          const uint2 e = vquad[byte];
+          av[u][2 * h2] = e.x;
+          av[u][2 * h2 + 1] = e.y;
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pp = 4 * u + i;
+          av[u][i] = vtab[(vw[pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
+        }
     }
-    auto entry = [&](int pp) -> uint32_t {
-      if constexpr (VB == 2) {
-        const uint32_t src = (pp & 1) ? vy[pp / 8] : vx[pp / 8];
-        const int byte = (pp % 8) / 2;
-        // one byte-select per offset (v_perm_b32: byte `byte` of src, upper bytes zero)
-        const uint32_t off = __builtin_amdgcn_perm(0u, src, 0x0C0C0C00u | static_cast<uint32_t>(byte));
-        return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(vtab) + off);
-      } else {
-        return vtab[(vw[pp / PPW] >> (2 * VB * (pp % PPW))) & PMASK];
-      }
-    };
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[u][i] = entry(4 * u + i);
   };
 
   // ---- the rest of one visit of a window, given its score contractions.  Tokens count
