@@ -61,6 +61,7 @@ typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 // both fp16 parts are normal numbers and the pair keeps ~22 bits.
 constexpr float kXMax = 15.0f;
 constexpr float kXAfter = 7.0f;
+constexpr uint32_t kHiLimitBits = 0x7800u;  // fp16 2^15 (= 2^kXMax)
 typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
 
 // Biased exponent field e of the largest of a lane's eight fp16 value scales (two per word):
@@ -141,6 +142,24 @@ __device__ __forceinline__ uint32_t mix_pair(float p0, float p1, uint32_t s, uin
       : "=&v"(d)
       : "v"(p0), "v"(s), "v"(c), "v"(p1));
   return d;
+}
+
+// The same for the four dwords of a lane's eight probabilities (dword q: p[2q], p[2q + 1]
+// with the halves of s[q] and c[q]), in one block with one wait state.
+__device__ __forceinline__ void mix_quad(const float (&p)[8], const uint32_t (&s)[4], const uint32_t (&c)[4],
+                                         uint32_t (&d)[4]) {
+  asm("s_nop 0\n\t"
+      "v_fma_mixlo_f16 %0, %4, %12, -%16 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %0, %5, %12, -%16 op_sel:[0,1,1] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixlo_f16 %1, %6, %13, -%17 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %1, %7, %13, -%17 op_sel:[0,1,1] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixlo_f16 %2, %8, %14, -%18 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %2, %9, %14, -%18 op_sel:[0,1,1] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixlo_f16 %3, %10, %15, -%19 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %3, %11, %15, -%19 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]),
+        "v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]), "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
 }
 
 template <int D>
@@ -246,49 +265,40 @@ struct Slot {
 // the compiler's wait insertion does not see it: it cannot tell ring slots apart and would
 // drain every copy in flight before each slot read.  The copy writes no VGPR; its only
 // consumers are the slot reads that follow an explicit wait_vmcnt.
-// M0 (which the copy reads at issue for its LDS base) is saved and restored inside the
-// asm, so the compiler's view of M0 is unchanged.
+// The copy takes its LDS base from M0, which the asm sets and declares clobbered (the
+// compiler re-establishes M0 itself wherever it relies on it).
 __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %0, off"
+      :
       : "v"(src), "s"(lds_addr)
-      : "memory");
+      : "memory", "m0");
 }
 
 // The same copy from a wave-uniform 64-bit base plus a 32-bit per-lane byte offset (the
 // scalar-base form of the global address), which keeps the address math in 32 bits.
 __device__ __forceinline__ void copy16_to_lds_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(voff), "s"(sbase), "s"(lds_addr)
-      : "memory");
+      : "memory", "m0");
 }
 
 // One 4-byte global->LDS copy per active lane (lane l writes lds_addr + 4 l); the same
 // M0 handling as above.
 __device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dword %0, off"
+      :
       : "v"(src), "s"(lds_addr)
-      : "memory");
+      : "memory", "m0");
 }
 
 template <int N>
@@ -545,7 +555,6 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   // areas, and a static LDS array that no visible code stores to would let the optimizer
   // treat its contents as undefined and fold the reads.
   extern __shared__ __attribute__((aligned(16))) uint8_t ring_mem[];
-  auto ring_slot = [&](int wv, int slot) -> uint8_t* { return ring_mem + (wv * RING + slot) * SG::BYTES; };
   __shared__ __attribute__((aligned(16))) float q_lds[kMaxGroup][D];
   __shared__ float zmax_lds[kMaxGroup];
   __shared__ uint32_t vtab[1 << (2 * VB)];
@@ -979,17 +988,35 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       // without one (tags out of range) is skipped, which keeps the column max finite
       if (!__any(any_counted)) return;
     }
-    float lmax = -INFINITY;
+    // ---- probabilities and the range of p sigma.  p sigma enters the value contraction as
+    // fp16 hi and lo parts; the reference moves when a lane's largest hi part passes 2^kXMax
+    // (or is not finite: as fp16 bit patterns of values >= 0 order like integers), and the
+    // window's probabilities are then recomputed.  The first visit sets the reference.
+    float p[8];
+    uint32_t bhi[4], blo[4];
+    const uint32_t zero4[4] = {0u, 0u, 0u, 0u};
+    auto probabilities = [&]() {
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+      for (int k = 0; k < 8; ++k) p[k] = exp2_raw(sc[k >> 2][k & 3]);
+      mix_quad(p, sgw, zero4, bhi);
+    };
+    bool big = fresh;
+    if (!fresh) {
+      probabilities();
+      const ushort2_t a = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, bhi[0]), __builtin_bit_cast(ushort2_t, bhi[1]));
+      const ushort2_t b2 = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, bhi[2]), __builtin_bit_cast(ushort2_t, bhi[3]));
+      const ushort2_t c2 = __builtin_elementwise_max(a, b2);
+      big = max(static_cast<uint32_t>(c2.x), static_cast<uint32_t>(c2.y)) > kHiLimitBits;
+    }
+    if (__any(big)) {
+      // log2(p sigma) + 14 < lx for every token of the lane (uncounted tokens' scales are
+      // zero); every visit has a counted token, so the column max is finite
+      float lmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, sc[tau][i]);
-    // log2(p sigma) + 14 < lx for every token of the lane (uncounted tokens' scales are zero)
-    const float lx = lmax + scale_exponent_field(sgw);
-    // The reference only has to move when that bound exceeds 2^kXMax; the column-wide max
-    // (a cross-lane reduction) is needed only then.
-    if (__any(fresh || lx > kXMax + 14.0f)) {
-      // every visit has a counted token, so the column max is finite
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, sc[tau][i]);
+      const float lx = lmax + scale_exponent_field(sgw);
       const float wmax = group_max(lx);
       const bool grow = fresh || wmax > kXMax + 14.0f;
       const float delta = grow ? wmax - (kXAfter + 14.0f) : 0.0f;
@@ -1006,19 +1033,11 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[tau][i] -= delta;
+      probabilities();
     }
-    // ---- probabilities times the value scale, as fp16 hi and lo = fp16(p sigma - hi)
-    uint32_t bhi[4], blo[4];
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int tau = qd >> 1;
-      const float p0 = exp2_raw(sc[tau][2 * (qd & 1)]);
-      const float p1 = exp2_raw(sc[tau][2 * (qd & 1) + 1]);
-      l_part += p0;
-      l_part += p1;
-      bhi[qd] = mix_pair(p0, p1, sgw[qd], 0u);
-      blo[qd] = mix_pair(p0, p1, sgw[qd], bhi[qd]);
-    }
+    for (int k = 0; k < 8; ++k) l_part += p[k];
+    mix_quad(p, sgw, bhi, blo);
     // ---- value contractions, one channel tile at a time (operands built before the visit)
     // the operand of one accumulator keeps, in each lane, the tokens of its column's
     // modality (dword qd holds tokens 2 (qd & 1), + 1 of byte group qd >> 1)
@@ -1089,6 +1108,10 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
   int stage = 0, next_change = q1;
   uint32_t cur = 0;  // ring offset of visit i's slot
   __builtin_amdgcn_s_setprio(3);
+  // Visits 0 .. nw - RING each issue the copies of the window RING - 1 ahead (the ring
+  // holds RING - 1 windows in flight, as issued before the set-up) and wait with a fixed
+  // count; the last RING - 1 visits issue nothing and wait for fewer groups.
+  const int nsteady = nw - (RING - 1);
   for (int i = 0; i < nw; ++i) {
     if (i == next_change) {
       do {
@@ -1099,9 +1122,13 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       else if (stage == 2) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
     }
-    issue_upto(min(nw, i + RING));
-    // wait for this visit's copies: later visits' copies may stay in flight
-    wait_groups<L, RING - 1>(issued - (i + 1));
+    if (i < nsteady) {
+      issue(wbeg + i + RING - 1);
+      wait_vmcnt<(RING - 1) * L>();
+    } else {
+      // wait for this visit's copies: later visits' copies may stay in flight
+      wait_groups<L, RING - 1>(issued + max(nsteady, 0) - (i + 1));
+    }
     uint8_t* slot = ring_mem + wave * RING * SG::BYTES + cur;
     cur = next_slot(cur);
     if constexpr (MX) mx_expand(slot);
