@@ -952,8 +952,11 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     // holds tokens 0 .. 3 in tg0, so its low byte is token 0's tag.
     const uint32_t t00 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tg0))) & 0xFFu;
     const uint32_t rep = t00 * 0x01010101u;
-    const bool uniform = t00 < static_cast<uint32_t>(kMaxModalities) && (tokb + kWindow <= len) &&
-                         __all((tg0 == rep) && (tg1 == rep));
+    const bool full = tokb + kWindow <= len;
+    const bool uniform = t00 < static_cast<uint32_t>(kMaxModalities) && full && __all((tg0 == rep) && (tg1 == rep));
+    // the next most common case: a window inside the sequence whose tags are all below 3
+    // (several modalities, every token counts), which needs no masking
+    bool clean = uniform;
     // ---- scores relative to m_ref (the first visit of a wave takes absolute scores)
     const bool fresh = m_ref == -INFINITY;
     const float aw = (cm[0] + row_ror8(cm[0])) * zh;
@@ -964,6 +967,11 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[tau][i] = fmaf(cs[tau][i] + row_ror8(cs[tau][i]), zfac, base);
     if (!uniform) {
+      static_assert(kMaxModalities == 3, "tags 0, 1, 2 are the bit patterns 00, 01, 10 of a byte");
+      const uint32_t three = (tg0 & (tg0 >> 1)) | (tg1 & (tg1 >> 1));  // bit 0 of a byte: both bits set
+      clean = full && __all(((tg0 | tg1) & 0xFCFCFCFCu) == 0u && (three & 0x01010101u) == 0u);
+    }
+    if (!clean) {
       // a real branch: the masking is rare, keep it off the common path
       asm volatile("" ::: "memory");
       bool any_counted = false;
@@ -1070,6 +1078,16 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       needA = t00 != 0u;
       needB = t00 == 0u;
       seen |= 1u << t00;
+    } else if (clean) {
+      // audio and video show as a set bit 0 or 1 in some byte, text as a byte with neither
+      // (bit 0 of each byte of y: the byte is not zero)
+      const uint32_t o = tg0 | tg1;
+      const uint32_t y = (tg0 | (tg0 >> 1)) & (tg1 | (tg1 >> 1));
+      const bool a0 = (y & 0x01010101u) != 0x01010101u;
+      const bool a1 = __any((o & 0x01010101u) != 0u), a2 = __any((o & 0x02020202u) != 0u);
+      needA = a1 || a2;
+      needB = __any(a0);
+      seen |= (needB ? 1u : 0u) | (a1 ? 2u : 0u) | (a2 ? 4u : 0u);
     } else {
       bool a12 = false, a0 = false, a1 = false, a2 = false;
 #pragma unroll
