@@ -125,6 +125,44 @@ __device__ __forceinline__ float group_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// value of lane l ^ (1 << K) within each 16-lane row (K = 0 .. 3), by DPP moves; each
+// move reads a valid source lane for every lane it writes
+template <int K>
+__device__ __forceinline__ float lane_xor_row(float x) {
+  const int v = __builtin_bit_cast(int, x);
+  if constexpr (K == 0) {  // quad_perm [1, 0, 3, 2]
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (K == 1) {  // quad_perm [2, 3, 0, 1]
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (K == 2) {
+    // lanes 0-3 and 8-11 of a row read lane + 4 (row_shl:4), lanes 4-7 and 12-15 lane - 4
+    // (row_shr:4); the bank mask picks which lanes each move writes
+    const int lo = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0x5, false);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(lo, v, 0x114, 0xF, 0xA, false));
+  } else {  // row_ror:8
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
+  }
+}
+
+// One radix-2 stage of the Walsh-Hadamard transform across the lanes of a wave, partner
+// lane l ^ ST: the lane with that bit clear takes own + partner, the other partner - own.
+template <int ST>
+__device__ __forceinline__ float wht_lane_stage(float z, int lane) {
+  if constexpr (ST < 16) {
+    constexpr int K = ST == 1 ? 0 : (ST == 2 ? 1 : (ST == 4 ? 2 : 3));
+    const float p = lane_xor_row<K>(z);
+    return (lane & ST) ? p - z : z + p;
+  } else {
+    static_assert(ST == 16 || ST == 32, "lane stages");
+    uint32_t a = __builtin_bit_cast(uint32_t, z), b = a;
+    if constexpr (ST == 16) swap16(a, b);
+    else swap32(a, b);
+    // a: the value of the lane with the bit clear, b: of the lane with it set
+    const float fa = __builtin_bit_cast(float, a), fb = __builtin_bit_cast(float, b);
+    return (lane & ST) ? fa - fb : fa + fb;
+  }
+}
+
 // 2^x by the hardware instruction (results below 2^-126 flush to zero; the softmax
 // weights it produces are relative to a running max, so those are negligible)
 __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -698,34 +736,46 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     }
   }
 
-  // ---- query rotation q' = c_d H D q (two heads per wave), scaled to log2 units
+  // ---- query rotation q' = c_d H D q (two heads per wave), scaled to log2 units.  The
+  // butterflies across lanes are DPP moves and lane swaps (register to register), both
+  // heads' stages side by side.
+  float z[2][NC];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) z[j][c] = qv[j][c];
+  auto wht_stage = [&](auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) z[j][c] = wht_lane_stage<ST>(z[j][c], lane);
+  };
+  wht_stage(std::integral_constant<int, 1>{});
+  wht_stage(std::integral_constant<int, 2>{});
+  wht_stage(std::integral_constant<int, 4>{});
+  wht_stage(std::integral_constant<int, 8>{});
+  wht_stage(std::integral_constant<int, 16>{});
+  wht_stage(std::integral_constant<int, 32>{});
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    float z[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) z[c] = qv[j][c];
-#pragma unroll
-    for (int st = 1; st < 64; st <<= 1) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float p = __shfl_xor(z[c], st, 64);
-        z[c] = (lane & st) ? (p - z[c]) : (z[c] + p);
-      }
-    }
     if constexpr (NC == 2) {
-      const float x0 = z[0] + z[1], x1 = z[0] - z[1];
-      z[0] = x0;
-      z[1] = x1;
+      const float x0 = z[j][0] + z[j][1], x1 = z[j][0] - z[j][1];
+      z[j][0] = x0;
+      z[j][1] = x1;
     }
     float am = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      z[c] = z[c] * RhtConst<D>::value * a.scale_log2;
-      q_lds[h0 + j][lane + 64 * c] = z[c];
-      am = fmaxf(am, fabsf(z[c]));
+      z[j][c] = z[j][c] * RhtConst<D>::value * a.scale_log2;
+      q_lds[h0 + j][lane + 64 * c] = z[j][c];
+      am = fmaxf(am, fabsf(z[j][c]));
     }
-#pragma unroll
-    for (int st = 32; st >= 1; st >>= 1) am = fmaxf(am, __shfl_xor(am, st, 64));
+    am = fmaxf(am, lane_xor_row<0>(am));
+    am = fmaxf(am, lane_xor_row<1>(am));
+    am = fmaxf(am, lane_xor_row<2>(am));
+    am = fmaxf(am, lane_xor_row<3>(am));
+    am = group_max(am);
     if (lane == 0) zmax_lds[h0 + j] = am;
   }
   __syncthreads();
@@ -1330,8 +1380,11 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
     const float2 ml = a.ws_ml[(base + s) * kMaxGroup + h];
     if (ml.y > 0.0f) mx = fmaxf(mx, ml.x);
   }
-#pragma unroll
-  for (int st = 32; st >= 1; st >>= 1) mx = fmaxf(mx, __shfl_xor(mx, st, 64));
+  mx = group_max(mx);
+  mx = fmaxf(mx, lane_xor_row<3>(mx));
+  mx = fmaxf(mx, lane_xor_row<2>(mx));
+  mx = fmaxf(mx, lane_xor_row<1>(mx));
+  mx = fmaxf(mx, lane_xor_row<0>(mx));
   mx = fmaxf(mx, tmx);
 
   // ---- (1) merge, 64 splits at a time: lane t holds split s0 + t's weight and mask.  A
@@ -1390,8 +1443,12 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(Combine
       merge_rest(s0, w, mk, s0);
     }
   }
-#pragma unroll
-  for (int st = 32; st >= 1; st >>= 1) lsum += __shfl_xor(lsum, st, 64);
+  // lanes l ^ 32, l ^ 16, then l ^ 8 .. l ^ 1 (register-to-register moves)
+  lsum = group_sum(lsum);
+  lsum += lane_xor_row<3>(lsum);
+  lsum += lane_xor_row<2>(lsum);
+  lsum += lane_xor_row<1>(lsum);
+  lsum += lane_xor_row<0>(lsum);
   if (tid < J) A[tid] = merger ? acc : 0.0f;
   // ---- streamed sequences: probabilities of the recent tokens and their values, which
   // are in the original space (added after the inverse rotation)
