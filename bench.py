@@ -235,10 +235,12 @@ def time_stream_append(ctx, cfg, cache, rings, n0, steps=128, reps=10):
     us = [ms * 1e3 / steps for ms in _replay_ms(graph, reps)]
     del graph
     kp = [binding.Context.stream_packed_lengths(n0 + i) for i in range(steps + 1)]
+    # a call launches at most one key flush and one value flush, whatever the batch; these count
+    # the calls (of `tokens`) that did
     key_flushes = sum(kp[i + 1][0] > kp[i][0] for i in range(steps))
     value_flushes = sum(kp[i + 1][1] > kp[i][1] for i in range(steps))
     return {"append_us": _spread(us), "tokens": steps, "from_length": n0, "batch": B,
-            "key_flush_launches": int(key_flushes), "value_flush_launches": int(value_flushes)}
+            "calls_with_key_flush": int(key_flushes), "calls_with_value_flush": int(value_flushes)}
 
 
 def _spread(us):
