@@ -77,6 +77,47 @@ __device__ __forceinline__ uint32_t row_shl(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x100 + N, 0xF, 0xF, false));
 }
 
+// Lane labels of the key rotation.  A token's 128 (64) channels sit 8 per lane on LPT = 16 (8)
+// lanes; lane l of the token's row holds channel group q = a + 2b + 4c + 8d, where
+// l = a ^ 2b ^ 7c ^ 8d (c, d: bits 2, 3 of l; a, b: bits 0, 1 of l, each xor c).  Flipping
+// group bit 0, 1, 2 or 3 is then lane l ^ 1, l ^ 2, l ^ 7 or l ^ 8: quad_perm, quad_perm,
+// row_half_mirror and row_ror:8, one DPP pattern each, so every butterfly stage across
+// lanes is one fused multiply-add with a DPP source.  A 32-channel block (group bits c, d
+// fixed) still fills one quad of lanes.
+__device__ __forceinline__ int channel_group(int l) {
+  const int c = (l >> 2) & 1, d = (l >> 3) & 1;
+  const int a = (l & 1) ^ c, b = ((l >> 1) & 1) ^ c;
+  return a + 2 * b + 4 * c + 8 * d;
+}
+
+// One butterfly stage over a lane's eight values: z[e] += sgn * (z[e] of the lane whose
+// channel group differs in bit K), one v_fmac_f32 with a DPP source each.  Written in asm:
+// the compiler does not fold a DPP move into fmac.  The leading wait states cover a value
+// written by the instruction just before the block (a DPP source needs two); inside the
+// block each source was written at least eight instructions earlier.
+#define OMNIKV_FMAC8(pat)                                                                   \
+  "s_nop 1\n\t"                                                                             \
+  "v_fmac_f32_dpp %0, %0, %8 " pat " row_mask:0xf bank_mask:0xf\n\t"                        \
+  "v_fmac_f32_dpp %1, %1, %8 " pat " row_mask:0xf bank_mask:0xf\n\t"                        \
+  "v_fmac_f32_dpp %2, %2, %8 " pat " row_mask:0xf bank_mask:0xf\n\t"                        \
+  "v_fmac_f32_dpp %3, %3, %8 " pat " row_mask:0xf bank_mask:0xf\n\t"                        \
+  "v_fmac_f32_dpp %4, %4, %8 " pat " row_mask:0xf bank_mask:0xf\n\t"                        \
+  "v_fmac_f32_dpp %5, %5, %8 " pat " row_mask:0xf bank_mask:0xf\n\t"                        \
+  "v_fmac_f32_dpp %6, %6, %8 " pat " row_mask:0xf bank_mask:0xf\n\t"                        \
+  "v_fmac_f32_dpp %7, %7, %8 " pat " row_mask:0xf bank_mask:0xf"
+template <int K>
+__device__ __forceinline__ void group_stage(float (&z)[8], float sgn) {
+#define OMNIKV_FMAC8_OPS                                                                     \
+  : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]), "+v"(z[4]), "+v"(z[5]), "+v"(z[6]), "+v"(z[7]) \
+  : "v"(sgn)
+  if constexpr (K == 0) asm(OMNIKV_FMAC8("quad_perm:[1,0,3,2]") OMNIKV_FMAC8_OPS);
+  else if constexpr (K == 1) asm(OMNIKV_FMAC8("quad_perm:[2,3,0,1]") OMNIKV_FMAC8_OPS);
+  else if constexpr (K == 2) asm(OMNIKV_FMAC8("row_half_mirror") OMNIKV_FMAC8_OPS);
+  else asm(OMNIKV_FMAC8("row_ror:8") OMNIKV_FMAC8_OPS);
+#undef OMNIKV_FMAC8_OPS
+}
+#undef OMNIKV_FMAC8
+
 // value of lane l ^ (1 << k) within each 16-lane row (k = 0 .. 3).  Each move reads a
 // valid source lane for every lane it writes, so no lane needs a prior value (no zero fill
 // or copy before the move).
@@ -122,7 +163,7 @@ __device__ __forceinline__ uint32_t mx_encode(float x, float inv, int e, float& 
 }
 
 template <int D, int KB, bool BF16, bool MX>
-__global__ __launch_bounds__(256) void quantize_keys_kernel(
+__global__ __launch_bounds__(256, 4) void quantize_keys_kernel(
     const void* __restrict__ k, int hkv, WindowSource src, int64_t nwin_cap,
     int64_t tasks, const float* __restrict__ signs, uint32_t* __restrict__ k_codes,
     uint16_t* __restrict__ k_min, uint16_t* __restrict__ k_scale) {
@@ -144,8 +185,11 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
   const int64_t b = wt.b;
   const int h = wt.h;
   const size_t blk = (static_cast<size_t>(b) * hkv + h) * nwin_cap + wt.tok0 / kWindow;
-  const int q = lane % LPT, r = lane / LPT;  // channels 8q .. 8q + 7 of token TPI * pass + r
+  // channels 8q .. 8q + 7 of token TPI * pass + r (q: the lane's channel group)
+  const int q = channel_group(lane % LPT), r = lane / LPT;
 
+  // c_d times the sign the cross stages leave on this lane's values
+  const float rht_lane = (__builtin_popcount(q & ((1 << XS) - 1)) & 1) ? -RhtConst<D>::value : RhtConst<D>::value;
   if (active) {
     float sg[8];
 #pragma unroll
@@ -186,13 +230,15 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
           z[e + hh] = a0 - b0;
         }
       }
-      // stages h = 8 << kk across lanes q ^ (1 << kk): the lower lane keeps own + partner,
-      // the upper gets partner - own, both one rounding of the exact sum (fma by +-1)
+      // stages h = 8 << kk across the lanes whose groups differ in bit kk.  Every lane
+      // computes own + sgn * partner (one rounding), sgn = -1 where group bit kk is set: the
+      // lower lane gets a + b, the upper b - a = -(a - b).  The stored value is therefore the
+      // butterfly's result times (-1)^(bits set among those stages), a sign of the lane that
+      // the final scale takes back (rounding is symmetric, so the values are those of the
+      // plain butterflies).
       auto cross = [&](auto kk_c) {
         constexpr int kk = decltype(kk_c)::value;
-        const float sgn = ((q >> kk) & 1) ? -1.0f : 1.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = __builtin_fmaf(z[e], sgn, row_xor<kk>(z[e]));
+        group_stage<kk>(z, ((q >> kk) & 1) ? -1.0f : 1.0f);
       };
       cross(std::integral_constant<int, 0>{});
       cross(std::integral_constant<int, 1>{});
@@ -200,7 +246,7 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
       if constexpr (XS == 4) cross(std::integral_constant<int, 3>{});
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float yy = z[e] * RhtConst<D>::value;
+        const float yy = z[e] * rht_lane;
         y[pp][e] = yy;
         mn[e] = fminf(mn[e], yy);
         mx[e] = fmaxf(mx[e], yy);
