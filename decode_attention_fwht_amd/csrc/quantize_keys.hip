@@ -194,6 +194,11 @@ __global__ __launch_bounds__(256, 4) void quantize_keys_kernel(
     float sg[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sg[e] = signs[8 * q + e];
+    // bf16 input: the signs flip the sign bits of each raw word (both halves at once)
+    uint32_t sx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sx[i] = (sg[2 * i] < 0.0f ? 0x00008000u : 0u) | (sg[2 * i + 1] < 0.0f ? 0x80000000u : 0u);
     float y[NP][8];
     float mn[8], mx[8];
 #pragma unroll
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(256, 4) void quantize_keys_kernel(
       float z[8];
       if constexpr (BF16) {
         const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + row);
-        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t wds[4] = {raw.x ^ sx[0], raw.y ^ sx[1], raw.z ^ sx[2], raw.w ^ sx[3]};
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = __uint_as_float((e & 1) ? (wds[e >> 1] & 0xFFFF0000u) : (wds[e >> 1] << 16));
       } else {
@@ -216,9 +221,9 @@ __global__ __launch_bounds__(256, 4) void quantize_keys_kernel(
         const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(k) + row + 4);
         z[0] = f0.x; z[1] = f0.y; z[2] = f0.z; z[3] = f0.w;
         z[4] = f1.x; z[5] = f1.y; z[6] = f1.z; z[7] = f1.w;
-      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = z[e] * sg[e];
+        for (int e = 0; e < 8; ++e) z[e] = z[e] * sg[e];
+      }
       // stages h = 1, 2, 4 inside the lane: lower index keeps a + b, upper gets a - b
 #pragma unroll
       for (int hh = 1; hh < 8; hh <<= 1) {
@@ -345,12 +350,16 @@ __global__ __launch_bounds__(256, 4) void quantize_keys_kernel(
       uint32_t cw[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        int code = 0;
         if constexpr (KB == 2) {
-#pragma unroll
-          for (int j = 0; j < L; ++j) code += (y[pp][e] >= th[e][j]) ? 1 : 0;
+          // the thresholds rise with j: the high bit is y >= theta_1, the low bit y >= theta_2
+          // or y >= theta_0 after it (the same count, two compares); both bits go straight to
+          // their byte
+          const bool hi = y[pp][e] >= th[e][1];
+          const bool lo = y[pp][e] >= (hi ? th[e][2] : th[e][0]);
+          cw[e >> 2] |= (hi ? (2u << (8 * (e & 3))) : 0u) | (lo ? (1u << (8 * (e & 3))) : 0u);
         } else {
           // invariant: y >= theta_j for every j < code
+          int code = 0;
 #pragma unroll
           for (int stp = 8; stp >= 1; stp >>= 1) {
             const int j = code + stp - 1;  // candidate: is y >= theta_j ?
@@ -359,8 +368,8 @@ __global__ __launch_bounds__(256, 4) void quantize_keys_kernel(
               code = (y[pp][e] >= thj) ? code + stp : code;
             }
           }
+          cw[e >> 2] |= static_cast<uint32_t>(code) << (8 * (e & 3));
         }
-        cw[e >> 2] |= static_cast<uint32_t>(code) << (8 * (e & 3));
       }
       *reinterpret_cast<uint2*>(&codes_lds[wave][TPI * pp + r][8 * q]) = make_uint2(cw[0], cw[1]);
     }
