@@ -269,6 +269,7 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
         lo_norm = std::max(lo_norm, std::sqrt(s2));
       }
   ctx->tb.rot_lo_col_norm = static_cast<float>(lo_norm * (1.0 + 1e-6));
+  ctx->tb.value_sym2 = nl == 4 && bnd[1] == 0.0f && bnd[0] == -bnd[2];
 
   omnikv_status st;
   if ((st = upload(&ctx->tb.signs, sg.data(), sg.size())) != OMNIKV_OK ||

@@ -33,6 +33,9 @@ struct DeviceTables {
   // host value: the same for the third bf16 part alone (the part the value quantizer's
   // matrix-core pass leaves out), rounded up
   float rot_lo_col_norm = 0.0f;
+  // host value: 2-bit values whose boundaries are (-b, 0, b) exactly (the built-in Gaussian
+  // codebook is symmetric); the value quantizer then classifies by sign and magnitude
+  bool value_sym2 = false;
 };
 
 // Streaming schedule ([paper] §3.1 Implementation details, captioning): after n

@@ -226,7 +226,7 @@ typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kNearList = 1024;  // near-threshold elements per block shared out by the block
 
-template <int D, int VB>
+template <int D, int VB, bool SYM>
 __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
     const uint16_t* __restrict__ v, const uint8_t* __restrict__ modality, int hkv, WindowSource src,
     int64_t t_cap, int64_t tasks, const uint4_t* __restrict__ rot_b16,
@@ -385,29 +385,43 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float x = acc[tt][i];
-          uint32_t code;
-          bool near;
-          if constexpr (kTwoBit) {
-            // the thresholds rise (finite scale), so the three comparisons form a
-            // thermometer: code = c0 + c1 + c2 has high bit c1 and low bit c0 ^ c1 ^ c2
-            const bool c0 = x >= th[tt][i][0], c1 = x >= th[tt][i][1], c2 = x >= th[tt][i][2];
-            code = (c1 ? 2u : 0u) | ((c0 ^ c1 ^ c2) ? 1u : 0u);
-            // a NaN distance (NaN sum) stays NaN through the min and counts as near
-            const float dmin = fminf(fminf(fabsf(x - th[tt][i][0]), fabsf(x - th[tt][i][1])), fabsf(x - th[tt][i][2]));
-            near = !(dmin > my_ep[tt][i]);
-          } else {
-            code = 0u;
-            near = false;
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-              const float thj = my_sg[tt][i] * beta[j];
-              code += (x >= thj) ? 1u : 0u;
-              near = near || !(fabsf(x - thj) > my_ep[tt][i]);  // NaN or infinite sums count
-            }
-          }
           const bool mine = !mixed || my_tag[tt][i] == m;
-          bits |= (mine ? code : 0u) << (VB * (4 * tt + i));
-          nearm |= (near && mine ? 1u : 0u) << (4 * tt + i);
+          const int sh = VB * (4 * tt + i);
+          if constexpr (kTwoBit && SYM) {
+            // boundaries (-b, 0, b): away from them (the only results this code decides:
+            // near ones take the sequential definition) the high bit is x >= 0 and the low
+            // bit |x| >= sigma b, flipped for x < 0.  Near: within eps of 0 or of +-sigma b
+            // (the two candidates for the nearest boundary); a NaN result counts.
+            const float tb = th[tt][i][2], ax = fabsf(x);
+            const bool pos = x >= 0.0f, outer = ax >= tb;
+            const bool near0 = !(ax > my_ep[tt][i]), near1 = !(fabsf(ax - tb) > my_ep[tt][i]);
+            const bool near = near0 | near1;  // both evaluated: no branch
+            bits |= (mine && pos ? (2u << sh) : 0u) | (mine && outer == pos ? (1u << sh) : 0u);
+            nearm |= (near && mine ? 1u : 0u) << (4 * tt + i);
+          } else {
+            uint32_t code;
+            bool near;
+            if constexpr (kTwoBit) {
+              // the thresholds rise (finite scale), so the three comparisons form a
+              // thermometer: code = c0 + c1 + c2 has high bit c1 and low bit c0 ^ c1 ^ c2
+              const bool c0 = x >= th[tt][i][0], c1 = x >= th[tt][i][1], c2 = x >= th[tt][i][2];
+              code = (c1 ? 2u : 0u) | ((c0 ^ c1 ^ c2) ? 1u : 0u);
+              // a NaN distance (NaN sum) stays NaN through the min and counts as near
+              const float dmin = fminf(fminf(fabsf(x - th[tt][i][0]), fabsf(x - th[tt][i][1])), fabsf(x - th[tt][i][2]));
+              near = !(dmin > my_ep[tt][i]);
+            } else {
+              code = 0u;
+              near = false;
+#pragma unroll
+              for (int j = 0; j < NB; ++j) {
+                const float thj = my_sg[tt][i] * beta[j];
+                code += (x >= thj) ? 1u : 0u;
+                near = near || !(fabsf(x - thj) > my_ep[tt][i]);  // NaN or infinite sums count
+              }
+            }
+            bits |= (mine ? code : 0u) << sh;
+            nearm |= (near && mine ? 1u : 0u) << (4 * tt + i);
+          }
         }
     };
 #pragma unroll
@@ -544,17 +558,26 @@ hipError_t launch_vb(const DeviceTables& tb, const void* v, bool bf16, const uin
                      hipStream_t stream) {
   const int64_t tasks = static_cast<int64_t>(batch) * hkv * src.windows_per_sequence();
   const dim3 grid(static_cast<unsigned>((tasks + kWaves - 1) / kWaves));
-  if (bf16 && tb.rot_bf16 != nullptr)
-    quantize_values_mfma_kernel<D, VB><<<grid, 256, 0, stream>>>(
+  const float eps = static_cast<float>(value_eps_unit<D>() * tb.rot_col_norm + 1.02 * tb.rot_lo_col_norm);
+  if (bf16 && tb.rot_bf16 != nullptr) {
+    if constexpr (VB == 2) {
+      if (tb.value_sym2) {
+        quantize_values_mfma_kernel<D, VB, true><<<grid, 256, 0, stream>>>(
+            static_cast<const uint16_t*>(v), mod, hkv, src, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
+            tb.rotations_t, tb.boundaries, eps, vc, vs);
+        return hipGetLastError();
+      }
+    }
+    quantize_values_mfma_kernel<D, VB, false><<<grid, 256, 0, stream>>>(
         static_cast<const uint16_t*>(v), mod, hkv, src, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
-        tb.rotations_t, tb.boundaries,
-        static_cast<float>(value_eps_unit<D>() * tb.rot_col_norm + 1.02 * tb.rot_lo_col_norm), vc, vs);
-  else if (bf16)
+        tb.rotations_t, tb.boundaries, eps, vc, vs);
+  } else if (bf16) {
     quantize_values_kernel<D, VB, true><<<grid, 256, 0, stream>>>(v, mod, hkv, src, t_cap, tasks, tb.rotations,
                                                                   tb.boundaries, vc, vs);
-  else
+  } else {
     quantize_values_kernel<D, VB, false><<<grid, 256, 0, stream>>>(v, mod, hkv, src, t_cap, tasks, tb.rotations,
                                                                    tb.boundaries, vc, vs);
+  }
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from oracle import omnikv_oracle as O
-from decode_attention_fwht_amd import synth
+from decode_attention_fwht_amd import binding, synth
 from tests.gpu_helpers import (bf16_tensor, cache_to_device, from_dev, make_context, row_errors,
                                sampled_unit_rows, say, to_dev)
 
@@ -62,6 +62,36 @@ def test_quantize_parity_full(cid, kbits, vbits, n):
     if not np.array_equal(gv, vc):
         gcodes = O.unpack_windows(gv, "value", cfg.head_dim, vbits)
         ocodes = O.unpack_windows(vc, "value", cfg.head_dim, vbits)
+        raise AssertionError(f"{np.count_nonzero(gcodes != ocodes)} of {gcodes.size} value codes differ")
+    ctx.close()
+
+
+@pytest.mark.parametrize("levels", [(-1.3, -0.35, 0.4, 1.7), (-2.0, -0.5, 0.5, 2.0)])
+def test_quantize_values_custom_codebook(levels):
+    """A caller's 2-bit value codebook: boundaries (-b, 0, b) take the value quantizer's
+    sign-and-magnitude classification, any others the three-threshold one; both must give
+    the oracle's codes with that codebook."""
+    import torch
+    cfg = synth.CONFIGS[3]
+    n = 1024
+    say(f"[codec] custom codebook {levels}")
+    d = cfg.head_dim
+    signs = synth.rademacher_signs(d, 0)
+    U = synth.value_rotations(d, 0, 3)
+    lv = O.f16_bits(np.asarray(levels, np.float32))
+    ctx = binding.Context(d, cfg.q_heads, cfg.kv_heads, 2, 2, signs, U, value_codebook=lv)
+    assert np.array_equal(ctx.value_codebook(), lv)
+    tags, k, v = _inputs(cfg, n)
+    cache = ctx.alloc_cache(cfg.batch, n)
+    cache["modality"].copy_(to_dev(tags[:, :n]))
+    ctx.quantize_values(_dev_kv(cfg, v), 0, cache)
+    torch.cuda.synchronize()
+    vc, vs = O.quantize_values(v, tags[:, :n], U, lv, 2)
+    assert np.array_equal(from_dev(cache["v_scale"], np.uint16), vs)
+    gv = from_dev(cache["v_codes"], np.uint32)
+    if not np.array_equal(gv, vc):
+        gcodes = O.unpack_windows(gv, "value", d, 2)
+        ocodes = O.unpack_windows(vc, "value", d, 2)
         raise AssertionError(f"{np.count_nonzero(gcodes != ocodes)} of {gcodes.size} value codes differ")
     ctx.close()
 
