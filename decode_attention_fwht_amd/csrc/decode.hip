@@ -84,10 +84,20 @@ __device__ __forceinline__ float4_t mfma16(uint4_t a, uint4_t b, float4_t c) {
                                                 __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
 }
 
-// value of lane (l ^ 8) within each row of 16 lanes (DPP row_ror:8)
+// value of lane (l ^ 8) within each row of 16 lanes (DPP row_ror:8).  Every lane reads a
+// valid source lane, so the move needs no prior value (a zero-filled destination would cost
+// one more instruction per move).
 __device__ __forceinline__ float row_ror8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
 }
+
+// Wave votes straight from the lane mask of the predicate (the __all / __any forms turn the
+// mask into a 0/1 per lane and compare that again).  The predicate should be one comparison:
+// a combination of several is materialized per lane before the vote.
+__device__ __forceinline__ bool wave_all(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) == __builtin_amdgcn_read_exec();
+}
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Cross-half lane swaps.  Written in asm: the compiler's combine of the
 // permlane{16,32}_swap builtins can replace the second result by the first
@@ -1003,12 +1013,15 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     const uint32_t t00 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tg0))) & 0xFFu;
     const uint32_t rep = t00 * 0x01010101u;
     const bool full = tokb + kWindow <= len;
-    const bool uniform = t00 < static_cast<uint32_t>(kMaxModalities) && full && __all((tg0 == rep) && (tg1 == rep));
+    const bool uniform = t00 < static_cast<uint32_t>(kMaxModalities) && full &&
+                         (__builtin_amdgcn_ballot_w64(tg0 == rep) & __builtin_amdgcn_ballot_w64(tg1 == rep)) ==
+                             __builtin_amdgcn_read_exec();
     // the next most common case: a window inside the sequence whose tags are all below 3
     // (several modalities, every token counts), which needs no masking
     bool clean = uniform;
     // ---- scores relative to m_ref (the first visit of a wave takes absolute scores)
-    const bool fresh = m_ref == -INFINITY;
+    // (every column's reference is set at the first visit: one lane speaks for the wave)
+    const bool fresh = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, m_ref)) == __builtin_bit_cast(int, -INFINITY);
     const float aw = (cm[0] + row_ror8(cm[0])) * zh;
     const float base = fresh ? aw : aw - m_ref;
     float sc[2][4];
@@ -1019,7 +1032,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     if (!uniform) {
       static_assert(kMaxModalities == 3, "tags 0, 1, 2 are the bit patterns 00, 01, 10 of a byte");
       const uint32_t three = (tg0 & (tg0 >> 1)) | (tg1 & (tg1 >> 1));  // bit 0 of a byte: both bits set
-      clean = full && __all(((tg0 | tg1) & 0xFCFCFCFCu) == 0u && (three & 0x01010101u) == 0u);
+      clean = full && wave_all((((tg0 | tg1) & 0xFCFCFCFCu) | (three & 0x01010101u)) == 0u);
     }
     if (!clean) {
       // a real branch: the masking is rare, keep it off the common path
@@ -1044,7 +1057,7 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       }
       // with tags in range every window inside the sequence has a counted token; a window
       // without one (tags out of range) is skipped, which keeps the column max finite
-      if (!__any(any_counted)) return;
+      if (!wave_any(any_counted)) return;
     }
     // ---- probabilities and the range of p sigma.  p sigma enters the value contraction as
     // fp16 hi and lo parts; the reference moves when a lane's largest hi part passes 2^kXMax
@@ -1058,15 +1071,16 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       for (int k = 0; k < 8; ++k) p[k] = exp2_raw(sc[k >> 2][k & 3]);
       mix_quad(p, sgw, zero4, bhi);
     };
-    bool big = fresh;
+    // (fresh is wave-uniform, so the vote below is one comparison's lane mask)
+    bool move = true;
     if (!fresh) {
       probabilities();
       const ushort2_t a = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, bhi[0]), __builtin_bit_cast(ushort2_t, bhi[1]));
       const ushort2_t b2 = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, bhi[2]), __builtin_bit_cast(ushort2_t, bhi[3]));
       const ushort2_t c2 = __builtin_elementwise_max(a, b2);
-      big = max(static_cast<uint32_t>(c2.x), static_cast<uint32_t>(c2.y)) > kHiLimitBits;
+      move = wave_any(max(static_cast<uint32_t>(c2.x), static_cast<uint32_t>(c2.y)) > kHiLimitBits);
     }
-    if (__any(big)) {
+    if (move) {
       // log2(p sigma) + 14 < lx for every token of the lane (uncounted tokens' scales are
       // zero); every visit has a counted token, so the column max is finite
       float lmax = -INFINITY;
@@ -1134,9 +1148,9 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
       const uint32_t o = tg0 | tg1;
       const uint32_t y = (tg0 | (tg0 >> 1)) & (tg1 | (tg1 >> 1));
       const bool a0 = (y & 0x01010101u) != 0x01010101u;
-      const bool a1 = __any((o & 0x01010101u) != 0u), a2 = __any((o & 0x02020202u) != 0u);
+      const bool a1 = wave_any((o & 0x01010101u) != 0u), a2 = wave_any((o & 0x02020202u) != 0u);
       needA = a1 || a2;
-      needB = __any(a0);
+      needB = wave_any(a0);
       seen |= (needB ? 1u : 0u) | (a1 ? 2u : 0u) | (a2 ? 4u : 0u);
     } else {
       bool a12 = false, a0 = false, a1 = false, a2 = false;
@@ -1150,10 +1164,10 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
           a1 = a1 || (ok && tgi == 1u);
           a2 = a2 || (ok && tgi == 2u);
         }
-      a12 = __any(a1 || a2);
+      a12 = wave_any(a1 || a2);
       needA = a12;
-      needB = __any(a0);
-      seen |= (needB ? 1u : 0u) | (__any(a1) ? 2u : 0u) | (__any(a2) ? 4u : 0u);
+      needB = wave_any(a0);
+      seen |= (needB ? 1u : 0u) | (wave_any(a1) ? 2u : 0u) | (wave_any(a2) ? 4u : 0u);
     }
     if (needA) {
       uint32_t kA[4];
