@@ -224,7 +224,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kNearList = 1024;  // near-threshold elements per block shared out by the block
+constexpr int kNearList = 64;    // near-threshold elements a wave lists (the rest: their own lane)
+constexpr int kNearBatch = 8;    // listed elements whose products are formed together
+
+// acc * 2 + (this lane's bit of the lane mask m): one v_addc whose carry-in is the mask, so
+// a comparison's lane mask enters a bit field with no 0/1 value in between
+__device__ __forceinline__ uint32_t push_bit(uint32_t acc, uint64_t m) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(m));
+  return r;
+}
 
 template <int D, int VB, bool SYM>
 __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
@@ -240,12 +250,12 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
   constexpr int TPW = PPW / 4;                // channel tiles per output word
   __shared__ float sig_lds[kWaves][kWindow];
   __shared__ float eps_lds[kWaves][kWindow];
-  // elements near a threshold, block-wide: (wave, token, channel, modality) entries, and
-  // the sequential definition's codes for them
-  __shared__ uint32_t near_list[kNearList];
-  __shared__ int near_count;
-  __shared__ uint64_t row0_lds[kWaves];
-  __shared__ uint8_t fix_lds[kWaves][kWindow][D];
+  // elements near a threshold, per wave: (token, channel, modality) entries, the sequential
+  // definition's codes for them, and one batch's fp32 products (rows padded by 4 floats so
+  // the summing lanes' 16-byte reads fall in different banks)
+  __shared__ uint32_t near_entry[kWaves][kNearList];
+  __shared__ uint8_t near_code[kWaves][kNearList];
+  __shared__ __attribute__((aligned(16))) float near_prod[kWaves][kNearBatch][D + 4];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t task = static_cast<int64_t>(blockIdx.x) * kWaves + wave;  // wave-uniform (scalar math)
@@ -326,8 +336,6 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
       nz[tt] = p16[0] | p16[1];
     }
   }
-  if (threadIdx.x == 0) near_count = 0;
-  if (lane == 0) row0_lds[wave] = row0;
   if (active && g == 0) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -377,6 +385,28 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
         }
       }
     }
+    // symmetric 2-bit codebook, boundaries (-b, 0, b): away from them (the only results this
+    // code decides: near ones take the sequential definition) the high bit is x >= 0 and the
+    // low bit |x| >= sigma b, flipped for x < 0.  Near: within eps of 0 or of +-sigma b (the
+    // two candidates for the nearest boundary); a NaN result counts.  Every test is one
+    // comparison's lane mask, combined on the scalar unit with the lane masks `own` of the
+    // tokens of the modality, and pushed into the bit fields from element 7 down to 0, so
+    // element k = 4 tt + i lands at bits 2k (low) and 2k + 1 (high) of `bits` and at bit k
+    // of `nearm`.
+    auto classify_sym = [&](const float4_t (&acc)[2], const uint64_t (&own)[2][4], uint32_t& bits, uint32_t& nearm) {
+#pragma unroll
+      for (int k = 7; k >= 0; --k) {
+        const int tt = k >> 2, i = k & 3;
+        const float x = acc[tt][i], tb = th[tt][i][kTwoBit ? 2 : 0], ax = fabsf(x), ep = my_ep[tt][i];
+        const uint64_t pos = __builtin_amdgcn_ballot_w64(x >= 0.0f);
+        const uint64_t outer = __builtin_amdgcn_ballot_w64(ax >= tb);
+        const uint64_t near =
+            __builtin_amdgcn_ballot_w64(!(ax > ep)) | __builtin_amdgcn_ballot_w64(!(fabsf(ax - tb) > ep));
+        bits = push_bit(bits, pos & own[tt][i]);
+        bits = push_bit(bits, ~(pos ^ outer) & own[tt][i]);
+        nearm = push_bit(nearm, near & own[tt][i]);
+      }
+    };
     // one channel tile's eight results -> codes (tt, i) at bit VB (4 tt + i) of `bits` and
     // near-threshold flags at bit 4 tt + i of `nearm`, for the tokens of modality m
     auto classify = [&](const float4_t (&acc)[2], uint32_t m, bool mixed, uint32_t& bits, uint32_t& nearm) {
@@ -387,47 +417,39 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
           const float x = acc[tt][i];
           const bool mine = !mixed || my_tag[tt][i] == m;
           const int sh = VB * (4 * tt + i);
-          if constexpr (kTwoBit && SYM) {
-            // boundaries (-b, 0, b): away from them (the only results this code decides:
-            // near ones take the sequential definition) the high bit is x >= 0 and the low
-            // bit |x| >= sigma b, flipped for x < 0.  Near: within eps of 0 or of +-sigma b
-            // (the two candidates for the nearest boundary); a NaN result counts.
-            const float tb = th[tt][i][2], ax = fabsf(x);
-            const bool pos = x >= 0.0f, outer = ax >= tb;
-            const bool near0 = !(ax > my_ep[tt][i]), near1 = !(fabsf(ax - tb) > my_ep[tt][i]);
-            const bool near = near0 | near1;  // both evaluated: no branch
-            bits |= (mine && pos ? (2u << sh) : 0u) | (mine && outer == pos ? (1u << sh) : 0u);
-            nearm |= (near && mine ? 1u : 0u) << (4 * tt + i);
+          uint32_t code;
+          bool near;
+          if constexpr (kTwoBit) {
+            // the thresholds rise (finite scale), so the three comparisons form a
+            // thermometer: code = c0 + c1 + c2 has high bit c1 and low bit c0 ^ c1 ^ c2
+            const bool c0 = x >= th[tt][i][0], c1 = x >= th[tt][i][1], c2 = x >= th[tt][i][2];
+            code = (c1 ? 2u : 0u) | ((c0 ^ c1 ^ c2) ? 1u : 0u);
+            // a NaN distance (NaN sum) stays NaN through the min and counts as near
+            const float dmin = fminf(fminf(fabsf(x - th[tt][i][0]), fabsf(x - th[tt][i][1])), fabsf(x - th[tt][i][2]));
+            near = !(dmin > my_ep[tt][i]);
           } else {
-            uint32_t code;
-            bool near;
-            if constexpr (kTwoBit) {
-              // the thresholds rise (finite scale), so the three comparisons form a
-              // thermometer: code = c0 + c1 + c2 has high bit c1 and low bit c0 ^ c1 ^ c2
-              const bool c0 = x >= th[tt][i][0], c1 = x >= th[tt][i][1], c2 = x >= th[tt][i][2];
-              code = (c1 ? 2u : 0u) | ((c0 ^ c1 ^ c2) ? 1u : 0u);
-              // a NaN distance (NaN sum) stays NaN through the min and counts as near
-              const float dmin = fminf(fminf(fabsf(x - th[tt][i][0]), fabsf(x - th[tt][i][1])), fabsf(x - th[tt][i][2]));
-              near = !(dmin > my_ep[tt][i]);
-            } else {
-              code = 0u;
-              near = false;
+            code = 0u;
+            near = false;
 #pragma unroll
-              for (int j = 0; j < NB; ++j) {
-                const float thj = my_sg[tt][i] * beta[j];
-                code += (x >= thj) ? 1u : 0u;
-                near = near || !(fabsf(x - thj) > my_ep[tt][i]);  // NaN or infinite sums count
-              }
+            for (int j = 0; j < NB; ++j) {
+              const float thj = my_sg[tt][i] * beta[j];
+              code += (x >= thj) ? 1u : 0u;
+              near = near || !(fabsf(x - thj) > my_ep[tt][i]);  // NaN or infinite sums count
             }
-            bits |= (mine ? code : 0u) << sh;
-            nearm |= (near && mine ? 1u : 0u) << (4 * tt + i);
           }
+          bits |= (mine ? code : 0u) << sh;
+          nearm |= (near && mine ? 1u : 0u) << (4 * tt + i);
         }
     };
 #pragma unroll
     for (int m = 0; m < kMaxModalities; ++m) {
       if (!(present & (1u << m))) continue;
       const bool mixed = present != (1u << m);  // wave-uniform
+      uint64_t own[2][4];  // lanes whose token (tt, i) has modality m
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) own[tt][i] = mixed ? __builtin_amdgcn_ballot_w64(my_tag[tt][i] == m) : ~uint64_t{0};
       const uint4_t* B = rot_b16 + static_cast<size_t>(m) * 3 * NCT * NKS * 64 + lane;
       // U_m's tiles come from L2: all eight of a channel tile are requested before its
       // products (a barrier keeps the scheduler from sinking each load to its use)
@@ -449,24 +471,43 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
               acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[tt][ks]),
                                                                 __builtin_bit_cast(bf16x8_t, bv[part][ks]), acc[tt], 0, 0, 0);
         uint32_t bits = 0u, nearm = 0u;
-        if (kTwoBit && !mixed)  // (a copy without the modality test for the common case)
-          classify(acc, static_cast<uint32_t>(m), false, bits, nearm);
-        else
-          classify(acc, static_cast<uint32_t>(m), mixed, bits, nearm);
+        if constexpr (kTwoBit && SYM) {
+          classify_sym(acc, own, bits, nearm);
+        } else {
+          if (kTwoBit && !mixed)  // (a copy without the modality test for the common case)
+            classify(acc, static_cast<uint32_t>(m), false, bits, nearm);
+          else
+            classify(acc, static_cast<uint32_t>(m), mixed, bits, nearm);
+        }
         // token pair p = 4 ct + 2 tt + (i >> 1) goes to word p / PPW at bit 2 VB (p % PPW) +
         // VB (i & 1) = 8 VB (ct % TPW) + VB (4 tt + i), TPW = PPW / 4 tiles per word
-        words[ct / TPW] |= bits << (8 * VB * (ct % TPW));
+        if constexpr (VB == 2 && VW == 4) {
+          // tile ct's 16 bits go to bits 16 ct .. 16 ct + 15 of the 128-bit word queue: each
+          // tile turns the queue right by 16 bits and ORs its bits into the top, so after a
+          // pass's eight tiles every earlier bit is back in place and tile ct's bits sit at 16 ct
+          const uint32_t w0 = words[0];
+          words[0] = __builtin_amdgcn_alignbit(words[1], words[0], 16);
+          words[1] = __builtin_amdgcn_alignbit(words[2], words[1], 16);
+          words[2] = __builtin_amdgcn_alignbit(words[3], words[2], 16);
+          words[3] = __builtin_amdgcn_alignbit(w0, words[3], 16) | (bits << 16);
+        } else {
+          words[ct / TPW] |= bits << (8 * VB * (ct % TPW));
+        }
         near_bits |= static_cast<uint64_t>(nearm) << (8 * ct);
       }
     }
   }
 
-  // ---- the sequential definition for the elements near a threshold (rare).  The block's
-  // flagged elements go to one list, which the block's threads share out, so one pass of
-  // the 128-term sum covers what would otherwise cost each wave a pass of its own.
-  auto exact_code = [&](int ew, int t, int c, uint32_t tg) -> uint32_t {
+  // ---- the sequential definition for the elements near a threshold (rare), wave by wave.
+  // The wave lists its flagged elements in LDS.  For each batch of listed elements, lane L
+  // loads terms 2L and 2L + 1 of every element's dot product (coalesced rows of U_m^T and
+  // of the token) and forms their fp32 products; one lane per element then adds its 128
+  // products in the definition's order.  A listed element costs the wave two loads and a
+  // few instructions, and its 128-term sum runs beside the batch's others; no other wave
+  // waits for it.  Elements past the list's room are computed by their own lane, alone.
+  auto exact_code = [&](int t, int c, uint32_t tg) -> uint32_t {
     const float* ut = rot_t + (static_cast<size_t>(tg) * D + c) * D;
-    const uint16_t* vr = v + row0_lds[ew] + t * rstride;
+    const uint16_t* vr = v + row0 + t * rstride;
     float s = 0.0f;
     for (int k0 = 0; k0 < D; k0 += 8) {
       const float4 u0 = *reinterpret_cast<const float4*>(ut + k0);
@@ -479,7 +520,7 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
         s = s + uu[kk] * __uint_as_float(half << 16);
       }
     }
-    const float sg = sig_lds[ew][t];
+    const float sg = sig_lds[wave][t];
     uint32_t code = 0;
     for (int j = 0; j < NB; ++j) code += (s >= sg * boundaries[j]) ? 1u : 0u;
     return code;
@@ -493,43 +534,94 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
       if (x == 4 * tt + i) tg = my_tag[x >> 2][x & 3];
     return tg;
   };
-  uint64_t own = 0u;  // flagged elements the list had no room for: this lane computes them
   if (active) {
-    uint64_t todo = near_bits;
-    while (todo != 0u) {
-      const int k = __builtin_ctzll(todo);
-      todo &= todo - 1u;
-      const int ct = k >> 3, tt = (k >> 2) & 1, i = k & 3;
-      const int idx = atomicAdd(&near_count, 1);
-      if (idx < kNearList)
-        near_list[idx] = (static_cast<uint32_t>(wave) << 14) | (static_cast<uint32_t>(16 * tt + 4 * g + i) << 9) |
-                         (static_cast<uint32_t>(16 * ct + nn) << 2) | tag_of(tt, i);
-      else
-        own |= uint64_t{1} << k;
+    // Slots: pass j gives each lane's j-th flagged element (lowest bit first) the next free
+    // slot, lanes in order.  The same passes run again for the patching below, so each lane
+    // finds its elements' slots without storing them.
+    uint32_t listed = 0u;  // wave-uniform
+    {
+      uint64_t todo = near_bits;
+      for (;;) {
+        const uint64_t has = __builtin_amdgcn_ballot_w64(todo != 0u);
+        if (has == 0u) break;
+        if (todo != 0u) {
+          const uint32_t slot = listed + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(has >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(has), 0u));
+          const int k = __builtin_ctzll(todo);
+          todo &= todo - 1u;
+          const int ct = k >> 3, tt = (k >> 2) & 1, i = k & 3;
+          if (slot < static_cast<uint32_t>(kNearList))
+            near_entry[wave][slot] = (static_cast<uint32_t>(16 * tt + 4 * g + i) << 9) |
+                                     (static_cast<uint32_t>(16 * ct + nn) << 2) | tag_of(tt, i);
+        }
+        listed += static_cast<uint32_t>(__builtin_popcountll(has));
+      }
     }
-  }
-  __syncthreads();
-  {
-    const int total = min(near_count, kNearList);
-    for (int e = threadIdx.x; e < total; e += kWaves * 64) {
-      const uint32_t en = near_list[e];
-      const int ew = static_cast<int>(en >> 14), t = static_cast<int>((en >> 9) & 31u), c = static_cast<int>((en >> 2) & 127u);
-      fix_lds[ew][t][c] = static_cast<uint8_t>(exact_code(ew, t, c, en & 3u));
-    }
-  }
-  __syncthreads();
-  if (active) {
-    uint64_t todo = near_bits;
-    while (todo != 0u) {
-      const int k = __builtin_ctzll(todo);
-      todo &= todo - 1u;
-      const int ct = k >> 3, tt = (k >> 2) & 1, i = k & 3;
-      const int t = 16 * tt + 4 * g + i, c = 16 * ct + nn;
-      const uint32_t code = ((own >> k) & 1u) ? exact_code(wave, t, c, tag_of(tt, i)) : fix_lds[wave][t][c];
-      const int bit = 8 * VB * (ct % TPW) + 4 * VB * tt + VB * i;
+    const int n = static_cast<int>(min(listed, static_cast<uint32_t>(kNearList)));
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int e0 = 0; e0 < n; e0 += kNearBatch) {
+      // every lane's two terms of each element of the batch, all requested before any use
+      float2 uu[kNearBatch];
+      uint32_t vv[kNearBatch];
+      const bool terms = 2 * lane < D;
 #pragma unroll
-      for (int x = 0; x < VW; ++x)
-        if (x == ct / TPW) words[x] = (words[x] & ~(((1u << VB) - 1u) << bit)) | (code << bit);
+      for (int j = 0; j < kNearBatch; ++j) {
+        uu[j] = make_float2(0.0f, 0.0f);
+        vv[j] = 0u;
+        if (e0 + j < n && terms) {
+          const uint32_t en = near_entry[wave][e0 + j];
+          const int et = static_cast<int>(en >> 9), ec = static_cast<int>((en >> 2) & 127u);
+          uu[j] = *reinterpret_cast<const float2*>(rot_t + (static_cast<size_t>(en & 3u) * D + ec) * D + 2 * lane);
+          vv[j] = *reinterpret_cast<const uint32_t*>(v + row0 + et * rstride + 2 * lane);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kNearBatch; ++j)
+        if (e0 + j < n && terms)
+          *reinterpret_cast<float2*>(&near_prod[wave][j][2 * lane]) =
+              make_float2(uu[j].x * __uint_as_float(vv[j] << 16), uu[j].y * __uint_as_float(vv[j] & 0xFFFF0000u));
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (lane < kNearBatch && e0 + lane < n) {
+        const float* pr = near_prod[wave][lane];
+        float s = 0.0f;
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(pr + k0);
+          s = s + q.x;
+          s = s + q.y;
+          s = s + q.z;
+          s = s + q.w;
+        }
+        const uint32_t en = near_entry[wave][e0 + lane];
+        const float sg = sig_lds[wave][en >> 9];
+        uint32_t code = 0;
+        for (int j = 0; j < NB; ++j) code += (s >= sg * boundaries[j]) ? 1u : 0u;
+        near_code[wave][e0 + lane] = static_cast<uint8_t>(code);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+    // patch: the same slot passes
+    {
+      uint64_t todo = near_bits;
+      listed = 0u;
+      for (;;) {
+        const uint64_t has = __builtin_amdgcn_ballot_w64(todo != 0u);
+        if (has == 0u) break;
+        if (todo != 0u) {
+          const uint32_t slot = listed + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(has >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(has), 0u));
+          const int k = __builtin_ctzll(todo);
+          todo &= todo - 1u;
+          const int ct = k >> 3, tt = (k >> 2) & 1, i = k & 3;
+          const int t = 16 * tt + 4 * g + i, c = 16 * ct + nn;
+          const uint32_t code = slot < static_cast<uint32_t>(kNearList) ? near_code[wave][slot] : exact_code(t, c, tag_of(tt, i));
+          const int bit = 8 * VB * (ct % TPW) + 4 * VB * tt + VB * i;
+#pragma unroll
+          for (int x = 0; x < VW; ++x)
+            if (x == ct / TPW) words[x] = (words[x] & ~(((1u << VB) - 1u) << bit)) | (code << bit);
+        }
+        listed += static_cast<uint32_t>(__builtin_popcountll(has));
+      }
     }
     uint32_t* dst = v_codes + blk * (D * VB) + lane * VW;
 #pragma unroll
