@@ -17,7 +17,8 @@ the same way.  The write path is timed separately on one prefill chunk per seque
 
 Prints one JSON line: the headline (effective KV GB/s of the decode step), the
 roofline of the partial kernel, the write-path timings, the other configurations
-(configs 4 and 5 at K2V2 and K4V4, the config-5 prefill write path) and a CPU-oracle
+(configs 4 and 5 at K2V2 and K4V4, the write path at K4V4 and the config-5 prefill
+write path at both widths) and a CPU-oracle
 baseline on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -350,7 +351,7 @@ def main():
     ap.add_argument("--buffers", type=int, default=0, help="independent caches cycled (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
-                    help="skip the other configurations (configs 4 and 5, K2V2 and K4V4, and the config-5 write path)")
+                    help="skip the other configurations (configs 4 and 5, K2V2 and K4V4, and the 4-bit and config-5 write paths)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="also run a plain device copy (out = 1 * in, fp32) of this many MiB, the "
@@ -441,12 +442,18 @@ def main():
         others = {}
         for cid, kb, vb in ((4, 2, 2), (4, 4, 4), (5, 2, 2), (5, 4, 4)):
             others[f"config{cid}_K{kb}V{vb}"] = decode_config(cid, kb, vb, "fp16", 10, 20, 10)
+        # the write path at 4 bits: this configuration's chunk, and the config-5 prefill at both widths
+        ctx4 = binding.Context(d, cfg.q_heads, cfg.kv_heads, 4, 4, signs, U)
+        others[f"config{cfg.cid}_write_K4V4"] = time_write_path(
+            ctx4, cfg, synth.modality_layout(cfg, 0, max(cfg.context, cfg.prefill or 4096)), reps=20)
+        ctx4.close()
         cfg5 = synth.CONFIGS[5]
-        ctx5 = binding.Context(cfg5.head_dim, cfg5.q_heads, cfg5.kv_heads, 2, 2, signs, U)
-        others["config5_prefill_write_K2V2"] = time_write_path(ctx5, cfg5, synth.modality_layout(cfg5, 0, cfg5.prefill),
-                                                               reps=10)
-        ctx5.close()
-        torch.cuda.empty_cache()
+        tags5 = synth.modality_layout(cfg5, 0, cfg5.prefill)
+        for bits in (2, 4):
+            ctx5 = binding.Context(cfg5.head_dim, cfg5.q_heads, cfg5.kv_heads, bits, bits, signs, U)
+            others[f"config5_prefill_write_K{bits}V{bits}"] = time_write_path(ctx5, cfg5, tags5, reps=10)
+            ctx5.close()
+            torch.cuda.empty_cache()
         res["configs"] = others
     if args.copy_reference_mib:
         n = args.copy_reference_mib * (1 << 20) // 4

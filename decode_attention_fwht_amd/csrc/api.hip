@@ -269,7 +269,14 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
         lo_norm = std::max(lo_norm, std::sqrt(s2));
       }
   ctx->tb.rot_lo_col_norm = static_cast<float>(lo_norm * (1.0 + 1e-6));
-  ctx->tb.value_sym2 = nl == 4 && bnd[1] == 0.0f && bnd[0] == -bnd[2];
+  // a symmetric codebook (boundaries -b_k .. -b_1, 0, b_1 .. b_k, as the built-in Lloyd-Max
+  // tables are) lets the value quantizer classify by sign and magnitude
+  {
+    const int nb = nl - 1, mid = nb / 2;
+    bool sym = bnd[mid] == 0.0f;
+    for (int j = 1; j <= mid; ++j) sym = sym && bnd[mid - j] == -bnd[mid + j];
+    ctx->tb.value_sym = sym;
+  }
 
   omnikv_status st;
   if ((st = upload(&ctx->tb.signs, sg.data(), sg.size())) != OMNIKV_OK ||

@@ -35,7 +35,7 @@ struct DeviceTables {
   float rot_lo_col_norm = 0.0f;
   // host value: 2-bit values whose boundaries are (-b, 0, b) exactly (the built-in Gaussian
   // codebook is symmetric); the value quantizer then classifies by sign and magnitude
-  bool value_sym2 = false;
+  bool value_sym = false;  // value boundaries symmetric about 0 (0 in the middle)
 };
 
 // Streaming schedule ([paper] §3.1 Implementation details, captioning): after n

@@ -235,6 +235,13 @@ __device__ __forceinline__ uint32_t push_bit(uint32_t acc, uint64_t m) {
   asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(m));
   return r;
 }
+// acc + (this lane's bit of the lane mask m): a count of comparisons, one v_addc each
+__device__ __forceinline__ uint32_t count_bit(uint32_t acc, uint64_t m) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(m));
+  return r;
+}
 
 template <int D, int VB, bool SYM>
 __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
@@ -385,6 +392,29 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
         }
       }
     }
+    // symmetric 4-bit codebook: the token's magnitude |x| / sigma against the positive
+    // boundaries, with a tolerance carried into that scale (below), and the code fields of the
+    // lane's all-zero tokens (code 15: every threshold is +-0 there and x = 0)
+    constexpr bool kSym4 = !kTwoBit && SYM;
+    float rsg[2][4], epy[2][4];
+    uint32_t zero_fields = 0u;
+    if constexpr (kSym4) {
+      const float bmax = beta[NB - 1];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sg = my_sg[tt][i], ep = my_ep[tt][i];
+          // an all-zero token has tolerance -1 (never near); a token whose squares underflow
+          // (sigma 0, tolerance 1e-20) gets y = 0 and a positive tolerance: all its elements
+          // are near and take the sequential definition, as the signs of their sums decide
+          const bool zero = ep < 0.0f;
+          rsg[tt][i] = sg > 0.0f ? 1.0f / sg : 0.0f;  // sigma is an fp16 value: 1 / sigma <= 2^24
+          epy[tt][i] = zero ? -1.0f
+                            : (!__builtin_isfinite(ep) ? INFINITY : ep * rsg[tt][i] * (1.0f + 0x1p-16f) + 0x1p-19f * bmax);
+          if (zero) zero_fields |= 0xFu << (VB * (4 * tt + i));
+        }
+    }
     // symmetric 2-bit codebook, boundaries (-b, 0, b): away from them (the only results this
     // code decides: near ones take the sequential definition) the high bit is x >= 0 and the
     // low bit |x| >= sigma b, flipped for x < 0.  Near: within eps of 0 or of +-sigma b (the
@@ -405,6 +435,33 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
         bits = push_bit(bits, pos & own[tt][i]);
         bits = push_bit(bits, ~(pos ^ outer) & own[tt][i]);
         nearm = push_bit(nearm, near & own[tt][i]);
+      }
+    };
+    // symmetric 4-bit codebook, boundaries (-b7 .. -b1, 0, b1 .. b7): with m = #{j : y >= b_j},
+    // y = |x| / sigma as computed (|x| times the rounded reciprocal), the code is 8 + m for
+    // x >= 0 and 7 - m below: (x >= 0 ? 8 : 7) XOR m.  Near: y within epy of 0 or of some
+    // b_j.  epy = eps / sigma (1 + 2^-16) + 2^-19 b7 covers the two roundings of y and the
+    // rounding of the definition's thresholds sigma b_j (relative 2^-23 and 2^-24 of values
+    // at most ~b7 where it matters), so an element outside every band has |x| on the same
+    // side of each threshold as y is of b_j, farther than eps.  A NaN result is near; an
+    // infinite scale has an infinite tolerance.  `mine` drops the tokens of other modalities.
+    auto classify_sym4 = [&](const float4_t (&acc)[2], const bool (&mine)[2][4], const uint64_t (&own)[2][4],
+                             uint32_t& bits, uint32_t& nearm) {
+#pragma unroll
+      for (int k = 7; k >= 0; --k) {
+        const int tt = k >> 2, i = k & 3;
+        const float x = acc[tt][i], y = fabsf(x) * rsg[tt][i];
+        uint32_t m = 0u;
+        float d = y;
+#pragma unroll
+        for (int j = 0; j < NB / 2; ++j) {
+          const float b = beta[NB / 2 + 1 + j];
+          m = count_bit(m, __builtin_amdgcn_ballot_w64(y >= b));
+          d = fminf(d, fabsf(y - b));
+        }
+        const uint32_t code = ((x >= 0.0f) ? 8u : 7u) ^ m;
+        bits = (bits << 4) | (mine[tt][i] ? code : 0u);
+        nearm = push_bit(nearm, __builtin_amdgcn_ballot_w64(!(d > epy[tt][i])) & own[tt][i]);
       }
     };
     // one channel tile's eight results -> codes (tt, i) at bit VB (4 tt + i) of `bits` and
@@ -446,10 +503,16 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
       if (!(present & (1u << m))) continue;
       const bool mixed = present != (1u << m);  // wave-uniform
       uint64_t own[2][4];  // lanes whose token (tt, i) has modality m
+      bool mine[2][4];
+      uint32_t mine_fields = 0u;  // (4-bit) code fields of this lane's tokens of modality m
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) own[tt][i] = mixed ? __builtin_amdgcn_ballot_w64(my_tag[tt][i] == m) : ~uint64_t{0};
+        for (int i = 0; i < 4; ++i) {
+          mine[tt][i] = !mixed || my_tag[tt][i] == static_cast<uint32_t>(m);
+          own[tt][i] = mixed ? __builtin_amdgcn_ballot_w64(my_tag[tt][i] == m) : ~uint64_t{0};
+          if (mine[tt][i]) mine_fields |= 0xFu << (VB * (4 * tt + i));
+        }
       const uint4_t* B = rot_b16 + static_cast<size_t>(m) * 3 * NCT * NKS * 64 + lane;
       // U_m's tiles come from L2: all eight of a channel tile are requested before its
       // products (a barrier keeps the scheduler from sinking each load to its use)
@@ -473,6 +536,9 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
         uint32_t bits = 0u, nearm = 0u;
         if constexpr (kTwoBit && SYM) {
           classify_sym(acc, own, bits, nearm);
+        } else if constexpr (kSym4) {
+          classify_sym4(acc, mine, own, bits, nearm);
+          bits |= zero_fields & mine_fields;
         } else {
           if (kTwoBit && !mixed)  // (a copy without the modality test for the common case)
             classify(acc, static_cast<uint32_t>(m), false, bits, nearm);
@@ -652,13 +718,11 @@ hipError_t launch_vb(const DeviceTables& tb, const void* v, bool bf16, const uin
   const dim3 grid(static_cast<unsigned>((tasks + kWaves - 1) / kWaves));
   const float eps = static_cast<float>(value_eps_unit<D>() * tb.rot_col_norm + 1.02 * tb.rot_lo_col_norm);
   if (bf16 && tb.rot_bf16 != nullptr) {
-    if constexpr (VB == 2) {
-      if (tb.value_sym2) {
-        quantize_values_mfma_kernel<D, VB, true><<<grid, 256, 0, stream>>>(
-            static_cast<const uint16_t*>(v), mod, hkv, src, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
-            tb.rotations_t, tb.boundaries, eps, vc, vs);
-        return hipGetLastError();
-      }
+    if (tb.value_sym) {
+      quantize_values_mfma_kernel<D, VB, true><<<grid, 256, 0, stream>>>(
+          static_cast<const uint16_t*>(v), mod, hkv, src, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
+          tb.rotations_t, tb.boundaries, eps, vc, vs);
+      return hipGetLastError();
     }
     quantize_values_mfma_kernel<D, VB, false><<<grid, 256, 0, stream>>>(
         static_cast<const uint16_t*>(v), mod, hkv, src, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),

@@ -66,32 +66,38 @@ def test_quantize_parity_full(cid, kbits, vbits, n):
     ctx.close()
 
 
-@pytest.mark.parametrize("levels", [(-1.3, -0.35, 0.4, 1.7), (-2.0, -0.5, 0.5, 2.0)])
+_SYM16 = (0.1, 0.35, 0.6, 0.9, 1.2, 1.6, 2.0, 2.6)
+
+
+@pytest.mark.parametrize("levels", [(-1.3, -0.35, 0.4, 1.7), (-2.0, -0.5, 0.5, 2.0),
+                                    tuple(np.round(np.linspace(-2.3, 1.9, 16) + 0.07 * np.sin(np.arange(16)), 3)),
+                                    tuple(-x for x in reversed(_SYM16)) + _SYM16])
 def test_quantize_values_custom_codebook(levels):
-    """A caller's 2-bit value codebook: boundaries (-b, 0, b) take the value quantizer's
-    sign-and-magnitude classification, any others the three-threshold one; both must give
-    the oracle's codes with that codebook."""
+    """A caller's value codebook (2 or 4 bits): boundaries symmetric about 0 take the value
+    quantizer's sign-and-magnitude classification, any others the general one; both must
+    give the oracle's codes with that codebook."""
     import torch
     cfg = synth.CONFIGS[3]
     n = 1024
-    say(f"[codec] custom codebook {levels}")
+    bits = 2 if len(levels) == 4 else 4
+    say(f"[codec] custom {bits}-bit codebook {levels}")
     d = cfg.head_dim
     signs = synth.rademacher_signs(d, 0)
     U = synth.value_rotations(d, 0, 3)
     lv = O.f16_bits(np.asarray(levels, np.float32))
-    ctx = binding.Context(d, cfg.q_heads, cfg.kv_heads, 2, 2, signs, U, value_codebook=lv)
+    ctx = binding.Context(d, cfg.q_heads, cfg.kv_heads, bits, bits, signs, U, value_codebook=lv)
     assert np.array_equal(ctx.value_codebook(), lv)
     tags, k, v = _inputs(cfg, n)
     cache = ctx.alloc_cache(cfg.batch, n)
     cache["modality"].copy_(to_dev(tags[:, :n]))
     ctx.quantize_values(_dev_kv(cfg, v), 0, cache)
     torch.cuda.synchronize()
-    vc, vs = O.quantize_values(v, tags[:, :n], U, lv, 2)
+    vc, vs = O.quantize_values(v, tags[:, :n], U, lv, bits)
     assert np.array_equal(from_dev(cache["v_scale"], np.uint16), vs)
     gv = from_dev(cache["v_codes"], np.uint32)
     if not np.array_equal(gv, vc):
-        gcodes = O.unpack_windows(gv, "value", d, 2)
-        ocodes = O.unpack_windows(vc, "value", d, 2)
+        gcodes = O.unpack_windows(gv, "value", d, bits)
+        ocodes = O.unpack_windows(vc, "value", d, bits)
         raise AssertionError(f"{np.count_nonzero(gcodes != ocodes)} of {gcodes.size} value codes differ")
     ctx.close()
 
@@ -125,7 +131,8 @@ def test_quantize_offset_chunk_writes_only_its_windows():
     ctx.close()
 
 
-def test_quantize_values_degenerate_tokens():
+@pytest.mark.parametrize("vbits", [2, 4])
+def test_quantize_values_degenerate_tokens(vbits):
     """Value codes for tokens at the edges of the bf16 matrix-core path: an all-zero window,
     zero tokens, tokens whose squares underflow (sum of squares 0, so sigma = 0 and every
     rotated value lies within the error bound of a threshold: 3 such tokens in a window are
@@ -134,8 +141,8 @@ def test_quantize_values_degenerate_tokens():
     import torch
     cfg = synth.CONFIGS[2]
     n = 256
-    say("[codec-degenerate] cfg2 n=256")
-    ctx, signs, U, lv = make_context(cfg)
+    say(f"[codec-degenerate] cfg2 V{vbits} n=256")
+    ctx, signs, U, lv = make_context(cfg, 2, vbits)
     tags, k, v = _inputs(cfg, n)
     v = v.copy()
     v[:, 0:32] = 0.0                      # window 0: all zero
@@ -150,12 +157,12 @@ def test_quantize_values_degenerate_tokens():
     ctx.quantize_values(bf16_tensor(v), 0, cache)
     torch.cuda.synchronize()
     with np.errstate(all="ignore"):
-        vc, vs = O.quantize_values(v, tags[:, :n], U, lv, 2)
+        vc, vs = O.quantize_values(v, tags[:, :n], U, lv, vbits)
     assert np.array_equal(from_dev(cache["v_scale"], np.uint16), vs)
     gv = from_dev(cache["v_codes"], np.uint32)
     if not np.array_equal(gv, vc):
-        gcodes = O.unpack_windows(gv, "value", cfg.head_dim, 2)
-        ocodes = O.unpack_windows(vc, "value", cfg.head_dim, 2)
+        gcodes = O.unpack_windows(gv, "value", cfg.head_dim, vbits)
+        ocodes = O.unpack_windows(vc, "value", cfg.head_dim, vbits)
         bad = np.argwhere(gcodes != ocodes)
         raise AssertionError(f"{len(bad)} value codes differ, first at {bad[:4].tolist()}")
     ctx.close()
