@@ -1022,13 +1022,24 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     // ---- scores relative to m_ref (the first visit of a wave takes absolute scores)
     // (every column's reference is set at the first visit: one lane speaks for the wave)
     const bool fresh = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, m_ref)) == __builtin_bit_cast(int, -INFINITY);
-    const float aw = (cm[0] + row_ror8(cm[0])) * zh;
+    // hi + lo column sums (lane n + 8's column into lane n's).  The empty asm keeps each sum
+    // in the block of its DPP move (the move, convergent, stays put; a sum sunk into a later
+    // block could not fold into it), so the pair becomes one v_add_f32_dpp.
+    float aws = cm[0] + row_ror8(cm[0]);
+    float hl[2][4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hl[tau][i] = cs[tau][i] + row_ror8(cs[tau][i]);
+    asm volatile("" : "+v"(aws), "+v"(hl[0][0]), "+v"(hl[0][1]), "+v"(hl[0][2]), "+v"(hl[0][3]),
+                 "+v"(hl[1][0]), "+v"(hl[1][1]), "+v"(hl[1][2]), "+v"(hl[1][3]));
+    const float aw = aws * zh;
     const float base = fresh ? aw : aw - m_ref;
     float sc[2][4];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[tau][i] = fmaf(cs[tau][i] + row_ror8(cs[tau][i]), zfac, base);
+      for (int i = 0; i < 4; ++i) sc[tau][i] = fmaf(hl[tau][i], zfac, base);
     if (!uniform) {
       static_assert(kMaxModalities == 3, "tags 0, 1, 2 are the bit patterns 00, 01, 10 of a byte");
       const uint32_t three = (tg0 & (tg0 >> 1)) | (tg1 & (tg1 >> 1));  // bit 0 of a byte: both bits set
@@ -1221,6 +1232,9 @@ __global__ __launch_bounds__(kWaves * 64, kBlocksPerCU) void decode_partial_kern
     uint4_t av[NU];
     value_operands(slot, av);
     visit(slot, (wbeg + i) * kWindow, cs, cm, av);
+    // no LDS read crosses into the next visit (a skipped window leaves its value-table reads
+    // in flight; unknown to the next visit, they made each of its LDS reads wait in turn)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
   }
 
   __builtin_amdgcn_s_setprio(0);
