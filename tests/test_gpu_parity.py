@@ -306,7 +306,8 @@ def test_decode_split_invariance():
     cache = cache_to_device(synth.random_packed_cache(cfg, 1, length=T))
     q = to_dev(synth.queries(cfg, 7))
     lens = to_dev(np.array([T - 3], np.int32))
-    outs = [from_dev(ctx.decode(q, lens, T, cache, num_splits=s)) for s in (1, 3, 0, 64, 320)]
+    # (5000 asks for more splits than the 320 windows: one window per split, as for 320)
+    outs = [from_dev(ctx.decode(q, lens, T, cache, num_splits=s)) for s in (1, 3, 0, 64, 320, 5000)]
     torch.cuda.synchronize()
     # Splits change each partial's reference max, hence the fp16 hi/lo rounding
     # of the probability operand (~2^-22 relative, 2^-25 absolute when the low
@@ -314,6 +315,32 @@ def test_decode_split_invariance():
     # below the 1e-3 bar against the oracle.
     for o in outs[1:]:
         assert row_errors(o, outs[0]).max() < 3e-5
+    ctx.close()
+
+
+def test_decode_max_splits():
+    """1024 splits per (sequence, KV head), the most the plan makes, and a request beyond it:
+    a 32,768-token context (1024 windows, one per split) against the default plan, and
+    against the oracle on sampled rows."""
+    import torch
+    cfg = synth.CONFIGS[2]
+    T = 32768
+    say(f"[max-splits] cfg2 T={T}")
+    ctx, signs, U, lv = make_context(cfg)
+    host = synth.random_packed_cache(cfg, 21, length=T)
+    cache = cache_to_device(host)
+    q_np = synth.queries(cfg, 21)
+    q = to_dev(q_np)
+    lens_np = np.array([T - 17], np.int32)
+    lens = to_dev(lens_np)
+    outs = [from_dev(ctx.decode(q, lens, T, cache, num_splits=s)) for s in (0, 1024, 100000)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert row_errors(o, outs[0]).max() < 3e-5
+    ref = O.decode_attention(q_np, lens_np, host, signs, U, lv)
+    err = row_errors(outs[1], ref)
+    say(f"    max row error {err.max():.3e}")
+    assert err.max() <= TOL
     ctx.close()
 
 
