@@ -18,6 +18,7 @@ import pytest
 
 from decode_attention_fwht_amd import build as B
 
+
 def _have_hipcc() -> bool:
     try:
         h = B._hipcc()
