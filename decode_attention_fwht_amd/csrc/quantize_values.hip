@@ -243,9 +243,26 @@ __device__ __forceinline__ uint32_t count_bit(uint32_t acc, uint64_t m) {
   return r;
 }
 
-template <int D, int VB, bool SYM>
+// A fp32 value v as the sum of two bf16 operands plus a small remainder: hi is v with its
+// low 16 bits cleared (exact), lo the nearest bf16 to v - hi (exact in fp32), so
+// |v - hi - lo| <= 2^-8 |v - hi| < 2^-15 |v| (for |v| >= 2^-126; below, at most half the
+// smallest bf16 subnormal, 2^-134).
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi16, uint32_t& lo16) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t h = u & 0xFFFF0000u;
+  const float r = x - __uint_as_float(h);
+  const uint32_t ru = __float_as_uint(r);
+  // round to nearest even at bit 16 (r is finite: x - hi of a finite x)
+  const uint32_t l = (ru + 0x7FFFu + ((ru >> 16) & 1u)) & 0xFFFF0000u;
+  hi16 = h >> 16;
+  lo16 = l >> 16;
+}
+
+// F32: the values come as fp32; each enters the matrix cores as a bf16 hi and lo part
+// (split_bf16), and the tolerance covers the remainder.  Otherwise bf16 values as they come.
+template <int D, int VB, bool SYM, bool F32>
 __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
-    const uint16_t* __restrict__ v, const uint8_t* __restrict__ modality, int hkv, WindowSource src,
+    const void* __restrict__ vin, const uint8_t* __restrict__ modality, int hkv, WindowSource src,
     int64_t t_cap, int64_t tasks, const uint4_t* __restrict__ rot_b16,
     const float* __restrict__ rot_t, const float* __restrict__ boundaries, float eps_c,
     uint32_t* __restrict__ v_codes, uint16_t* __restrict__ v_scale) {
@@ -277,15 +294,37 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
   const int nn = lane & 15, g = lane >> 4;
 
   // ---- the window as matrix-core A operands: lane (nn, g) holds token 16 tt + nn,
-  // channels 32 ks + 8 g .. + 7 (bf16 as they come)
+  // channels 32 ks + 8 g .. + 7 (bf16 as they come; fp32 as hi parts in av, lo parts in al)
+  const uint16_t* v = static_cast<const uint16_t*>(vin);
+  const float* vf = static_cast<const float*>(vin);
   uint4_t av[2][NKS];
+  uint4_t al[F32 ? 2 : 1][F32 ? NKS : 1];
+  float xf[F32 ? 2 : 1][F32 ? NKS : 1][F32 ? 8 : 1];  // fp32: the values themselves, for the scale
   uint32_t tw[8];
   if (active) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        av[tt][ks] = *reinterpret_cast<const uint4_t*>(v + row0 + (16 * tt + nn) * rstride + 32 * ks + 8 * g);
+      for (int ks = 0; ks < NKS; ++ks) {
+        if constexpr (F32) {
+          const float* src8 = vf + row0 + (16 * tt + nn) * rstride + 32 * ks + 8 * g;
+          const float4 f0 = *reinterpret_cast<const float4*>(src8);
+          const float4 f1 = *reinterpret_cast<const float4*>(src8 + 4);
+          const float e8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            uint32_t h0, l0, h1, l1;
+            split_bf16(e8[2 * x], h0, l0);
+            split_bf16(e8[2 * x + 1], h1, l1);
+            av[tt][ks][x] = h0 | (h1 << 16);
+            al[tt][ks][x] = l0 | (l1 << 16);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xf[tt][ks][e] = e8[e];
+        } else {
+          av[tt][ks] = *reinterpret_cast<const uint4_t*>(v + row0 + (16 * tt + nn) * rstride + 32 * ks + 8 * g);
+        }
+      }
     const uint32_t* tagp = reinterpret_cast<const uint32_t*>(modality + static_cast<size_t>(b) * t_cap + tok0);
 #pragma unroll
     for (int x = 0; x < 8; ++x) tw[x] = tagp[x];
@@ -306,13 +345,22 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
       uint32_t mag = 0u;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
+        if constexpr (F32) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const uint32_t wd = av[tt][ks][x];
-          mag |= wd & 0x7FFF7FFFu;
-          const float lo = __uint_as_float(wd << 16), hi = __uint_as_float(wd & 0xFFFF0000u);
-          sq[ks][2 * x] = lo * lo;
-          sq[ks][2 * x + 1] = hi * hi;
+          for (int e = 0; e < 8; ++e) {
+            const float x = xf[tt][ks][e];
+            mag |= __float_as_uint(x) & 0x7FFFFFFFu;
+            sq[ks][e] = x * x;
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const uint32_t wd = av[tt][ks][x];
+            mag |= wd & 0x7FFF7FFFu;
+            const float lo = __uint_as_float(wd << 16), hi = __uint_as_float(wd & 0xFFFF0000u);
+            sq[ks][2 * x] = lo * lo;
+            sq[ks][2 * x + 1] = hi * hi;
+          }
         }
       }
       float s2[8];
@@ -530,9 +578,13 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < 2; ++tt) {
               acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[tt][ks]),
                                                                 __builtin_bit_cast(bf16x8_t, bv[part][ks]), acc[tt], 0, 0, 0);
+              if constexpr (F32)
+                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al[tt][ks]),
+                                                                  __builtin_bit_cast(bf16x8_t, bv[part][ks]), acc[tt], 0, 0, 0);
+            }
         uint32_t bits = 0u, nearm = 0u;
         if constexpr (kTwoBit && SYM) {
           classify_sym(acc, own, bits, nearm);
@@ -573,18 +625,25 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
   // waits for it.  Elements past the list's room are computed by their own lane, alone.
   auto exact_code = [&](int t, int c, uint32_t tg) -> uint32_t {
     const float* ut = rot_t + (static_cast<size_t>(tg) * D + c) * D;
-    const uint16_t* vr = v + row0 + t * rstride;
     float s = 0.0f;
     for (int k0 = 0; k0 < D; k0 += 8) {
       const float4 u0 = *reinterpret_cast<const float4*>(ut + k0);
       const float4 u1 = *reinterpret_cast<const float4*>(ut + k0 + 4);
-      const uint4_t vb = *reinterpret_cast<const uint4_t*>(vr + k0);
       const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      float xv[8];
+      if constexpr (F32) {
+        const float* vr = vf + row0 + t * rstride;
+        const float4 a0 = *reinterpret_cast<const float4*>(vr + k0);
+        const float4 a1 = *reinterpret_cast<const float4*>(vr + k0 + 4);
+        xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+        xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+      } else {
+        const uint4_t vb = *reinterpret_cast<const uint4_t*>(v + row0 + t * rstride + k0);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const uint32_t half = (vb[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu;
-        s = s + uu[kk] * __uint_as_float(half << 16);
+        for (int kk = 0; kk < 8; ++kk) xv[kk] = __uint_as_float(((vb[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu) << 16);
       }
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) s = s + uu[kk] * xv[kk];
     }
     const float sg = sig_lds[wave][t];
     uint32_t code = 0;
@@ -627,25 +686,33 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     for (int e0 = 0; e0 < n; e0 += kNearBatch) {
       // every lane's two terms of each element of the batch, all requested before any use
+      // (the bf16 pairs stay packed until every load is issued: unpacked at the load, each
+      // would wait for its own load before the next is requested)
       float2 uu[kNearBatch];
-      uint32_t vv[kNearBatch];
+      float2 vf2[F32 ? kNearBatch : 1];
+      uint32_t vv[F32 ? 1 : kNearBatch];
       const bool terms = 2 * lane < D;
 #pragma unroll
       for (int j = 0; j < kNearBatch; ++j) {
         uu[j] = make_float2(0.0f, 0.0f);
-        vv[j] = 0u;
+        if constexpr (F32) vf2[j] = make_float2(0.0f, 0.0f);
+        else vv[j] = 0u;
         if (e0 + j < n && terms) {
           const uint32_t en = near_entry[wave][e0 + j];
           const int et = static_cast<int>(en >> 9), ec = static_cast<int>((en >> 2) & 127u);
           uu[j] = *reinterpret_cast<const float2*>(rot_t + (static_cast<size_t>(en & 3u) * D + ec) * D + 2 * lane);
-          vv[j] = *reinterpret_cast<const uint32_t*>(v + row0 + et * rstride + 2 * lane);
+          if constexpr (F32) vf2[j] = *reinterpret_cast<const float2*>(vf + row0 + et * rstride + 2 * lane);
+          else vv[j] = *reinterpret_cast<const uint32_t*>(v + row0 + et * rstride + 2 * lane);
         }
       }
 #pragma unroll
       for (int j = 0; j < kNearBatch; ++j)
-        if (e0 + j < n && terms)
-          *reinterpret_cast<float2*>(&near_prod[wave][j][2 * lane]) =
-              make_float2(uu[j].x * __uint_as_float(vv[j] << 16), uu[j].y * __uint_as_float(vv[j] & 0xFFFF0000u));
+        if (e0 + j < n && terms) {
+          float2 x;
+          if constexpr (F32) x = vf2[j];
+          else x = make_float2(__uint_as_float(vv[j] << 16), __uint_as_float(vv[j] & 0xFFFF0000u));
+          *reinterpret_cast<float2*>(&near_prod[wave][j][2 * lane]) = make_float2(uu[j].x * x.x, uu[j].y * x.y);
+        }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       if (lane < kNearBatch && e0 + lane < n) {
         const float* pr = near_prod[wave][lane];
@@ -709,6 +776,14 @@ template <int D>
 constexpr double value_eps_unit() {
   return 1.02 * 1.01 * (68.0 * (2 * (D / 32) + 1) + (2 * D + 2)) / 16777216.0;
 }
+// The same for fp32 values (split_bf16): twice the matrix-core instructions per output, the
+// terms' magnitudes at most (1 + 2^-7) those of the definition (one more 1.01), and the
+// remainder v - hi - lo, at most 2^-15 |v| per value, whose dot product with a column of
+// U_m is at most 2^-15 ||U_m column|| ||v||_2 (the last term, in units of the column norm).
+template <int D>
+constexpr double value_eps_unit_f32() {
+  return 1.02 * 1.01 * 1.01 * (68.0 * (4 * (D / 32) + 1) + (2 * D + 2)) / 16777216.0 + 1.02 / 32768.0;
+}
 
 template <int D, int VB>
 hipError_t launch_vb(const DeviceTables& tb, const void* v, bool bf16, const uint8_t* mod, int hkv,
@@ -716,17 +791,23 @@ hipError_t launch_vb(const DeviceTables& tb, const void* v, bool bf16, const uin
                      hipStream_t stream) {
   const int64_t tasks = static_cast<int64_t>(batch) * hkv * src.windows_per_sequence();
   const dim3 grid(static_cast<unsigned>((tasks + kWaves - 1) / kWaves));
-  const float eps = static_cast<float>(value_eps_unit<D>() * tb.rot_col_norm + 1.02 * tb.rot_lo_col_norm);
-  if (bf16 && tb.rot_bf16 != nullptr) {
-    if (tb.value_sym) {
-      quantize_values_mfma_kernel<D, VB, true><<<grid, 256, 0, stream>>>(
-          static_cast<const uint16_t*>(v), mod, hkv, src, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
-          tb.rotations_t, tb.boundaries, eps, vc, vs);
-      return hipGetLastError();
-    }
-    quantize_values_mfma_kernel<D, VB, false><<<grid, 256, 0, stream>>>(
-        static_cast<const uint16_t*>(v), mod, hkv, src, t_cap, tasks, reinterpret_cast<const uint4_t*>(tb.rot_bf16),
-        tb.rotations_t, tb.boundaries, eps, vc, vs);
+  if (tb.rot_bf16 != nullptr) {
+    // matrix cores, bf16 values as they come or fp32 values as two bf16 parts each
+    const double unit = bf16 ? value_eps_unit<D>() : value_eps_unit_f32<D>();
+    const float eps = static_cast<float>(unit * tb.rot_col_norm + 1.02 * tb.rot_lo_col_norm);
+    const uint4_t* rb = reinterpret_cast<const uint4_t*>(tb.rot_bf16);
+    if (bf16 && tb.value_sym)
+      quantize_values_mfma_kernel<D, VB, true, false><<<grid, 256, 0, stream>>>(
+          v, mod, hkv, src, t_cap, tasks, rb, tb.rotations_t, tb.boundaries, eps, vc, vs);
+    else if (bf16)
+      quantize_values_mfma_kernel<D, VB, false, false><<<grid, 256, 0, stream>>>(
+          v, mod, hkv, src, t_cap, tasks, rb, tb.rotations_t, tb.boundaries, eps, vc, vs);
+    else if (tb.value_sym)
+      quantize_values_mfma_kernel<D, VB, true, true><<<grid, 256, 0, stream>>>(
+          v, mod, hkv, src, t_cap, tasks, rb, tb.rotations_t, tb.boundaries, eps, vc, vs);
+    else
+      quantize_values_mfma_kernel<D, VB, false, true><<<grid, 256, 0, stream>>>(
+          v, mod, hkv, src, t_cap, tasks, rb, tb.rotations_t, tb.boundaries, eps, vc, vs);
   } else if (bf16) {
     quantize_values_kernel<D, VB, true><<<grid, 256, 0, stream>>>(v, mod, hkv, src, t_cap, tasks, tb.rotations,
                                                                   tb.boundaries, vc, vs);

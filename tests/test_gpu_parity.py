@@ -69,6 +69,40 @@ def test_quantize_parity_full(cid, kbits, vbits, n):
 _SYM16 = (0.1, 0.35, 0.6, 0.9, 1.2, 1.6, 2.0, 2.6)
 
 
+@pytest.mark.parametrize("vbits,levels", [(2, None), (4, None), (2, (-1.3, -0.35, 0.4, 1.7))])
+def test_quantize_values_fp32_inputs(vbits, levels):
+    """fp32 values through the matrix-core path (each value as a bf16 hi part and a rounded
+    bf16 lo part, the remainder inside the near-threshold tolerance): codes and scales
+    bit-exact against the oracle's fp32 definition, d = 128, 4096 tokens of drift data with
+    full 24-bit significands, the built-in codebooks and an asymmetric caller codebook."""
+    import torch
+    cfg = synth.CONFIGS[2]
+    n = 4096
+    say(f"[codec-fp32] cfg2 V{vbits} n={n} levels={levels}")
+    if levels is None:
+        ctx, signs, U, lv = make_context(cfg, 2, vbits)
+    else:
+        lv = O.f16_bits(np.asarray(levels, np.float32))
+        signs, U = synth.rademacher_signs(cfg.head_dim, 0), synth.value_rotations(cfg.head_dim, 0)
+        ctx = binding.Context(cfg.head_dim, cfg.q_heads, cfg.kv_heads, 2, vbits, signs, U, value_codebook=lv)
+    f32 = synth.Config(**{**cfg.__dict__, "fp32_inputs": True})
+    tags, k, v = _inputs(f32, n)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    assert np.count_nonzero(v.view(np.uint32) & 0xFFFF) > v.size // 2   # not bf16 in disguise
+    cache = ctx.alloc_cache(cfg.batch, n)
+    cache["modality"].copy_(to_dev(tags[:, :n]))
+    ctx.quantize_values(torch.from_numpy(v).cuda(), 0, cache)
+    torch.cuda.synchronize()
+    vc, vs = O.quantize_values(v, tags[:, :n], U, lv, vbits)
+    assert np.array_equal(from_dev(cache["v_scale"], np.uint16), vs)
+    gv = from_dev(cache["v_codes"], np.uint32)
+    if not np.array_equal(gv, vc):
+        gcodes = O.unpack_windows(gv, "value", cfg.head_dim, vbits)
+        ocodes = O.unpack_windows(vc, "value", cfg.head_dim, vbits)
+        raise AssertionError(f"{np.count_nonzero(gcodes != ocodes)} of {gcodes.size} value codes differ")
+    ctx.close()
+
+
 @pytest.mark.parametrize("levels", [(-1.3, -0.35, 0.4, 1.7), (-2.0, -0.5, 0.5, 2.0),
                                     tuple(np.round(np.linspace(-2.3, 1.9, 16) + 0.07 * np.sin(np.arange(16)), 3)),
                                     tuple(-x for x in reversed(_SYM16)) + _SYM16])
@@ -132,8 +166,10 @@ def test_quantize_offset_chunk_writes_only_its_windows():
 
 
 @pytest.mark.parametrize("vbits", [2, 4])
-def test_quantize_values_degenerate_tokens(vbits):
-    """Value codes for tokens at the edges of the bf16 matrix-core path: an all-zero window,
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_values_degenerate_tokens(vbits, dtype):
+    """Value codes for tokens at the edges of the matrix-core path (bf16 values, or fp32 values
+    as two bf16 parts each): an all-zero window,
     zero tokens, tokens whose squares underflow (sum of squares 0, so sigma = 0 and every
     rotated value lies within the error bound of a threshold: 3 such tokens in a window are
     recomputed one element at a time, 8 force the whole window through the sequential sum),
@@ -141,7 +177,7 @@ def test_quantize_values_degenerate_tokens(vbits):
     import torch
     cfg = synth.CONFIGS[2]
     n = 256
-    say(f"[codec-degenerate] cfg2 V{vbits} n=256")
+    say(f"[codec-degenerate] cfg2 V{vbits} n=256 {dtype}")
     ctx, signs, U, lv = make_context(cfg, 2, vbits)
     tags, k, v = _inputs(cfg, n)
     v = v.copy()
@@ -151,10 +187,11 @@ def test_quantize_values_degenerate_tokens(vbits):
     v[:, 96] = 0.0                        # window 3: a zero token and an overflowing one
     v[:, 101] *= 1e19
     v[:, 130, :, :64] = 0.0               # window 4: a half-zero token
-    v = torch.from_numpy(v).to(torch.bfloat16).float().numpy()   # what the bf16 path sees
+    if dtype == "bf16":
+        v = torch.from_numpy(v).to(torch.bfloat16).float().numpy()   # what the bf16 path sees
     cache = ctx.alloc_cache(cfg.batch, n)
     cache["modality"].copy_(to_dev(tags[:, :n]))
-    ctx.quantize_values(bf16_tensor(v), 0, cache)
+    ctx.quantize_values(bf16_tensor(v) if dtype == "bf16" else torch.from_numpy(v).cuda(), 0, cache)
     torch.cuda.synchronize()
     with np.errstate(all="ignore"):
         vc, vs = O.quantize_values(v, tags[:, :n], U, lv, vbits)
