@@ -17,8 +17,8 @@ the same way.  The write path is timed separately on one prefill chunk per seque
 
 Prints one JSON line: the headline (effective KV GB/s of the decode step), the
 roofline of the partial kernel, the write-path timings, the other configurations
-(configs 4 and 5 at K2V2 and K4V4, the write path at K4V4 and the config-5 prefill
-write path at both widths) and a CPU-oracle
+(configs 4 and 5 at K2V2 and K4V4, the write path at K4V4 and with fp32 inputs, and the
+config-5 prefill write path at both widths) and a CPU-oracle
 baseline on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -447,6 +447,13 @@ def main():
         others[f"config{cfg.cid}_write_K4V4"] = time_write_path(
             ctx4, cfg, synth.modality_layout(cfg, 0, max(cfg.context, cfg.prefill or 4096)), reps=20)
         ctx4.close()
+        # the same chunk handed over as fp32 (both codecs' matrix-core paths take fp32 too)
+        cfg32 = synth.Config(**{**cfg.__dict__, "fp32_inputs": True})
+        ctx2 = binding.Context(d, cfg.q_heads, cfg.kv_heads, 2, 2, signs, U)
+        others[f"config{cfg.cid}_write_fp32_K2V2"] = time_write_path(
+            ctx2, cfg32, synth.modality_layout(cfg, 0, max(cfg.context, cfg.prefill or 4096)), reps=20)
+        ctx2.close()
+        torch.cuda.empty_cache()
         cfg5 = synth.CONFIGS[5]
         tags5 = synth.modality_layout(cfg5, 0, cfg5.prefill)
         for bits in (2, 4):
