@@ -260,8 +260,10 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi16, uint32_t& lo
 
 // F32: the values come as fp32; each enters the matrix cores as a bf16 hi and lo part
 // (split_bf16), and the tolerance covers the remainder.  Otherwise bf16 values as they come.
+// bf16 values with a symmetric codebook fit four waves per SIMD (at most 128 VGPRs); the
+// bound holds them there (the fp32 and asymmetric 4-bit forms need more registers)
 template <int D, int VB, bool SYM, bool F32>
-__global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
+__global__ __launch_bounds__(256, (!F32 && (SYM || VB == 2)) ? 4 : 1) void quantize_values_mfma_kernel(
     const void* __restrict__ vin, const uint8_t* __restrict__ modality, int hkv, WindowSource src,
     int64_t t_cap, int64_t tasks, const uint4_t* __restrict__ rot_b16,
     const float* __restrict__ rot_t, const float* __restrict__ boundaries, float eps_c,
@@ -493,20 +495,28 @@ __global__ __launch_bounds__(256) void quantize_values_mfma_kernel(
     // at most ~b7 where it matters), so an element outside every band has |x| on the same
     // side of each threshold as y is of b_j, farther than eps.  A NaN result is near; an
     // infinite scale has an infinite tolerance.  `mine` drops the tokens of other modalities.
+    // m comes from a three-level binary search over b1 .. b7 (b4, then b2 or b6, then one of
+    // b1, b3, b5, b7), its three outcomes the bits of m.  The interval [b_m, b_(m+1)) that
+    // holds y is bounded by two of those split points (or by 0 below b1), so the nearest
+    // boundary to y is 0 or a split point on y's path: the four distances give the same
+    // minimum as all eight.
+    static_assert(!kSym4 || NB == 15, "the binary search covers seven positive boundaries");
     auto classify_sym4 = [&](const float4_t (&acc)[2], const bool (&mine)[2][4], const uint64_t (&own)[2][4],
                              uint32_t& bits, uint32_t& nearm) {
+      const float b1 = beta[8], b2 = beta[9], b3 = beta[10], b4 = beta[11], b5 = beta[12], b6 = beta[13], b7 = beta[14];
 #pragma unroll
       for (int k = 7; k >= 0; --k) {
         const int tt = k >> 2, i = k & 3;
         const float x = acc[tt][i], y = fabsf(x) * rsg[tt][i];
-        uint32_t m = 0u;
-        float d = y;
-#pragma unroll
-        for (int j = 0; j < NB / 2; ++j) {
-          const float b = beta[NB / 2 + 1 + j];
-          m = count_bit(m, __builtin_amdgcn_ballot_w64(y >= b));
-          d = fminf(d, fabsf(y - b));
-        }
+        const bool c1 = y >= b4;
+        const float t2 = c1 ? b6 : b2;
+        const bool c2 = y >= t2;
+        const float t3 = c1 ? (c2 ? b7 : b5) : (c2 ? b3 : b1);
+        const bool c3 = y >= t3;
+        uint32_t m = push_bit(0u, __builtin_amdgcn_ballot_w64(c1));
+        m = push_bit(m, __builtin_amdgcn_ballot_w64(c2));
+        m = push_bit(m, __builtin_amdgcn_ballot_w64(c3));
+        const float d = fminf(fminf(y, fabsf(y - b4)), fminf(fabsf(y - t2), fabsf(y - t3)));
         const uint32_t code = ((x >= 0.0f) ? 8u : 7u) ^ m;
         bits = (bits << 4) | (mine[tt][i] ? code : 0u);
         nearm = push_bit(nearm, __builtin_amdgcn_ballot_w64(!(d > epy[tt][i])) & own[tt][i]);
