@@ -83,20 +83,28 @@ def test_streaming_decode_parity(cid, lens, cap, kbits, vbits):
     ctx.close()
 
 
-def test_stream_append_writes_what_the_schedule_quantizes():
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_stream_append_writes_what_the_schedule_quantizes(dtype):
     """Token-by-token appends: the packed cache equals the oracle's quantization of the
     same tokens over the packed ranges, the rings hold the recent tokens, and decoding
-    the stream matches the oracle, at several points of the stream."""
+    the stream matches the oracle, at several points of the stream.  bf16 and fp32 rings
+    (fp32 tokens with full significands: the flushes take the quantizers' fp32 forms)."""
     import torch
     cfg = synth.CONFIGS[2]
+    if dtype == "fp32":
+        cfg = synth.Config(**{**cfg.__dict__, "fp32_inputs": True})
     B, T, cap = 2, 576, 256
-    say(f"[stream-append] cfg2 B={B} {T} tokens ring {cap}")
+    say(f"[stream-append] cfg2 B={B} {T} tokens ring {cap} {dtype}")
     ctx, signs, U, lv = make_context(cfg)
     tags, k, v = _tokens(cfg, T, 5)
     tags, k, v = tags[:1].repeat(B, 0), np.repeat(k[:1], B, 0), np.repeat(v[:1], B, 0)
     cache = ctx.alloc_cache(B, T)
-    rings = ctx.alloc_rings(B, cap)
-    kd, vd = bf16_tensor(k), bf16_tensor(v)
+    if dtype == "fp32":
+        rings = ctx.alloc_rings(B, cap, dtype=torch.float32)
+        kd, vd = torch.from_numpy(np.ascontiguousarray(k)).cuda(), torch.from_numpy(np.ascontiguousarray(v)).cuda()
+    else:
+        rings = ctx.alloc_rings(B, cap)
+        kd, vd = bf16_tensor(k), bf16_tensor(v)
     tg = to_dev(tags)
     q_np = synth.queries(cfg, 6, B)
     q = torch.from_numpy(q_np).cuda()
