@@ -344,6 +344,10 @@ __global__ __launch_bounds__(256, 4) void quantize_keys_kernel(
       for (int e = 0; e < 8; ++e)
 #pragma unroll
         for (int j = 0; j < L; ++j) th[e][j] = mf[e] + sf[e] * (static_cast<float>(j) + 0.5f);
+    } else {
+      // the search's first candidate is j = 7 for every element of a channel
+#pragma unroll
+      for (int e = 0; e < 8; ++e) th[e][0] = mf[e] + sf[e] * 7.5f;
     }
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
@@ -358,17 +362,18 @@ __global__ __launch_bounds__(256, 4) void quantize_keys_kernel(
           const bool lo = y[pp][e] >= (hi ? th[e][2] : th[e][0]);
           cw[e >> 2] |= (hi ? (2u << (8 * (e & 3))) : 0u) | (lo ? (1u << (8 * (e & 3))) : 0u);
         } else {
-          // invariant: y >= theta_j for every j < code
-          int code = 0;
+          // invariant: y >= theta_j for every j < code.  The code is carried as a float (small
+          // integers and halves are exact), so a candidate's j + 1/2 takes one add and its
+          // threshold is the definition's fl(m + fl(s (j + 1/2))); the first candidate, j = 7,
+          // has its threshold per channel.
+          static_assert(KB != 4 || L == 15, "four halvings cover codes 0 .. 15");
+          float fc = y[pp][e] >= th[e][0] ? 8.0f : 0.0f;
 #pragma unroll
-          for (int stp = 8; stp >= 1; stp >>= 1) {
-            const int j = code + stp - 1;  // candidate: is y >= theta_j ?
-            if (j < L) {
-              const float thj = mf[e] + sf[e] * (static_cast<float>(j) + 0.5f);
-              code = (y[pp][e] >= thj) ? code + stp : code;
-            }
+          for (int stp = 4; stp >= 1; stp >>= 1) {
+            const float thj = mf[e] + sf[e] * (fc + (static_cast<float>(stp) - 0.5f));
+            fc = (y[pp][e] >= thj) ? fc + static_cast<float>(stp) : fc;
           }
-          cw[e >> 2] |= static_cast<uint32_t>(code) << (8 * (e & 3));
+          cw[e >> 2] |= static_cast<uint32_t>(fc) << (8 * (e & 3));
         }
       }
       *reinterpret_cast<uint2*>(&codes_lds[wave][TPI * pp + r][8 * q]) = make_uint2(cw[0], cw[1]);
