@@ -101,13 +101,20 @@ struct WindowTask {
   int64_t src_row;  // source row of the window's first token
   int64_t tok0;     // cache position of the window's first token
 };
+// The launchers keep `tasks` below 2^32 (kMaxWindowTasks), so the task's indices come from two
+// 32-bit divisions (64-bit ones expand to some 600 scalar instructions ahead of the wave's
+// first load; measured, that prologue did not bound the launch).
+constexpr int64_t kMaxWindowTasks = int64_t{0xFFFFFFFF};
 __device__ inline WindowTask map_window_task(const WindowSource& s, int64_t task, int64_t tasks, int hkv) {
   WindowTask r{task < tasks, 0, 0, 0, 0};
   if (!r.active) return r;
-  const int64_t per = s.windows_per_sequence();
-  r.b = task / (per * hkv);
-  const int64_t w = (task / hkv) % per;
-  r.h = static_cast<int>(task % hkv);
+  const uint32_t t = static_cast<uint32_t>(task), H = static_cast<uint32_t>(hkv);
+  const uint32_t per = static_cast<uint32_t>(s.windows_per_sequence());
+  const uint32_t th = t / H;           // task / hkv
+  const uint32_t b = th / per;         // task / (hkv per)
+  r.b = b;
+  const int64_t w = th - b * per;      // (task / hkv) % per
+  r.h = static_cast<int>(t - th * H);  // task % hkv
   if (!s.flush_lens) {
     r.src_row = r.b * s.n + w * kWindow;
     r.tok0 = s.t0 + w * kWindow;

@@ -412,6 +412,7 @@ template <int D, int KB, bool MX>
 hipError_t launch_kb(const DeviceTables& tb, const void* k, bool bf16, int hkv, int batch, const WindowSource& src,
                      int64_t t_cap, uint32_t* kc, uint16_t* km, uint16_t* ks, hipStream_t stream) {
   const int64_t tasks = static_cast<int64_t>(batch) * hkv * src.windows_per_sequence();
+  if (tasks > kMaxWindowTasks) return hipErrorInvalidConfiguration;  // the task indices are 32-bit
   const dim3 grid(static_cast<unsigned>((tasks + kWavesPerBlock - 1) / kWavesPerBlock));
   if (bf16)
     quantize_keys_kernel<D, KB, true, MX><<<grid, 256, 0, stream>>>(k, hkv, src, t_cap / kWindow, tasks, tb.signs,

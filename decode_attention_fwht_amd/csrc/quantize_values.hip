@@ -800,6 +800,7 @@ hipError_t launch_vb(const DeviceTables& tb, const void* v, bool bf16, const uin
                      int batch, const WindowSource& src, int64_t t_cap, uint32_t* vc, uint16_t* vs,
                      hipStream_t stream) {
   const int64_t tasks = static_cast<int64_t>(batch) * hkv * src.windows_per_sequence();
+  if (tasks > kMaxWindowTasks) return hipErrorInvalidConfiguration;  // the task indices are 32-bit
   const dim3 grid(static_cast<unsigned>((tasks + kWaves - 1) / kWaves));
   if (tb.rot_bf16 != nullptr) {
     // matrix cores, bf16 values as they come or fp32 values as two bf16 parts each
