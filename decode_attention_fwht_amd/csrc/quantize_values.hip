@@ -235,14 +235,6 @@ __device__ __forceinline__ uint32_t push_bit(uint32_t acc, uint64_t m) {
   asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(m));
   return r;
 }
-// acc + (this lane's bit of the lane mask m): a count of comparisons, one v_addc each
-__device__ __forceinline__ uint32_t count_bit(uint32_t acc, uint64_t m) {
-  uint32_t r;
-  uint64_t carry_out;
-  asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(m));
-  return r;
-}
-
 // A fp32 value v as the sum of two bf16 operands plus a small remainder: hi is v with its
 // low 16 bits cleared (exact), lo the nearest bf16 to v - hi (exact in fp32), so
 // |v - hi - lo| <= 2^-8 |v - hi| < 2^-15 |v| (for |v| >= 2^-126; below, at most half the
