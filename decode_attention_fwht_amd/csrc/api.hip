@@ -325,6 +325,8 @@ omnikv_status omnikv_quantize_keys(const omnikv_ctx* ctx, const void* k, omnikv_
     return fail(OMNIKV_EINVAL, "quantize_keys: device pointers must be 16-byte aligned");
   if (dt != OMNIKV_F32 && dt != OMNIKV_BF16) return fail(OMNIKV_EINVAL, "quantize_keys: dtype must be F32 or BF16");
   if ((st = check_chunk(batch, t0, n, t_cap)) != OMNIKV_OK) return st;
+  if (static_cast<int64_t>(batch) * ctx->sh.hkv * (n / omnikv::kWindow) > omnikv::kMaxWindowTasks)
+    return fail(OMNIKV_EINVAL, "quantize_keys: one call covers at most 2^32 - 1 windows (batch x KV heads x n / 32)");
   omnikv::WindowSource src;
   src.n = n;
   src.t0 = t0;
@@ -344,6 +346,8 @@ omnikv_status omnikv_quantize_values(const omnikv_ctx* ctx, const void* v, omnik
     return fail(OMNIKV_EINVAL, "quantize_values: device pointers must be 16-byte aligned");
   if (dt != OMNIKV_F32 && dt != OMNIKV_BF16) return fail(OMNIKV_EINVAL, "quantize_values: dtype must be F32 or BF16");
   if ((st = check_chunk(batch, t0, n, t_cap)) != OMNIKV_OK) return st;
+  if (static_cast<int64_t>(batch) * ctx->sh.hkv * (n / omnikv::kWindow) > omnikv::kMaxWindowTasks)
+    return fail(OMNIKV_EINVAL, "quantize_values: one call covers at most 2^32 - 1 windows (batch x KV heads x n / 32)");
   omnikv::WindowSource src;
   src.n = n;
   src.t0 = t0;

@@ -182,7 +182,8 @@ omnikv_status omnikv_key_meta_bytes(const omnikv_ctx* ctx, size_t* bytes /* host
 /* Quantize keys of tokens [t0, t0+n) of every sequence ([paper] §3.1: 32-token
  * groups; [paper] §3.3: FP16 m_gc and s_gc, or the MXFP4 records of §3.1).
  * k (device): [B][n][Hkv][d] of dtype dt (fp32 or bf16), token-major.
- * t0 % 32 == 0, n % 32 == 0, n > 0, t0 + n <= t_cap, t_cap % 32 == 0.
+ * t0 % 32 == 0, n % 32 == 0, n > 0, t0 + n <= t_cap, t_cap % 32 == 0, and at
+ * most 2^32 - 1 windows per call (batch x Hkv x n / 32; more: OMNIKV_EINVAL).
  * Writes k_codes / k_min / k_scale for windows t0/32 .. (t0+n)/32 - 1 only. */
 omnikv_status omnikv_quantize_keys(const omnikv_ctx* ctx, const void* k, omnikv_dtype dt,
                                    int32_t batch, int64_t t0, int64_t n, int64_t t_cap,

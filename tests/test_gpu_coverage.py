@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from oracle import omnikv_oracle as O
-from decode_attention_fwht_amd import synth
+from decode_attention_fwht_amd import binding, synth
 from tests.gpu_helpers import (bf16_tensor, cache_to_device, from_dev, make_context, oracle_codebook,
                                row_errors, say, to_dev)
 
@@ -222,4 +222,27 @@ def test_error_metrics_of_the_gpu_codec(bits):
         say(f"    KV head {h}: key MSE {got[h, 0]:.4f}  attention KL {got[h, 1]:.4f}  output MSE {got[h, 2]:.5f}")
     assert np.array_equal(got, ref)
     assert np.all(np.isfinite(got)) and np.all(got > 0)
+    ctx.close()
+
+
+def test_quantize_rejects_more_than_2_32_windows_per_call():
+    """A chunk of more than 2^32 - 1 windows (batch x KV heads x n / 32) is refused on the
+    host before anything is launched (the kernels index windows in 32 bits); the buffers
+    are never touched."""
+    import ctypes
+    import torch
+    cfg = synth.CONFIGS[2]
+    ctx, signs, U, lv = make_context(cfg)
+    L = binding.load()
+    buf = torch.zeros(1 << 12, dtype=torch.uint8, device="cuda")
+    p = ctypes.c_void_p(buf.data_ptr())
+    batch, n = (1 << 31) - 1, 128            # x 2 KV heads x 4 windows: 2^34 windows
+    for fn in ("keys", "values"):
+        if fn == "keys":
+            st = L.omnikv_quantize_keys(ctx._h, p, binding.BF16, batch, 0, n, n, p, p, p, None)
+        else:
+            st = L.omnikv_quantize_values(ctx._h, p, binding.BF16, p, batch, 0, n, n, p, p, None)
+        assert st == binding.EINVAL, fn
+        assert "2^32" in L.omnikv_last_error().decode()
+    torch.cuda.synchronize()
     ctx.close()
