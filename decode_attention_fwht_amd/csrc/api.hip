@@ -195,7 +195,10 @@ omnikv_status omnikv_create(const omnikv_config* cfg, const int8_t* key_signs, c
   ctx->sh = omnikv::Shape{d, cfg->num_q_heads, cfg->num_kv_heads, group, cfg->key_bits, cfg->value_bits, M,
                           cfg->key_meta == OMNIKV_META_MXFP4 ? 1 : 0};
   ctx->levels = levels;
-  (void)hipGetDevice(&ctx->device);
+  if (const hipError_t e = hipGetDevice(&ctx->device); e != hipSuccess) {
+    delete ctx;
+    return hip_fail(e, "hipGetDevice");
+  }
   if (const hipError_t e = scratch_address(ctx->device, &ctx->scratch); e != hipSuccess) {
     delete ctx;
     return hip_fail(e, "hipGetSymbolAddress(scratch)");
